@@ -1,0 +1,156 @@
+"""Benchmark of the hot path: exact self-kNN -> core distances -> Boruvka MST.
+
+One step is one pass of the whole path over the 500,000 x 61 spike-clip set
+(min_samples = 10): ekh_core_distances (self-kNN with K = 11 on MFMA, core
+distance = entry 10) followed by ekh_mst_boruvka (all rounds, with the exact
+shortcuts, edges sorted).  Inputs are resident in HBM before the timed region.
+
+Prints one JSON line.  ``value`` is distance pairs (n^2, the exact self-kNN's
+pair count) per second of the WHOLE step; the kNN-only rate, MST time and the
+per-kernel roofline of the dominant kernel are reported beside it.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "kNN pair-distances/s + Borůvka MST time at 500k×61; % fp32 MFMA peak"
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X published dense fp32 matrix peak
+HBM_PEAK_GBS = 8000.0
+
+
+def cpu_baseline(X, k, budget_s=15.0):
+    """The oracle (float64 C, all host threads) on a bounded sample of the same
+    workload: exact k-NN of the first rows against all n points, in batches of
+    64 rows until ~budget_s seconds have been spent."""
+    import numpy as np
+
+    import oracle
+
+    n = X.shape[1]
+    rows = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and rows < n:
+        b = min(64, n - rows)
+        oracle.knn(np.ascontiguousarray(X[:, rows:rows + b]), X, k)
+        rows += b
+    dt = time.perf_counter() - t0
+    return {
+        "value": rows * n / dt,
+        "unit": "pairs/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": "float64 exact %d-NN of the first %d of %d points against all %d (%.1f s)" % (k, rows, n, n, dt),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="clips_500000x61")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_knn_hdbscan_amd as ekh
+    from exact_knn_hdbscan_amd import datagen
+
+    wl = datagen.make(args.workload)
+    X = wl["X"]
+    d, n = X.shape
+    ms = wl.get("min_samples", 10)
+    dev = torch.device("cuda:0")
+    Xg = torch.from_numpy(X).to(dev)
+    ws_core = torch.empty(ekh.core_workspace_bytes(n, d, ms), dtype=torch.uint8, device=dev)
+    ws_mst = torch.empty(ekh.mst_workspace_bytes(n, d, ms, True), dtype=torch.uint8, device=dev)
+
+    def step():
+        core, ni, nd2 = ekh.core_distances(Xg, ms, return_neighbours=True, workspace=ws_core)
+        t_knn_end = torch.cuda.Event(enable_timing=True)
+        t_knn_end.record()
+        out = ekh.mst_boruvka(Xg, core, ms, ni, nd2, return_stats=True, workspace=ws_mst)
+        return out, t_knn_end
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    timer = ekh.kernel_timer()
+    timer.__enter__()
+    stats = None
+    knn_ms = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        s0 = torch.cuda.Event(enable_timing=True)
+        s0.record()
+        (lo, hi, w, stats), e_knn = step()
+        torch.cuda.synchronize()
+        knn_ms.append(s0.elapsed_time(e_knn))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    total_s = t1 - t0
+    ms_step = 1000.0 * total_s / args.steps
+    tk = timer.read(timer.KNN_TILE)
+    ts = timer.read(timer.SCAN_TILE)
+    timer.stop()
+
+    pairs = float(n) * float(n)
+    value = pairs / (total_s / args.steps)
+    dom_name, dom = ("knn_tile_kernel", tk) if tk["ms"] >= ts["ms"] else ("scan_tile_kernel", ts)
+    achieved = dom["flop"] / (dom["ms"] / 1e3) / 1e12 if dom["ms"] > 0 else 0.0
+    knn_step_ms = float(np.median(knn_ms))
+    mst_step_ms = ms_step - knn_step_ms
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "n": n, "d": d, "min_samples": ms, "k": ms + 1,
+                   "step": "core_distances(self-kNN K=11) + mst_boruvka (all rounds, shortcuts on)"},
+        "knn": {"ms": knn_step_ms, "pairs_per_s": pairs / (knn_step_ms / 1e3),
+                "kernel_tflops": tk["flop"] / (tk["ms"] / 1e3) / 1e12 if tk["ms"] else None,
+                "kernel_ms_per_step": tk["ms"] / args.steps},
+        "mst": {"ms": mst_step_ms, "rounds": stats["rounds"], "scanned": stats["scanned"],
+                "resolved": stats["resolved"], "skipped": stats["skipped"],
+                "components": stats["n_components"],
+                "scan_kernel_ms_per_step": ts["ms"] / args.steps,
+                "scan_tflops": ts["flop"] / (ts["ms"] / 1e3) / 1e12 if ts["ms"] else None},
+        "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
+                     "launches": dom["launches"], "avg_launch_ms": dom["ms"] / max(dom["launches"], 1),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(X, ms + 1)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

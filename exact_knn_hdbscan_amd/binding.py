@@ -1,0 +1,240 @@
+"""Thin ctypes binding of libekh.so (C ABI in include/ekh.h).
+
+Argument marshalling only: every computation runs in the HIP library.  Point
+sets are torch float32 CUDA tensors of shape [d, n] with unit stride along n
+(feature-major, the layout of the clustering page); the leading dimension is
+taken from ``stride(0)``.  Outputs and the workspace are allocated with torch on
+the input's device and the work is enqueued on torch's current stream.
+
+There is no fallback: if the library is missing or no GPU is present the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libekh.so")
+
+EKH_OK = 0
+EKH_EINVAL = -1
+EKH_EWORKSPACE = -2
+EKH_EHIP = -3
+EKH_EINTERNAL = -4
+MAX_K = 32
+MAX_DIM = 256
+MAX_ROUNDS = 64
+MST_NO_NEIGHBOUR_EDGES = 1
+MST_NO_COMPONENT_BOUND = 2
+
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_u32 = ctypes.c_uint32
+_p = ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+
+class MstStats(ctypes.Structure):
+    _fields_ = [
+        ("rounds", ctypes.c_int32),
+        ("n_components", ctypes.c_int32 * MAX_ROUNDS),
+        ("resolved", ctypes.c_int64 * MAX_ROUNDS),
+        ("skipped", ctypes.c_int64 * MAX_ROUNDS),
+        ("scanned", ctypes.c_int64 * MAX_ROUNDS),
+        ("edges_added", ctypes.c_int64 * MAX_ROUNDS),
+        ("round_ms", ctypes.c_double * MAX_ROUNDS),
+    ]
+
+    def as_dict(self) -> dict:
+        r = self.rounds
+        return {
+            "rounds": r,
+            "n_components": list(self.n_components[:r]),
+            "resolved": list(self.resolved[:r]),
+            "skipped": list(self.skipped[:r]),
+            "scanned": list(self.scanned[:r]),
+            "edges_added": list(self.edges_added[:r]),
+            "round_ms": list(self.round_ms[:r]),
+        }
+
+
+class EkhError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("ekh error %d: %s" % (code, msg))
+        self.code = code
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Loads libekh.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError("libekh.so is not built (run __graft_entry__.build())")
+            lib = ctypes.CDLL(LIB_PATH)
+            lib.ekh_version.restype = ctypes.c_int
+            lib.ekh_last_error.restype = ctypes.c_char_p
+            lib.ekh_knn_workspace_bytes.argtypes = [_i64, _i64, _i32, _i32, _i64]
+            lib.ekh_knn_workspace_bytes.restype = _sz
+            lib.ekh_knn.argtypes = [_p, _i64, _i64, _p, _i64, _i64, _i32, _i32, _p, _p, _i64, _p, _sz, _p]
+            lib.ekh_core_workspace_bytes.argtypes = [_i64, _i32, _i32]
+            lib.ekh_core_workspace_bytes.restype = _sz
+            lib.ekh_core_distances.argtypes = [_p, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _sz, _p]
+            lib.ekh_mst_workspace_bytes.argtypes = [_i64, _i32, _i32, ctypes.c_int]
+            lib.ekh_mst_workspace_bytes.restype = _sz
+            lib.ekh_mst_boruvka.argtypes = [_p, _i64, _i64, _i32, _p, _i32, _p, _p, _u32, _p, _p, _p, _p, _p, _sz,
+                                            _p]
+            lib.ekh_timer_enable.argtypes = [ctypes.c_int]
+            lib.ekh_timer_read.argtypes = [ctypes.c_int, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double),
+                                           ctypes.POINTER(ctypes.c_double)]
+            _lib = lib
+    return _lib
+
+
+def _check(rc: int):
+    if rc != EKH_OK:
+        raise EkhError(rc, library().ekh_last_error().decode(errors="replace"))
+
+
+def _points(X: torch.Tensor, name: str):
+    if not isinstance(X, torch.Tensor) or X.dtype != torch.float32 or X.dim() != 2:
+        raise TypeError("%s must be a float32 tensor [d, n]" % name)
+    if not X.is_cuda:
+        raise ValueError("%s must be on a GPU" % name)
+    if X.stride(1) != 1 and X.shape[1] > 1:
+        raise ValueError("%s must have unit stride along points" % name)
+    ld = X.stride(0) if X.shape[0] > 1 else X.shape[1]
+    return X.data_ptr(), int(ld), int(X.shape[1]), int(X.shape[0])
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _workspace(nbytes: int, dev):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dev)
+
+
+def knn_workspace_bytes(n: int, m: int, d: int, k: int, max_chunk_dots: int = 0) -> int:
+    return int(library().ekh_knn_workspace_bytes(n, m, d, k, max_chunk_dots))
+
+
+def core_workspace_bytes(n: int, d: int, min_samples: int) -> int:
+    return int(library().ekh_core_workspace_bytes(n, d, min_samples))
+
+
+def mst_workspace_bytes(n: int, d: int, min_samples: int, with_neighbours: bool = True) -> int:
+    return int(library().ekh_mst_workspace_bytes(n, d, min_samples, 1 if with_neighbours else 0))
+
+
+def knn(X: torch.Tensor, Y: torch.Tensor, k: int, max_chunk_dots: int = 0, workspace: torch.Tensor = None):
+    """k nearest points of Y for every point of X.
+
+    Returns ``(idx int32 [n, k], dist float32 [n, k])``; rows ascending under
+    (squared distance, index).  Passing the same tensor as X and Y makes the set
+    its own database (self pairs at distance 0).
+    """
+    lib = library()
+    px, ldx, n, d = _points(X, "X")
+    py, ldy, m, dy = _points(Y, "Y")
+    if dy != d:
+        raise ValueError("X and Y differ in dimension")
+    if X.device != Y.device:
+        raise ValueError("X and Y on different devices")
+    idx = torch.empty((n, k), dtype=torch.int32, device=X.device)
+    dist = torch.empty((n, k), dtype=torch.float32, device=X.device)
+    need = lib.ekh_knn_workspace_bytes(n, m, d, k, max_chunk_dots)
+    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, X.device)
+    _check(lib.ekh_knn(px, ldx, n, py, ldy, m, d, k, idx.data_ptr(), dist.data_ptr(), max_chunk_dots,
+                       ws.data_ptr(), ws.numel(), _stream(X.device)))
+    return idx, dist
+
+
+def core_distances(X: torch.Tensor, min_samples: int, return_neighbours: bool = False, workspace=None):
+    """Core distances [n] (float32); with ``return_neighbours`` also the self-kNN
+    rows ``(idx int32 [n, ms+1], d2 float32 [n, ms+1])``."""
+    lib = library()
+    px, ldx, n, d = _points(X, "X")
+    core = torch.empty(n, dtype=torch.float32, device=X.device)
+    nb_idx = nb_d2 = None
+    if return_neighbours:
+        nb_idx = torch.empty((n, min_samples + 1), dtype=torch.int32, device=X.device)
+        nb_d2 = torch.empty((n, min_samples + 1), dtype=torch.float32, device=X.device)
+    need = lib.ekh_core_workspace_bytes(n, d, min_samples)
+    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, X.device)
+    _check(lib.ekh_core_distances(px, ldx, n, d, min_samples, core.data_ptr(), _ptr(nb_idx), _ptr(nb_d2),
+                                  ws.data_ptr(), ws.numel(), _stream(X.device)))
+    if return_neighbours:
+        return core, nb_idx, nb_d2
+    return core
+
+
+def mst_boruvka(X: torch.Tensor, core: torch.Tensor, min_samples: int, nbr_idx: torch.Tensor = None,
+                nbr_d2: torch.Tensor = None, flags: int = 0, return_stats: bool = False, workspace=None):
+    """Minimum spanning tree of max(core_a, core_b, |a - b|).
+
+    Returns ``(lo int32 [n-1], hi int32 [n-1], w float32 [n-1])`` sorted by
+    (w, lo, hi), plus a stats dict if ``return_stats``.  Blocks until done.
+    """
+    lib = library()
+    px, ldx, n, d = _points(X, "X")
+    if core.dtype != torch.float32 or core.shape != (n,) or not core.is_contiguous() or core.device != X.device:
+        raise ValueError("core must be a contiguous float32 [n] tensor on X's device")
+    with_nb = nbr_idx is not None
+    if with_nb:
+        K = min_samples + 1
+        for t, dt in ((nbr_idx, torch.int32), (nbr_d2, torch.float32)):
+            if t is None or t.dtype != dt or t.shape != (n, K) or not t.is_contiguous():
+                raise ValueError("neighbour rows must be contiguous [n, min_samples + 1] (int32, float32)")
+    ne = max(n - 1, 0)
+    lo = torch.empty(ne, dtype=torch.int32, device=X.device)
+    hi = torch.empty(ne, dtype=torch.int32, device=X.device)
+    w = torch.empty(ne, dtype=torch.float32, device=X.device)
+    stats = MstStats()
+    need = lib.ekh_mst_workspace_bytes(n, d, min_samples, 1 if with_nb else 0)
+    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, X.device)
+    _check(lib.ekh_mst_boruvka(px, ldx, n, d, core.data_ptr(), min_samples, _ptr(nbr_idx), _ptr(nbr_d2), flags,
+                               lo.data_ptr(), hi.data_ptr(), w.data_ptr(), ctypes.byref(stats), ws.data_ptr(),
+                               ws.numel(), _stream(X.device)))
+    if return_stats:
+        return lo, hi, w, stats.as_dict()
+    return lo, hi, w
+
+
+class kernel_timer:
+    """Context manager around ekh_timer_enable / ekh_timer_read: HIP events on
+    the launch stream around every launch of the two dense kernels."""
+
+    KNN_TILE = 0
+    SCAN_TILE = 1
+
+    def __enter__(self):
+        _check(library().ekh_timer_enable(1))
+        return self
+
+    def __exit__(self, *exc):
+        return False
+
+    def read(self, kernel_id: int) -> dict:
+        n = _i64()
+        ms = ctypes.c_double()
+        fl = ctypes.c_double()
+        _check(library().ekh_timer_read(kernel_id, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(fl)))
+        return {"launches": n.value, "ms": ms.value, "flop": fl.value}
+
+    @staticmethod
+    def stop():
+        library().ekh_timer_enable(0)
+

@@ -1,0 +1,479 @@
+// Host side of libekh: the C ABI declared in include/ekh.h.
+//
+// Validation, workspace carving, the chunk / split planner for the dense
+// kernels, the Boruvka round loop and the optional kernel timer.  All GPU work
+// is enqueued on the caller's stream; nothing here allocates device memory.
+#include "ekh.h"
+#include "ekh_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+using namespace ekh;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+#define EKH_HIP(call)                                                                                                  \
+    do {                                                                                                               \
+        hipError_t e_ = (call);                                                                                        \
+        if (e_ != hipSuccess) return fail(EKH_EHIP, "%s failed: %s", #call, hipGetErrorString(e_));                    \
+    } while (0)
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Sequential carving of the caller's workspace (also used to size it).
+struct Carver {
+    char *base;
+    size_t used = 0;
+    explicit Carver(void *b) : base((char *)b) {}
+    template <class T> T *take(size_t count) {
+        T *p = base ? (T *)(base + used) : nullptr;
+        used += align_up(sizeof(T) * std::max<size_t>(count, 1));
+        return p;
+    }
+};
+
+// ---- kernel timer -----------------------------------------------------------
+struct TimerRec {
+    int id;
+    hipEvent_t e0, e1;
+    double flop;
+};
+std::mutex g_tmu;
+bool g_timer_on = false;
+std::vector<TimerRec> g_trecs;
+
+struct TimedLaunch {
+    TimerRec rec{};
+    bool on = false;
+    hipStream_t s;
+    TimedLaunch(int id, double flop, hipStream_t st) : s(st) {
+        std::lock_guard<std::mutex> lk(g_tmu);
+        if (!g_timer_on) return;
+        rec.id = id;
+        rec.flop = flop;
+        if (hipEventCreate(&rec.e0) != hipSuccess || hipEventCreate(&rec.e1) != hipSuccess) return;
+        on = hipEventRecord(rec.e0, s) == hipSuccess;
+    }
+    void done() {
+        if (!on) return;
+        hipEventRecord(rec.e1, s);
+        std::lock_guard<std::mutex> lk(g_tmu);
+        g_trecs.push_back(rec);
+    }
+};
+
+// ---- kNN planning -----------------------------------------------------------
+struct KnnPlan {
+    int K, QM, TR, QT, chunks;
+    int64_t rows;   // rows per chunk
+    int splits;
+    int64_t tiles;  // database tiles
+};
+
+constexpr int64_t kTargetGroups = 1024; // workgroups per launch to aim for (256 CUs)
+constexpr int64_t kMinTilesPerSplit = 4;
+
+KnnPlan plan_knn(int64_t n, int64_t m, int d, int k, int64_t max_chunk_dots) {
+    KnnPlan p{};
+    p.K = pick_k(k);
+    p.QM = pick_qm(d);
+    p.TR = tile_rows(p.QM);
+    p.QT = knn_query_tile(p.K, p.QM);
+    p.chunks = feature_chunks(d);
+    p.rows = n;
+    if (max_chunk_dots > 0 && m > 0) {
+        const int64_t r = max_chunk_dots / m / p.QT * p.QT;
+        p.rows = std::min<int64_t>(n, std::max<int64_t>(r, p.QT));
+    }
+    p.tiles = (m + p.TR - 1) / p.TR;
+    const int64_t qtiles = std::max<int64_t>(1, (p.rows + p.QT - 1) / p.QT);
+    int64_t s = (kTargetGroups + qtiles - 1) / qtiles;
+    s = std::min<int64_t>(s, std::max<int64_t>(1, p.tiles / kMinTilesPerSplit));
+    s = std::max<int64_t>(1, std::min<int64_t>(s, 65535));
+    p.splits = (int)s;
+    return p;
+}
+
+size_t knn_ws(const KnnPlan &p, int64_t n, int64_t m, bool self, Carver &c, float **nx, float **ny, Entry **part) {
+    *nx = c.take<float>(n);
+    *ny = self ? *nx : c.take<float>(m);
+    *part = p.splits > 1 ? c.take<Entry>((size_t)p.rows * p.splits * p.K) : nullptr;
+    return c.used;
+}
+
+int check_points(const float *X, int64_t ld, int64_t n, int d, const char *name) {
+    if (!X) return fail(EKH_EINVAL, "%s is NULL", name);
+    if (n < 1 || n > INT32_MAX) return fail(EKH_EINVAL, "%s: number of points %lld out of range", name, (long long)n);
+    if (d < 1 || d > EKH_MAX_DIM) return fail(EKH_EINVAL, "%s: d = %d out of range [1, %d]", name, d, EKH_MAX_DIM);
+    if (ld < n) return fail(EKH_EINVAL, "%s: leading dimension %lld < n = %lld", name, (long long)ld, (long long)n);
+    return EKH_OK;
+}
+
+// Runs the dense kNN over all chunks.  out_mode: kOutKnn or kOutCore.
+int run_knn(const KnnPlan &p, const float *X, int64_t ldx, int64_t n, const float *Y, int64_t ldy, int64_t m, int d,
+            bool self, int out_mode, int k_out, int min_samples, int32_t *out_idx, float *out_dist, float *out_core,
+            float *nx, float *ny, Entry *part, hipStream_t s) {
+    EKH_HIP(launch_norms(X, ldx, n, d, nx, s));
+    if (!self) EKH_HIP(launch_norms(Y, ldy, m, d, ny, s));
+    for (int64_t q0 = 0; q0 < n; q0 += p.rows) {
+        KnnArgs a{};
+        a.Q = X;
+        a.ldq = ldx;
+        a.q0 = q0;
+        a.nq = std::min<int64_t>(p.rows, n - q0);
+        a.nrm_q = nx;
+        a.B = Y;
+        a.ldb = ldy;
+        a.m = m;
+        a.nrm_b = ny;
+        a.d = d;
+        a.chunks = p.chunks;
+        a.self = self ? 1 : 0;
+        a.splits = p.splits;
+        a.tiles = p.tiles;
+        a.k_out = k_out;
+        a.min_samples = min_samples;
+        a.part = part;
+        a.out_idx = out_idx;
+        a.out_dist = out_dist;
+        a.out_core = out_core;
+        a.out_mode = p.splits > 1 ? kOutPartial : out_mode;
+        TimedLaunch tl(0, 2.0 * d * (double)a.nq * (double)m, s);
+        EKH_HIP(launch_knn_tile(p.K, p.QM, a, s));
+        tl.done();
+        if (p.splits > 1) {
+            a.out_mode = out_mode;
+            EKH_HIP(launch_knn_merge(p.K, a, s));
+        }
+    }
+    return EKH_OK;
+}
+
+// ---- MST workspace ----------------------------------------------------------
+struct MstWs {
+    float *nrm;
+    int32_t *comp, *parent, *act;
+    uint8_t *resolved;
+    uint64_t *best, *cmin1;
+    uint32_t *cmin2, *compW;
+    int32_t *e_lo, *e_hi;
+    float *e_w;
+    uint32_t *sa, *sb, *sc, *sd;
+    uint64_t *s64a, *s64b;
+    void *sort_tmp;
+    size_t sort_tmp_bytes;
+    BvCounters *ctr;
+    int32_t *nbr_idx;
+    float *nbr_d2;
+    float *knn_nx;
+    Entry *knn_part;
+};
+
+size_t carve_mst(Carver &c, int64_t n, int d, int ms, bool with_nb, MstWs &w) {
+    w.nrm = c.take<float>(n);
+    w.comp = c.take<int32_t>(n);
+    w.parent = c.take<int32_t>(n);
+    w.act = c.take<int32_t>(n);
+    w.resolved = c.take<uint8_t>(n);
+    w.best = c.take<uint64_t>(n);
+    w.cmin1 = c.take<uint64_t>(n);
+    w.cmin2 = c.take<uint32_t>(n);
+    w.compW = c.take<uint32_t>(n);
+    w.e_lo = c.take<int32_t>(n);
+    w.e_hi = c.take<int32_t>(n);
+    w.e_w = c.take<float>(n);
+    w.sa = c.take<uint32_t>(n);
+    w.sb = c.take<uint32_t>(n);
+    w.sc = c.take<uint32_t>(n);
+    w.sd = c.take<uint32_t>(n);
+    w.s64a = c.take<uint64_t>(n);
+    w.s64b = c.take<uint64_t>(n);
+    w.sort_tmp_bytes = edge_sort_temp_bytes(n - 1);
+    w.sort_tmp = c.take<char>(w.sort_tmp_bytes);
+    w.ctr = c.take<BvCounters>(1);
+    w.nbr_idx = nullptr;
+    w.nbr_d2 = nullptr;
+    w.knn_nx = nullptr;
+    w.knn_part = nullptr;
+    if (!with_nb) {
+        const int K = ms + 1;
+        w.nbr_idx = c.take<int32_t>((size_t)n * K);
+        w.nbr_d2 = c.take<float>((size_t)n * K);
+        const KnnPlan p = plan_knn(n, n, d, K, 0);
+        float *ny;
+        knn_ws(p, n, n, true, c, &w.knn_nx, &ny, &w.knn_part);
+    }
+    return c.used;
+}
+
+int ceil_log2(int64_t x) {
+    int r = 0;
+    while ((int64_t(1) << r) < x) ++r;
+    return r;
+}
+
+} // namespace
+
+extern "C" {
+
+int ekh_version(void) { return 100; }
+
+const char *ekh_last_error(void) { return g_err.c_str(); }
+
+size_t ekh_knn_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t k, int64_t max_chunk_dots) {
+    if (n < 1 || m < 1 || d < 1 || d > EKH_MAX_DIM || k < 1 || k > EKH_MAX_K) return 0;
+    const KnnPlan p = plan_knn(n, m, d, k, max_chunk_dots);
+    Carver c(nullptr);
+    float *nx, *ny;
+    Entry *part;
+    return knn_ws(p, n, m, false, c, &nx, &ny, &part);
+}
+
+int ekh_knn(const float *X, int64_t ldx, int64_t n, const float *Y, int64_t ldy, int64_t m, int32_t d, int32_t k,
+            int32_t *out_idx, float *out_dist, int64_t max_chunk_dots, void *ws, size_t ws_bytes, void *stream) {
+    int rc;
+    if ((rc = check_points(X, ldx, n, d, "X")) != EKH_OK) return rc;
+    if ((rc = check_points(Y, ldy, m, d, "Y")) != EKH_OK) return rc;
+    if (k < 1 || k > EKH_MAX_K || k > m) return fail(EKH_EINVAL, "k = %d out of range [1, min(m, %d)]", k, EKH_MAX_K);
+    if (max_chunk_dots < 0) return fail(EKH_EINVAL, "max_chunk_dots < 0");
+    if (!out_idx && !out_dist) return fail(EKH_EINVAL, "no output requested");
+    if (!ws) return fail(EKH_EINVAL, "workspace is NULL");
+    const size_t need = ekh_knn_workspace_bytes(n, m, d, k, max_chunk_dots);
+    if (ws_bytes < need) return fail(EKH_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    const bool self = (X == Y) && (ldx == ldy) && (n == m);
+    const KnnPlan p = plan_knn(n, m, d, k, max_chunk_dots);
+    Carver c(ws);
+    float *nx, *ny;
+    Entry *part;
+    knn_ws(p, n, m, false, c, &nx, &ny, &part);
+    if (self) ny = nx;
+    return run_knn(p, X, ldx, n, Y, ldy, m, d, self, kOutKnn, k, 0, out_idx, out_dist, nullptr, nx, ny, part,
+                   (hipStream_t)stream);
+}
+
+size_t ekh_core_workspace_bytes(int64_t n, int32_t d, int32_t min_samples) {
+    if (n < 1 || d < 1 || d > EKH_MAX_DIM || min_samples < 1 || min_samples + 1 > EKH_MAX_K) return 0;
+    const KnnPlan p = plan_knn(n, n, d, min_samples + 1, 0);
+    Carver c(nullptr);
+    float *nx, *ny;
+    Entry *part;
+    return knn_ws(p, n, n, true, c, &nx, &ny, &part);
+}
+
+int ekh_core_distances(const float *X, int64_t ldx, int64_t n, int32_t d, int32_t min_samples, float *out_core,
+                       int32_t *out_nbr_idx, float *out_nbr_d2, void *ws, size_t ws_bytes, void *stream) {
+    int rc;
+    if ((rc = check_points(X, ldx, n, d, "X")) != EKH_OK) return rc;
+    if (min_samples < 1 || min_samples + 1 > EKH_MAX_K || min_samples >= n)
+        return fail(EKH_EINVAL, "min_samples = %d out of range [1, min(n - 1, %d)]", min_samples, EKH_MAX_K - 1);
+    if (!out_core) return fail(EKH_EINVAL, "out_core is NULL");
+    if ((out_nbr_idx == nullptr) != (out_nbr_d2 == nullptr))
+        return fail(EKH_EINVAL, "out_nbr_idx and out_nbr_d2 must both be NULL or both be set");
+    if (!ws) return fail(EKH_EINVAL, "workspace is NULL");
+    const size_t need = ekh_core_workspace_bytes(n, d, min_samples);
+    if (ws_bytes < need) return fail(EKH_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    const int K = min_samples + 1;
+    const KnnPlan p = plan_knn(n, n, d, K, 0);
+    Carver c(ws);
+    float *nx, *ny;
+    Entry *part;
+    knn_ws(p, n, n, true, c, &nx, &ny, &part);
+    return run_knn(p, X, ldx, n, X, ldx, n, d, true, kOutCore, K, min_samples, out_nbr_idx, out_nbr_d2, out_core, nx,
+                   nx, part, (hipStream_t)stream);
+}
+
+size_t ekh_mst_workspace_bytes(int64_t n, int32_t d, int32_t min_samples, int with_neighbours) {
+    if (n < 1 || d < 1 || d > EKH_MAX_DIM || min_samples < 1 || min_samples + 1 > EKH_MAX_K) return 0;
+    Carver c(nullptr);
+    MstWs w;
+    return carve_mst(c, n, d, min_samples, with_neighbours != 0, w);
+}
+
+int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const float *core, int32_t min_samples,
+                    const int32_t *nbr_idx, const float *nbr_d2, uint32_t flags, int32_t *out_lo, int32_t *out_hi,
+                    float *out_w, ekh_mst_stats *stats, void *ws, size_t ws_bytes, void *stream) {
+    int rc;
+    if ((rc = check_points(X, ldx, n, d, "X")) != EKH_OK) return rc;
+    if (!core) return fail(EKH_EINVAL, "core is NULL");
+    if (min_samples < 1 || min_samples + 1 > EKH_MAX_K || (n >= 2 && min_samples >= n))
+        return fail(EKH_EINVAL, "min_samples = %d out of range [1, min(n - 1, %d)]", min_samples, EKH_MAX_K - 1);
+    if ((nbr_idx == nullptr) != (nbr_d2 == nullptr))
+        return fail(EKH_EINVAL, "nbr_idx and nbr_d2 must both be NULL or both be set");
+    if (flags & ~(EKH_MST_NO_NEIGHBOUR_EDGES | EKH_MST_NO_COMPONENT_BOUND)) return fail(EKH_EINVAL, "unknown flags");
+    if (n >= 2 && (!out_lo || !out_hi || !out_w)) return fail(EKH_EINVAL, "edge outputs are NULL");
+    if (!ws) return fail(EKH_EINVAL, "workspace is NULL");
+    const bool with_nb = nbr_idx != nullptr;
+    const size_t need = ekh_mst_workspace_bytes(n, d, min_samples, with_nb ? 1 : 0);
+    if (ws_bytes < need) return fail(EKH_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    if (stats) std::memset(stats, 0, sizeof *stats);
+    if (n == 1) return EKH_OK;
+
+    hipStream_t s = (hipStream_t)stream;
+    Carver c(ws);
+    MstWs w;
+    carve_mst(c, n, d, min_samples, with_nb, w);
+    const int K = min_samples + 1;
+
+    if (!with_nb) {
+        // the self-kNN rows (K = min_samples + 1) the shortcuts read
+        const KnnPlan p = plan_knn(n, n, d, K, 0);
+        float *scratch_core = (float *)w.sa; // core as computed here is not used: the caller's core rules
+        if ((rc = run_knn(p, X, ldx, n, X, ldx, n, d, true, kOutCore, K, min_samples, w.nbr_idx, w.nbr_d2,
+                          scratch_core, w.knn_nx, w.knn_nx, w.knn_part, s)) != EKH_OK)
+            return rc;
+        nbr_idx = w.nbr_idx;
+        nbr_d2 = w.nbr_d2;
+    }
+    EKH_HIP(launch_norms(X, ldx, n, d, w.nrm, s));
+
+    BvState st{};
+    st.n = n;
+    st.K = K;
+    st.nbr_idx = nbr_idx;
+    st.nbr_d2 = nbr_d2;
+    st.core = core;
+    st.comp = w.comp;
+    st.parent = w.parent;
+    st.act = w.act;
+    st.resolved = w.resolved;
+    st.best = w.best;
+    st.cmin1 = w.cmin1;
+    st.cmin2 = w.cmin2;
+    st.compW = w.compW;
+    st.e_lo = w.e_lo;
+    st.e_hi = w.e_hi;
+    st.e_w = w.e_w;
+    st.ctr = w.ctr;
+
+    const int use_nb = (flags & EKH_MST_NO_NEIGHBOUR_EDGES) ? 0 : 1;
+    const int use_bound = (flags & EKH_MST_NO_COMPONENT_BOUND) ? 0 : 1;
+    const int QM = pick_qm(d);
+    const int TR = tile_rows(QM);
+    const int QT = scan_query_tile(QM);
+    const int64_t tiles = (n + TR - 1) / TR;
+    const int cap = std::max(1, ceil_log2(n));
+
+    EKH_HIP(bv_init(st, s));
+    int64_t ncomp = n;
+    int round = 0;
+    BvCounters h{};
+    while (ncomp > 1) {
+        if (round >= cap)
+            return fail(EKH_EINTERNAL, "Boruvka did not finish in %d rounds (%lld components left)", cap,
+                        (long long)ncomp);
+        const auto t0 = std::chrono::steady_clock::now();
+        EKH_HIP(bv_reset_counters(st, s));
+        EKH_HIP(bv_candidates(st, use_nb, use_bound, s));
+        EKH_HIP(bv_select_active(st, use_bound, s));
+        EKH_HIP(hipMemcpyAsync(&h, w.ctr, sizeof h, hipMemcpyDeviceToHost, s));
+        EKH_HIP(hipStreamSynchronize(s));
+        const int64_t nact = h.n_active;
+        if (nact > 0) {
+            ScanArgs sa{};
+            sa.X = X;
+            sa.ldx = ldx;
+            sa.n = n;
+            sa.nrm = w.nrm;
+            sa.core = core;
+            sa.comp = w.comp;
+            sa.compW = w.compW;
+            sa.act = w.act;
+            sa.nact = nact;
+            sa.best = w.best;
+            sa.d = d;
+            sa.chunks = feature_chunks(d);
+            sa.tiles = tiles;
+            const int64_t ctiles = (nact + QT - 1) / QT;
+            int64_t sp = (kTargetGroups + ctiles - 1) / ctiles;
+            sp = std::min<int64_t>(sp, std::max<int64_t>(1, tiles / kMinTilesPerSplit));
+            sa.splits = (int)std::max<int64_t>(1, std::min<int64_t>(sp, 65535));
+            TimedLaunch tl(1, 2.0 * d * (double)nact * (double)n, s);
+            EKH_HIP(launch_scan_tile(QM, sa, s));
+            tl.done();
+        }
+        EKH_HIP(bv_component_min(st, s));
+        EKH_HIP(bv_select_edges(st, s));
+        const int jumps = ceil_log2(ncomp) + 1;
+        for (int j = 0; j < jumps; ++j) EKH_HIP(bv_jump(st, s));
+        EKH_HIP(bv_relabel(st, s));
+        EKH_HIP(hipMemcpyAsync(&h, w.ctr, sizeof h, hipMemcpyDeviceToHost, s));
+        EKH_HIP(hipStreamSynchronize(s));
+        if (h.n_missing) return fail(EKH_EINTERNAL, "round %d: %u components found no outgoing edge", round, h.n_missing);
+        const int64_t before = ncomp;
+        ncomp = h.n_roots;
+        if (ncomp >= before || ncomp < 1)
+            return fail(EKH_EINTERNAL, "round %d: components %lld -> %lld", round, (long long)before, (long long)ncomp);
+        if (stats && round < EKH_MAX_ROUNDS) {
+            stats->n_components[round] = (int32_t)ncomp;
+            stats->resolved[round] = h.n_resolved;
+            stats->skipped[round] = h.n_skipped;
+            stats->scanned[round] = nact;
+            stats->edges_added[round] = before - ncomp;
+            stats->round_ms[round] =
+                std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+        }
+        ++round;
+    }
+    if (stats) stats->rounds = round;
+    if ((int64_t)h.n_edges != n - 1)
+        return fail(EKH_EINTERNAL, "tree has %u edges, expected %lld", h.n_edges, (long long)(n - 1));
+    EKH_HIP(edge_sort(w.e_lo, w.e_hi, w.e_w, n - 1, w.sort_tmp, w.sort_tmp_bytes, w.sa, w.sb, w.sc, w.sd, w.s64a,
+                      w.s64b, out_lo, out_hi, out_w, s));
+    return EKH_OK;
+}
+
+int ekh_timer_enable(int on) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    for (auto &r : g_trecs) {
+        hipEventDestroy(r.e0);
+        hipEventDestroy(r.e1);
+    }
+    g_trecs.clear();
+    g_timer_on = on != 0;
+    return EKH_OK;
+}
+
+int ekh_timer_read(int kernel_id, int64_t *launches, double *total_ms, double *algo_flop) {
+    if (kernel_id < 0 || kernel_id > 1) return fail(EKH_EINVAL, "unknown kernel id %d", kernel_id);
+    std::lock_guard<std::mutex> lk(g_tmu);
+    int64_t cnt = 0;
+    double ms = 0.0, fl = 0.0;
+    for (auto &r : g_trecs) {
+        if (r.id != kernel_id) continue;
+        if (hipEventSynchronize(r.e1) != hipSuccess) return fail(EKH_EHIP, "hipEventSynchronize failed");
+        float t = 0.f;
+        if (hipEventElapsedTime(&t, r.e0, r.e1) != hipSuccess) return fail(EKH_EHIP, "hipEventElapsedTime failed");
+        ++cnt;
+        ms += t;
+        fl += r.flop;
+    }
+    if (launches) *launches = cnt;
+    if (total_ms) *total_ms = ms;
+    if (algo_flop) *algo_flop = fl;
+    return EKH_OK;
+}
+
+} // extern "C"

