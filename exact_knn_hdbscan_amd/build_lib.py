@@ -15,7 +15,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(PKG, "libekh.so")
-SOURCES = ["tile_kernels.hip", "boruvka_kernels.hip", "api.hip"]
+# (source, object name, extra flags); the kNN kernels are instantiated once per list length
+KNN_KS = [2, 4, 8, 11, 16, 32]
+SOURCES = [("tile_kernels.hip", "tile_kernels", []), ("boruvka_kernels.hip", "boruvka_kernels", []),
+           ("api.hip", "api", [])] + [("knn_inst.hip", "knn_k%d" % k, ["-DEKH_KNN_K=%d" % k]) for k in KNN_KS]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no v_pk_*_f32 in generated code.
@@ -31,9 +34,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, name, extra = job
+    obj = os.path.join(BUILD, name + ".o")
+    cmd = [hipcc()] + COMMON + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr[-6000:]))
@@ -42,7 +46,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), max(2, os.cpu_count() or 2))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs

@@ -16,14 +16,14 @@
 namespace ekh {
 
 // ---- tile geometry -------------------------------------------------------
-constexpr int kWaves = 8;             // waves per workgroup
-constexpr int kThreads = kWaves * 64; // 512 threads
+constexpr int kWaves = 4;             // waves per workgroup (two workgroups per CU)
+constexpr int kThreads = kWaves * 64; // 256 threads
 
 // QM = k-steps held in registers (4 features each): d <= 4 * QM.
 // CB = 16-column query blocks per wave; TR = database rows per LDS tile.
 template <int QM> struct TileGeo;
-template <> struct TileGeo<16> { static constexpr int TR = 64; };
-template <> struct TileGeo<32> { static constexpr int TR = 64; };
+template <> struct TileGeo<16> { static constexpr int TR = 32; };
+template <> struct TileGeo<32> { static constexpr int TR = 32; };
 template <> struct TileGeo<64> { static constexpr int TR = 32; };
 
 // instantiated list lengths; a request for k uses the smallest K >= k
@@ -35,7 +35,7 @@ inline int pick_k(int k) {
     return -1;
 }
 inline int pick_qm(int d) { return d <= 64 ? 16 : (d <= 128 ? 32 : 64); }
-inline int tile_rows(int qm) { return qm == 64 ? 32 : 64; }
+inline int tile_rows(int qm) { return 32; }
 // 16-column query blocks per wave: two when the registers allow it
 constexpr int knn_col_blocks(int K, int QM) { return (K > 11 || QM > 16) ? 1 : 2; }
 constexpr int scan_col_blocks(int QM) { return QM > 16 ? 1 : 2; }

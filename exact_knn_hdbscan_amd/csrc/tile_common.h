@@ -1,0 +1,429 @@
+// Device templates shared by the dense tile kernels of libekh (gfx950).
+//
+// Distances follow the clustering page, "k-nearest neighbours are a matrix
+// product": D2 = (|q|^2 + |b|^2) - 2 q.b, the q.b contraction being one dense
+// product that is never materialised: each 16 x 16 block of it lives in the
+// accumulator registers of v_mfma_f32_16x16x4_f32 and is consumed there.
+//
+// MFMA 16x16x4 f32 lane layout (lane = 16 * g + i, g = 0..3, i = 0..15):
+//   A operand: lane holds A[i][g]    (database row i, feature 4s + g of k-step s)
+//   B operand: lane holds B[g][i]    (feature 4s + g of query column i)
+//   result   : lane holds C[4g + r][i], r = 0..3
+// so a lane owns one query column and sees database rows 4g..4g+3 of every
+// 16-row block, in ascending order; four lanes (g = 0..3) share a column.
+#pragma once
+
+#include "ekh_internal.h"
+
+#include <float.h>
+#include <math.h>
+
+namespace ekh {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f4 mfma16(float a, float b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- tile loop
+// Feature order of the contraction: with qs = 4 * ceil(d / 16) k-steps, lane
+// group g supplies feature g * qs + s at k-step s (features >= d are zero).
+// Any fixed assignment of features to (s, g) gives the same dot product up to
+// rounding; using this one in every kernel keeps D2 bitwise identical (and
+// symmetric), and it lets a lane read four consecutive k-steps of its A
+// operand with one 16-byte LDS read.
+template <int QM> struct Tile {
+    static constexpr int TR = TileGeo<QM>::TR;  // database rows per tile
+    static constexpr int RB = TR / 16;          // 16-row blocks per tile
+    static constexpr int FD = QM * 4;           // features held (d <= FD)
+    static constexpr int RS = FD + 4;           // LDS row stride in floats: 16-byte reads of 8 rows hit distinct banks
+    static constexpr int FSTEP = kThreads / TR; // feature rows per load pass
+    static constexpr int PF = FD / FSTEP;       // prefetch registers per thread
+    static_assert(FD % FSTEP == 0, "tile shape");
+};
+
+// Streams database tiles [t_begin, t_end) through a double-buffered LDS tile
+// (row-major: [row][feature]) and hands each tile's accumulator blocks to
+// epi.tile().  PAYLOAD also stages the per-row component label and core
+// distance (scan epilogue).  FULL: the dimension fills all QM k-steps, so the
+// k-loop has no runtime guard and is one basic block.
+template <int QM, int CB, bool PAYLOAD, bool FULL, class Epi>
+__device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t ldb, int64_t m,
+                                          const float *__restrict__ nrm_b, const int32_t *__restrict__ comp_b,
+                                          const float *__restrict__ core_b, int d, int chunks, int64_t t_begin,
+                                          int64_t t_end, const float (&bq)[CB][QM], Epi &epi) {
+    using T = Tile<QM>;
+    __shared__ __align__(16) float sm_tile[2][T::TR * T::RS];
+    __shared__ __align__(16) float sm_nrm[2][T::TR];
+    __shared__ int32_t sm_comp[2][PAYLOAD ? T::TR : 1];
+    __shared__ float sm_core[2][PAYLOAD ? T::TR : 1];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, g = lane >> 4, li = lane & 15;
+    const int lrow = tid % T::TR, lf0 = tid / T::TR;
+    const int qs = FULL ? QM : 4 * chunks; // k-steps run
+    const int fused = 4 * qs;
+
+    float pf[T::PF];
+    float pn = 0.f, pcore = 0.f;
+    int32_t pcomp = -1;
+
+    auto load = [&](int64_t t) {
+        const int64_t j = t * T::TR + lrow;
+        const bool jv = j < m;
+#pragma unroll
+        for (int p = 0; p < T::PF; ++p) {
+            const int f = lf0 + p * T::FSTEP;
+            pf[p] = (jv && f < d) ? B[(int64_t)f * ldb + j] : 0.f;
+        }
+        if (tid < T::TR) {
+            const int64_t jj = t * T::TR + tid;
+            const bool v = jj < m;
+            pn = v ? nrm_b[jj] : INFINITY; // padding rows never qualify
+            if (PAYLOAD) {
+                pcomp = v ? comp_b[jj] : -1;
+                pcore = v ? core_b[jj] : INFINITY;
+            }
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < T::PF; ++p) {
+            const int f = lf0 + p * T::FSTEP;
+            if (FULL || f < fused) sm_tile[buf][lrow * T::RS + f] = pf[p];
+        }
+        if (tid < T::TR) {
+            sm_nrm[buf][tid] = pn;
+            if (PAYLOAD) {
+                sm_comp[buf][tid] = pcomp;
+                sm_core[buf][tid] = pcore;
+            }
+        }
+    };
+
+    if (t_begin < t_end) {
+        load(t_begin);
+        store(0);
+    }
+    __syncthreads();
+    int buf = 0;
+    for (int64_t t = t_begin; t < t_end; ++t) {
+        const bool more = t + 1 < t_end;
+        if (more) load(t + 1);
+        f4 acc[T::RB][CB];
+#pragma unroll
+        for (int rb = 0; rb < T::RB; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f4{0.f, 0.f, 0.f, 0.f};
+        // this lane's feature block of each row it reads
+        const float *tl = sm_tile[buf] + li * T::RS + g * qs;
+        if (FULL) {
+            constexpr int PRE = QM < 16 ? QM : 16; // k-steps whose A operands are read ahead
+#pragma unroll
+            for (int s0 = 0; s0 < QM; s0 += PRE) {
+                f4 a4[PRE / 4][T::RB];
+#pragma unroll
+                for (int c = 0; c < PRE / 4; ++c)
+#pragma unroll
+                    for (int rb = 0; rb < T::RB; ++rb)
+                        a4[c][rb] = *reinterpret_cast<const f4 *>(tl + rb * 16 * T::RS + s0 + 4 * c);
+#pragma unroll
+                for (int s = 0; s < PRE; ++s)
+#pragma unroll
+                    for (int rb = 0; rb < T::RB; ++rb)
+#pragma unroll
+                        for (int cb = 0; cb < CB; ++cb)
+                            acc[rb][cb] = mfma16(a4[s / 4][rb][s % 4], bq[cb][s0 + s], acc[rb][cb]);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < QM / 4; ++c) {
+                if (c < chunks) {
+                    f4 a4[T::RB];
+#pragma unroll
+                    for (int rb = 0; rb < T::RB; ++rb)
+                        a4[rb] = *reinterpret_cast<const f4 *>(tl + rb * 16 * T::RS + 4 * c);
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                        for (int rb = 0; rb < T::RB; ++rb)
+#pragma unroll
+                            for (int cb = 0; cb < CB; ++cb)
+                                acc[rb][cb] = mfma16(a4[rb][s4], bq[cb][c * 4 + s4], acc[rb][cb]);
+                }
+            }
+        }
+        if (PAYLOAD)
+            epi.tile(acc, sm_nrm[buf], sm_comp[buf], sm_core[buf], t * T::TR);
+        else
+            epi.tile(acc, sm_nrm[buf], nullptr, nullptr, t * T::TR);
+        if (more) store(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+    }
+}
+
+// Loads the register-resident query operand: lane (g, i) holds feature
+// g * qs + s of its query column at k-step s (qs = 4 * chunks).
+template <int QM>
+__device__ __forceinline__ void load_query(const float *__restrict__ Q, int64_t ldq, int64_t col, bool valid, int d,
+                                           int chunks, int g, float (&bq)[QM]) {
+    const int qs = 4 * chunks;
+#pragma unroll
+    for (int s = 0; s < QM; ++s) {
+        const int f = g * qs + s;
+        bq[s] = (valid && s < qs && f < d) ? Q[(int64_t)f * ldq + col] : 0.f;
+    }
+}
+
+// ---------------------------------------------------------------- top-K list
+// Sorted ascending list of K (d2, idx) entries in registers.  Insertion is the
+// fixed, compile-time-unrolled compare-and-swap sequence of the HDBSCAN page
+// ("The hang"): the candidate replaces the last entry and moves towards the
+// front through K - 1 conditional swaps, with no data-dependent loop.
+template <int K> struct TopK {
+    float d[K];
+    int32_t i[K];
+
+    __device__ __forceinline__ void clear() {
+#pragma unroll
+        for (int t = 0; t < K; ++t) {
+            d[t] = INFINITY;
+            i[t] = 0x7fffffff;
+        }
+    }
+    // Candidate from a stream whose indices ascend: it is larger than every
+    // entry in index, so a strict '<' on d2 keeps equal distances in index order.
+    __device__ __forceinline__ void push_ascending(float v, int32_t j) {
+        d[K - 1] = v;
+        i[K - 1] = j;
+#pragma unroll
+        for (int t = K - 1; t > 0; --t) {
+            const bool sw = d[t] < d[t - 1];
+            const float a = sw ? d[t] : d[t - 1], b = sw ? d[t - 1] : d[t];
+            const int32_t ia = sw ? i[t] : i[t - 1], ib = sw ? i[t - 1] : i[t];
+            d[t - 1] = a;
+            d[t] = b;
+            i[t - 1] = ia;
+            i[t] = ib;
+        }
+    }
+    __device__ __forceinline__ static bool less(float a, int32_t ia, float b, int32_t ib) {
+        return a < b || (a == b && ia < ib);
+    }
+    // Candidate in any order: full (d2, idx) comparison.
+    __device__ __forceinline__ void push_any(float v, int32_t j) {
+        if (!less(v, j, d[K - 1], i[K - 1])) return;
+        d[K - 1] = v;
+        i[K - 1] = j;
+#pragma unroll
+        for (int t = K - 1; t > 0; --t) {
+            const bool sw = less(d[t], i[t], d[t - 1], i[t - 1]);
+            const float a = sw ? d[t] : d[t - 1], b = sw ? d[t - 1] : d[t];
+            const int32_t ia = sw ? i[t] : i[t - 1], ib = sw ? i[t - 1] : i[t];
+            d[t - 1] = a;
+            d[t] = b;
+            i[t - 1] = ia;
+            i[t] = ib;
+        }
+    }
+    // Merge with the list held by lane (lane ^ mask); both lanes end equal.
+    __device__ __forceinline__ void merge_xor(int mask) {
+        float od[K];
+        int32_t oi[K];
+#pragma unroll
+        for (int t = 0; t < K; ++t) {
+            od[t] = __shfl_xor(d[t], mask);
+            oi[t] = __shfl_xor(i[t], mask);
+        }
+#pragma unroll
+        for (int t = 0; t < K; ++t) push_any(od[t], oi[t]);
+    }
+};
+
+// ---------------------------------------------------------------- kNN epilogue
+// Each lane keeps CB lists (one per query column it owns) in a lane-private
+// region of LDS; only the last entry's D2 (the admission threshold) stays in a
+// register.  Per tile every D2 is computed and tested against that threshold in
+// straight-line code; a lane that has a candidate loads the list, inserts its
+// candidates in ascending row order (recomputing the same D2) and stores it back.
+template <int K, int CB, int RB> struct EpiKnn {
+    Entry *lists; // LDS, [CB][K][kThreads]
+    float thr[CB];
+    float nq[CB];
+    int32_t qrow[CB];
+    int64_t qlo, qhi; // absolute query rows of this workgroup, for the self diagonal
+    int self;
+    int g;
+    int tid;
+
+    __device__ __forceinline__ Entry &at(int cb, int t) { return lists[(cb * K + t) * kThreads + tid]; }
+
+    __device__ __forceinline__ void init() {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+            for (int t = 0; t < K; ++t) at(cb, t) = Entry{INFINITY, 0x7fffffff};
+            thr[cb] = INFINITY;
+        }
+    }
+    __device__ __forceinline__ void load(int cb, TopK<K> &L) {
+#pragma unroll
+        for (int t = 0; t < K; ++t) {
+            const Entry e = at(cb, t);
+            L.d[t] = e.d2;
+            L.i[t] = e.idx;
+        }
+    }
+    __device__ __forceinline__ void store(int cb, const TopK<K> &L) {
+#pragma unroll
+        for (int t = 0; t < K; ++t) at(cb, t) = Entry{L.d[t], L.i[t]};
+    }
+
+    __device__ __forceinline__ void tile(const f4 (&acc)[RB][CB], const float *nrm, const int32_t *, const float *,
+                                         int64_t j0) {
+        const bool diag = self && (j0 < qhi) && (j0 + RB * 16 > qlo);
+        if (diag)
+            tile_impl<true>(acc, nrm, j0);
+        else
+            tile_impl<false>(acc, nrm, j0);
+    }
+    template <bool DIAG>
+    __device__ __forceinline__ float dist2(const f4 (&acc)[RB][CB], const f4 (&nb4)[RB], int rb, int r, int cb,
+                                           int32_t j) const {
+        float d2 = fmaf(-2.f, acc[rb][cb][r], nq[cb] + nb4[rb][r]);
+        if (DIAG && j == qrow[cb]) d2 = 0.f;
+        return d2;
+    }
+    template <bool DIAG>
+    __device__ __forceinline__ void tile_impl(const f4 (&acc)[RB][CB], const float *nrm, int64_t j0) {
+        f4 nb4[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) nb4[rb] = *reinterpret_cast<const f4 *>(nrm + rb * 16 + 4 * g);
+        bool hit[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) hit[cb] = false;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    const int32_t j = (int32_t)(j0 + rb * 16 + 4 * g + r);
+                    hit[cb] |= dist2<DIAG>(acc, nb4, rb, r, cb, j) < thr[cb];
+                }
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            if (!hit[cb]) continue;
+            TopK<K> L;
+            load(cb, L);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int32_t j = (int32_t)(j0 + rb * 16 + 4 * g + r);
+                    const float d2 = dist2<DIAG>(acc, nb4, rb, r, cb, j);
+                    if (d2 < L.d[K - 1]) L.push_ascending(d2 > 0.f ? d2 : 0.f, j);
+                }
+            store(cb, L);
+            thr[cb] = L.d[K - 1];
+        }
+    }
+};
+
+// Writes a finished list for absolute row q.
+template <int K>
+__device__ __forceinline__ void write_list(const KnnArgs &a, const TopK<K> &L, int64_t q, int split) {
+    if (a.out_mode == kOutPartial) {
+        Entry *dst = a.part + ((int64_t)split * a.nq + (q - a.q0)) * K;
+#pragma unroll
+        for (int t = 0; t < K; ++t) dst[t] = Entry{L.d[t], L.i[t]};
+    } else if (a.out_mode == kOutKnn) {
+#pragma unroll
+        for (int t = 0; t < K; ++t) {
+            if (t < a.k_out) {
+                if (a.out_idx) a.out_idx[q * a.k_out + t] = L.i[t];
+                if (a.out_dist) a.out_dist[q * a.k_out + t] = sqrt_rn(L.d[t]);
+            }
+        }
+    } else {
+        float c = 0.f;
+#pragma unroll
+        for (int t = 0; t < K; ++t) {
+            if (t == a.min_samples - 1) c = L.d[t];
+            if (t < a.k_out) {
+                if (a.out_idx) a.out_idx[q * a.k_out + t] = L.i[t];
+                if (a.out_dist) a.out_dist[q * a.k_out + t] = L.d[t];
+            }
+        }
+        a.out_core[q] = sqrt_rn(c);
+    }
+}
+
+template <int K, int QM, bool FULL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void knn_tile_kernel(KnnArgs a) {
+    constexpr int CB = knn_col_blocks(K, QM);
+    using T = Tile<QM>;
+    constexpr int QT = kWaves * 16 * CB;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, li = lane & 15;
+    const int split = blockIdx.y;
+    const int64_t qbase = (int64_t)blockIdx.x * QT; // local row of the workgroup's first query
+
+    __shared__ Entry sm_lists[CB * K * kThreads];
+    EpiKnn<K, CB, T::RB> epi;
+    epi.lists = sm_lists;
+    epi.tid = tid;
+    float bq[CB][QM];
+    bool qv[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const int64_t ql = qbase + wave * 16 * CB + cb * 16 + li;
+        qv[cb] = ql < a.nq;
+        const int64_t q = a.q0 + (qv[cb] ? ql : 0);
+        load_query<QM>(a.Q, a.ldq, q, qv[cb], a.d, a.chunks, g, bq[cb]);
+        epi.nq[cb] = qv[cb] ? a.nrm_q[q] : 0.f;
+        epi.qrow[cb] = (int32_t)(a.q0 + ql);
+    }
+    epi.init();
+    epi.qlo = a.q0 + qbase;
+    epi.qhi = a.q0 + (qbase + QT < a.nq ? qbase + QT : a.nq);
+    epi.self = a.self;
+    epi.g = g;
+
+    const int64_t tb = a.tiles * split / a.splits, te = a.tiles * (split + 1) / a.splits;
+    run_tiles<QM, CB, false, FULL>(a.B, a.ldb, a.m, a.nrm_b, nullptr, nullptr, a.d, a.chunks, tb, te, bq, epi);
+
+    // merge the four lane groups that share each query column
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        TopK<K> L;
+        epi.load(cb, L);
+        L.merge_xor(16);
+        L.merge_xor(32);
+        if (g == 0 && qv[cb]) write_list<K>(a, L, epi.qrow[cb], split);
+    }
+}
+
+// One thread per row: merges the split lists in split order.
+template <int K> __global__ void knn_merge_kernel(KnnArgs a) {
+    const int64_t ql = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (ql >= a.nq) return;
+    TopK<K> L;
+    L.clear();
+    for (int s = 0; s < a.splits; ++s) {
+        const Entry *src = a.part + ((int64_t)s * a.nq + ql) * K;
+#pragma unroll
+        for (int t = 0; t < K; ++t) {
+            const Entry e = src[t];
+            L.push_any(e.d2, e.idx);
+        }
+    }
+    write_list<K>(a, L, a.q0 + ql, 0); // a.out_mode is the final mode here
+}
+
+template <int K> hipError_t launch_knn_tile_k(int QM, const KnnArgs &a, hipStream_t s);
+template <int K> hipError_t launch_knn_merge_k(const KnnArgs &a, hipStream_t s);
+
+} // namespace ekh

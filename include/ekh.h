@@ -30,8 +30,9 @@
  *    ekh_knn and ekh_core_distances do not synchronise the host.
  *    ekh_mst_boruvka blocks: it reads a few counters back after each round.
  *  - Squared distances are float32, D2 = max(0, (|x|^2 + |y|^2) - 2 x.y), with
- *    the product on MFMA and the norms from one fixed-order kernel, so that
- *    D2(a, b) is bitwise symmetric and identical in every entry point.
+ *    the product on MFMA and the norms computed by the same MFMA contraction
+ *    (same feature order), so that D2(a, b) is bitwise symmetric, identical in
+ *    every entry point, and exactly 0 for bitwise-identical points.
  *    Distances are the correctly rounded square root of D2.
  *  - Neighbour rows are ascending under (D2, index): equal distances keep the
  *    lower index first.

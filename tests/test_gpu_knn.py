@@ -158,3 +158,22 @@ def test_core_closed_forms():
     D = datagen.duplicates(12, 61, seed=5, n_other=50)
     c = host(ekh.core_distances(dev(D), 10))
     assert np.all(c[:12] == 0) and np.all(c[12:] > 0)
+
+
+def test_identical_points_at_distance_zero():
+    """Norms come from the same MFMA contraction as the dot products, so two
+    bitwise-identical points are at D2 = 0 exactly, wherever they sit."""
+    rng = np.random.default_rng(12)
+    base = datagen.spike_clips(900, 6, seed=12)
+    X = base.copy()
+    src = rng.choice(900, 60, replace=False)
+    dst = rng.choice(np.setdiff1d(np.arange(900), src), 60, replace=False)
+    X[:, dst] = X[:, src]
+    say("identical points, scattered")
+    Xg = dev(X)
+    core, ni, nd2 = ekh.core_distances(Xg, 3, return_neighbours=True)
+    ni, nd2 = host(ni), host(nd2)
+    for a, b in zip(src, dst):
+        for p, q in ((a, b), (b, a)):
+            row = ni[p].tolist()
+            assert q in row and nd2[p][row.index(q)] == 0.0
