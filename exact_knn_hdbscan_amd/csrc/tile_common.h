@@ -45,9 +45,12 @@ template <int QM> struct Tile {
 
 // Streams database tiles [t_begin, t_end) through a double-buffered LDS tile
 // (row-major: [row][feature]) and hands each tile's accumulator blocks to
-// epi.tile().  PAYLOAD also stages the per-row component label and core
-// distance (scan epilogue).  FULL: the dimension fills all QM k-steps, so the
-// k-loop has no runtime guard and is one basic block.
+// epi.tile().  The loop is software-pipelined: while the MFMAs of tile t run
+// into one accumulator set, the epilogue consumes tile t - 1 from the other,
+// and the global loads of tile t + 2 are in flight.  Per-row norms (and, with
+// PAYLOAD, component labels and core distances) live in a three-slot ring so
+// that tile t - 1's stay valid while tile t + 1's are stored.  FULL: the
+// dimension fills all QM k-steps, so the k-loop has no runtime guard.
 template <int QM, int CB, bool PAYLOAD, bool FULL, class Epi>
 __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t ldb, int64_t m,
                                           const float *__restrict__ nrm_b, const int32_t *__restrict__ comp_b,
@@ -55,9 +58,9 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
                                           int64_t t_end, const float (&bq)[CB][QM], Epi &epi) {
     using T = Tile<QM>;
     __shared__ __align__(16) float sm_tile[2][T::TR * T::RS];
-    __shared__ __align__(16) float sm_nrm[2][T::TR];
-    __shared__ int32_t sm_comp[2][PAYLOAD ? T::TR : 1];
-    __shared__ float sm_core[2][PAYLOAD ? T::TR : 1];
+    __shared__ __align__(16) float sm_nrm[3][T::TR];
+    __shared__ int32_t sm_comp[3][PAYLOAD ? T::TR : 1];
+    __shared__ float sm_core[3][PAYLOAD ? T::TR : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, g = lane >> 4, li = lane & 15;
@@ -65,53 +68,44 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
     const int qs = FULL ? QM : 4 * chunks; // k-steps run
     const int fused = 4 * qs;
 
-    float pf[T::PF];
-    float pn = 0.f, pcore = 0.f;
-    int32_t pcomp = -1;
-
-    auto load = [&](int64_t t) {
+    struct Pref {
+        float v[T::PF];
+        float n, core;
+        int32_t comp;
+    };
+    auto load = [&](Pref &P, int64_t t) {
         const int64_t j = t * T::TR + lrow;
         const bool jv = j < m;
 #pragma unroll
         for (int p = 0; p < T::PF; ++p) {
             const int f = lf0 + p * T::FSTEP;
-            pf[p] = (jv && f < d) ? B[(int64_t)f * ldb + j] : 0.f;
+            P.v[p] = (jv && f < d) ? B[(int64_t)f * ldb + j] : 0.f;
         }
         if (tid < T::TR) {
             const int64_t jj = t * T::TR + tid;
             const bool v = jj < m;
-            pn = v ? nrm_b[jj] : INFINITY; // padding rows never qualify
+            P.n = v ? nrm_b[jj] : INFINITY; // padding rows never qualify
             if (PAYLOAD) {
-                pcomp = v ? comp_b[jj] : -1;
-                pcore = v ? core_b[jj] : INFINITY;
+                P.comp = v ? comp_b[jj] : -1;
+                P.core = v ? core_b[jj] : INFINITY;
             }
         }
     };
-    auto store = [&](int buf) {
+    auto store = [&](const Pref &P, int buf, int slot) {
 #pragma unroll
         for (int p = 0; p < T::PF; ++p) {
             const int f = lf0 + p * T::FSTEP;
-            if (FULL || f < fused) sm_tile[buf][lrow * T::RS + f] = pf[p];
+            if (FULL || f < fused) sm_tile[buf][lrow * T::RS + f] = P.v[p];
         }
         if (tid < T::TR) {
-            sm_nrm[buf][tid] = pn;
+            sm_nrm[slot][tid] = P.n;
             if (PAYLOAD) {
-                sm_comp[buf][tid] = pcomp;
-                sm_core[buf][tid] = pcore;
+                sm_comp[slot][tid] = P.comp;
+                sm_core[slot][tid] = P.core;
             }
         }
     };
-
-    if (t_begin < t_end) {
-        load(t_begin);
-        store(0);
-    }
-    __syncthreads();
-    int buf = 0;
-    for (int64_t t = t_begin; t < t_end; ++t) {
-        const bool more = t + 1 < t_end;
-        if (more) load(t + 1);
-        f4 acc[T::RB][CB];
+    auto mma = [&](int buf, f4 (&acc)[T::RB][CB]) {
 #pragma unroll
         for (int rb = 0; rb < T::RB; ++rb)
 #pragma unroll
@@ -119,7 +113,7 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
         // this lane's feature block of each row it reads
         const float *tl = sm_tile[buf] + li * T::RS + g * qs;
         if (FULL) {
-            constexpr int PRE = QM < 16 ? QM : 16; // k-steps whose A operands are read ahead
+            constexpr int PRE = QM < 8 ? QM : 8; // k-steps whose A operands are read ahead
 #pragma unroll
             for (int s0 = 0; s0 < QM; s0 += PRE) {
                 f4 a4[PRE / 4][T::RB];
@@ -154,14 +148,53 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
                 }
             }
         }
-        if (PAYLOAD)
-            epi.tile(acc, sm_nrm[buf], sm_comp[buf], sm_core[buf], t * T::TR);
-        else
-            epi.tile(acc, sm_nrm[buf], nullptr, nullptr, t * T::TR);
-        if (more) store(buf ^ 1);
+    };
+    auto finish = [&](const f4 (&acc)[T::RB][CB], int64_t t, int slot) {
+        epi.tile(acc, sm_nrm[slot], PAYLOAD ? sm_comp[slot] : nullptr, PAYLOAD ? sm_core[slot] : nullptr,
+                 t * T::TR);
+    };
+
+    if (t_begin >= t_end) return;
+    // ring slot of tile t is (t - t_begin) mod 3, tracked without division
+    auto next3 = [](int x) { return x == 2 ? 0 : x + 1; };
+    Pref P0, P1;
+    P0.n = P1.n = 0.f;
+    P0.core = P1.core = 0.f;
+    P0.comp = P1.comp = -1;
+    load(P0, t_begin);
+    store(P0, 0, 0);
+    if (t_begin + 1 < t_end) load(P1, t_begin + 1);
+    __syncthreads();
+    f4 accA[T::RB][CB], accB[T::RB][CB];
+    int buf = 0;
+    int sl = 0; // slot of tile t
+    for (int64_t t = t_begin; t < t_end; t += 2) {
+        // slots of tiles t + 1 and t + 2; tile t - 1 shares t + 2's slot (its
+        // epilogue runs before t + 2 is stored there, with a barrier between)
+        const int sl1 = next3(sl), sl2 = next3(sl1), slp = sl2;
+        // tile t into accA; epilogue of tile t - 1 (accB)
+        if (t + 2 < t_end) load(P0, t + 2);
+        mma(buf, accA);
+        if (t > t_begin) finish(accB, t - 1, slp);
+        if (t + 1 < t_end) store(P1, buf ^ 1, sl1);
         __syncthreads();
         buf ^= 1;
+        if (t + 1 >= t_end) break;
+        // tile t + 1 into accB; epilogue of tile t (accA)
+        if (t + 3 < t_end) load(P1, t + 3);
+        mma(buf, accB);
+        finish(accA, t, sl);
+        if (t + 2 < t_end) store(P0, buf ^ 1, sl2);
+        __syncthreads();
+        buf ^= 1;
+        sl = sl2;
     }
+    const int64_t last = t_end - 1;
+    const int lsl = (int)((last - t_begin) % 3);
+    if (((last - t_begin) & 1) == 0)
+        finish(accA, last, lsl);
+    else
+        finish(accB, last, lsl);
 }
 
 // Loads the register-resident query operand: lane (g, i) holds feature
@@ -242,19 +275,51 @@ template <int K> struct TopK {
     }
 };
 
+// ---------------------------------------------------------------- lane groups
+// Min / max over the four lanes (lane ^ 16, lane ^ 32) that share a query
+// column, with the gfx950 lane-swap instructions: permlane16_swap(v, v) yields
+// v and the value of lane ^ 16 (in an order that depends on the row), and
+// permlane32_swap likewise for lane ^ 32, so a symmetric min or max needs no
+// lane select and no LDS round trip.
+__device__ __forceinline__ uint32_t group_min_u32(uint32_t v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    const uint32_t m = a[0] < a[1] ? a[0] : a[1];
+    const auto b = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+    return b[0] < b[1] ? b[0] : b[1];
+}
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    const uint32_t m = a[0] > a[1] ? a[0] : a[1];
+    const auto b = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+    return b[0] > b[1] ? b[0] : b[1];
+}
+// For non-negative floats (and +inf) the bit patterns order like the values.
+__device__ __forceinline__ float group_min_nonneg(float v) { return __uint_as_float(group_min_u32(__float_as_uint(v))); }
+__device__ __forceinline__ float group_max_nonneg(float v) { return __uint_as_float(group_max_u32(__float_as_uint(v))); }
+
 // ---------------------------------------------------------------- kNN epilogue
 // Each lane keeps CB lists (one per query column it owns) in a lane-private
-// region of LDS; only the last entry's D2 (the admission threshold) stays in a
-// register.  Per tile every D2 is computed and tested against that threshold in
-// straight-line code; a lane that has a candidate loads the list, inserts its
-// candidates in ascending row order (recomputing the same D2) and stores it back.
+// region of LDS; only the last entry's D2 stays in a register.  Per tile every
+// D2 is computed and tested against an admission threshold in straight-line
+// code; a lane that has a candidate loads the list, inserts its candidates in
+// ascending row order (recomputing the same D2) and stores it back.
+//
+// The four lanes of a query column see disjoint rows and keep separate lists
+// that are merged at the end.  Any K real candidates bound the query's final
+// K-th D2 from above, and two such bounds are cheap to share between the four
+// lanes: the smallest of their last entries (one full list), and the largest of
+// their J-th entries, J = ceil(K / 4) - 1 (four lists with J + 1 entries each
+// hold at least K candidates).  A candidate above the smaller bound can never
+// reach the final list and is not admitted (on equality it is, since a lower
+// index can still win the tie).  Without this, each lane would keep filling its
+// own list with candidates that the final merge drops.
 template <int K, int CB, int RB> struct EpiKnn {
+    static constexpr int J = (K + 3) / 4 - 1;
     Entry *lists; // LDS, [CB][K][kThreads]
-    float thr[CB];
+    float thr[CB]; // this lane's last entry
+    float qj[CB];  // this lane's J-th entry
     float nq[CB];
     int32_t qrow[CB];
-    int64_t qlo, qhi; // absolute query rows of this workgroup, for the self diagonal
-    int self;
     int g;
     int tid;
 
@@ -266,6 +331,7 @@ template <int K, int CB, int RB> struct EpiKnn {
 #pragma unroll
             for (int t = 0; t < K; ++t) at(cb, t) = Entry{INFINITY, 0x7fffffff};
             thr[cb] = INFINITY;
+            qj[cb] = INFINITY;
         }
     }
     __device__ __forceinline__ void load(int cb, TopK<K> &L) {
@@ -281,38 +347,33 @@ template <int K, int CB, int RB> struct EpiKnn {
         for (int t = 0; t < K; ++t) at(cb, t) = Entry{L.d[t], L.i[t]};
     }
 
+    __device__ __forceinline__ float dist2(const f4 (&acc)[RB][CB], const f4 (&nb4)[RB], int rb, int r, int cb) const {
+        return fmaf(-2.f, acc[rb][cb][r], nq[cb] + nb4[rb][r]);
+    }
+    // D2 of the pair (i, i) needs no special case: the norms come from the same
+    // MFMA chain as the dot products, so it is fma(-2, n_i, 2 n_i) = 0 exactly.
     __device__ __forceinline__ void tile(const f4 (&acc)[RB][CB], const float *nrm, const int32_t *, const float *,
                                          int64_t j0) {
-        const bool diag = self && (j0 < qhi) && (j0 + RB * 16 > qlo);
-        if (diag)
-            tile_impl<true>(acc, nrm, j0);
-        else
-            tile_impl<false>(acc, nrm, j0);
-    }
-    template <bool DIAG>
-    __device__ __forceinline__ float dist2(const f4 (&acc)[RB][CB], const f4 (&nb4)[RB], int rb, int r, int cb,
-                                           int32_t j) const {
-        float d2 = fmaf(-2.f, acc[rb][cb][r], nq[cb] + nb4[rb][r]);
-        if (DIAG && j == qrow[cb]) d2 = 0.f;
-        return d2;
-    }
-    template <bool DIAG>
-    __device__ __forceinline__ void tile_impl(const f4 (&acc)[RB][CB], const float *nrm, int64_t j0) {
         f4 nb4[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) nb4[rb] = *reinterpret_cast<const f4 *>(nrm + rb * 16 + 4 * g);
+        float adm[CB]; // admission bound shared by the four lanes of the column
         bool hit[CB];
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) hit[cb] = false;
+        for (int cb = 0; cb < CB; ++cb) {
+            // list entries are >= 0 or +inf (clamped on insertion)
+            adm[cb] = fminf(group_min_nonneg(thr[cb]), group_max_nonneg(qj[cb]));
+            hit[cb] = false;
+        }
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+        for (int cb = 0; cb < CB; ++cb) {
+            float mn = INFINITY;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+            for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    const int32_t j = (int32_t)(j0 + rb * 16 + 4 * g + r);
-                    hit[cb] |= dist2<DIAG>(acc, nb4, rb, r, cb, j) < thr[cb];
-                }
+                for (int r = 0; r < 4; ++r) mn = fminf(mn, dist2(acc, nb4, rb, r, cb));
+            hit[cb] = mn <= adm[cb];
+        }
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             if (!hit[cb]) continue;
@@ -323,11 +384,12 @@ template <int K, int CB, int RB> struct EpiKnn {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int32_t j = (int32_t)(j0 + rb * 16 + 4 * g + r);
-                    const float d2 = dist2<DIAG>(acc, nb4, rb, r, cb, j);
-                    if (d2 < L.d[K - 1]) L.push_ascending(d2 > 0.f ? d2 : 0.f, j);
+                    const float d2 = dist2(acc, nb4, rb, r, cb);
+                    if (d2 <= adm[cb] && d2 < L.d[K - 1]) L.push_ascending(d2 > 0.f ? d2 : 0.f, j);
                 }
             store(cb, L);
             thr[cb] = L.d[K - 1];
+            qj[cb] = L.d[J];
         }
     }
 };
@@ -387,9 +449,6 @@ void knn_tile_kernel(KnnArgs a) {
         epi.qrow[cb] = (int32_t)(a.q0 + ql);
     }
     epi.init();
-    epi.qlo = a.q0 + qbase;
-    epi.qhi = a.q0 + (qbase + QT < a.nq ? qbase + QT : a.nq);
-    epi.self = a.self;
     epi.g = g;
 
     const int64_t tb = a.tiles * split / a.splits, te = a.tiles * (split + 1) / a.splits;
