@@ -117,10 +117,12 @@ KnnPlan plan_knn(int64_t n, int64_t m, int d, int k, int64_t max_chunk_dots) {
     return p;
 }
 
-size_t knn_ws(const KnnPlan &p, int64_t n, int64_t m, bool self, Carver &c, float **nx, float **ny, Entry **part) {
+size_t knn_ws(const KnnPlan &p, int64_t n, int64_t m, bool self, Carver &c, float **nx, float **ny, Entry **part,
+              int32_t **idx_scratch = nullptr, int k = 0) {
     *nx = c.take<float>(n);
     *ny = self ? *nx : c.take<float>(m);
     *part = p.splits > 1 ? c.take<Entry>((size_t)p.rows * p.splits * p.K) : nullptr;
+    if (idx_scratch) *idx_scratch = c.take<int32_t>((size_t)n * k);
     return c.used;
 }
 
@@ -167,6 +169,10 @@ int run_knn(const KnnPlan &p, const float *X, int64_t ldx, int64_t n, const floa
         if (p.splits > 1) {
             a.out_mode = out_mode;
             EKH_HIP(launch_knn_merge(p.K, a, s));
+        }
+        if (out_mode == kOutKnn) {
+            a.out_mode = out_mode;
+            EKH_HIP(launch_knn_rescore(p.K, a, s));
         }
     }
     return EKH_OK;
@@ -249,7 +255,8 @@ size_t ekh_knn_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t k, int64
     Carver c(nullptr);
     float *nx, *ny;
     Entry *part;
-    return knn_ws(p, n, m, false, c, &nx, &ny, &part);
+    int32_t *idx;
+    return knn_ws(p, n, m, false, c, &nx, &ny, &part, &idx, k);
 }
 
 int ekh_knn(const float *X, int64_t ldx, int64_t n, const float *Y, int64_t ldy, int64_t m, int32_t d, int32_t k,
@@ -268,10 +275,11 @@ int ekh_knn(const float *X, int64_t ldx, int64_t n, const float *Y, int64_t ldy,
     Carver c(ws);
     float *nx, *ny;
     Entry *part;
-    knn_ws(p, n, m, false, c, &nx, &ny, &part);
+    int32_t *idx_scratch;
+    knn_ws(p, n, m, false, c, &nx, &ny, &part, &idx_scratch, k);
     if (self) ny = nx;
-    return run_knn(p, X, ldx, n, Y, ldy, m, d, self, kOutKnn, k, 0, out_idx, out_dist, nullptr, nx, ny, part,
-                   (hipStream_t)stream);
+    return run_knn(p, X, ldx, n, Y, ldy, m, d, self, kOutKnn, k, 0, out_idx ? out_idx : idx_scratch, out_dist,
+                   nullptr, nx, ny, part, (hipStream_t)stream);
 }
 
 size_t ekh_core_workspace_bytes(int64_t n, int32_t d, int32_t min_samples) {

@@ -93,6 +93,7 @@ struct KnnArgs {
 hipError_t launch_norms(const float *X, int64_t ldx, int64_t n, int d, float *out, hipStream_t s);
 hipError_t launch_knn_tile(int K, int QM, const KnnArgs &a, hipStream_t s);
 hipError_t launch_knn_merge(int K, const KnnArgs &a, hipStream_t s);
+hipError_t launch_knn_rescore(int K, const KnnArgs &a, hipStream_t s);
 
 // ---- Boruvka ---------------------------------------------------------------
 constexpr uint64_t kNoEdge = ~0ull;

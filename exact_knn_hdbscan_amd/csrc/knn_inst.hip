@@ -31,6 +31,12 @@ template <> hipError_t launch_knn_tile_k<EKH_KNN_K>(int QM, const KnnArgs &a, hi
     }
 }
 
+template <> hipError_t launch_knn_rescore_k<EKH_KNN_K>(const KnnArgs &a, hipStream_t s) {
+    const int bs = 128;
+    hipLaunchKernelGGL(knn_rescore_kernel<EKH_KNN_K>, dim3((unsigned)((a.nq + bs - 1) / bs)), dim3(bs), 0, s, a);
+    return hipGetLastError();
+}
+
 template <> hipError_t launch_knn_merge_k<EKH_KNN_K>(const KnnArgs &a, hipStream_t s) {
     const int bs = 256;
     hipLaunchKernelGGL(knn_merge_kernel<EKH_KNN_K>, dim3((unsigned)((a.nq + bs - 1) / bs)), dim3(bs), 0, s, a);

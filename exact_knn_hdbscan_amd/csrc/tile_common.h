@@ -482,7 +482,36 @@ template <int K> __global__ void knn_merge_kernel(KnnArgs a) {
     write_list<K>(a, L, a.q0 + ql, 0); // a.out_mode is the final mode here
 }
 
+// Reported kNN distances: the selected neighbours' D2 recomputed by direct
+// differences, sum_f (q_f - y_f)^2 with fmaf in feature order, which carries no
+// cancellation error; each row is then sorted by (that D2, index).  The
+// neighbour set itself is the one the GEMM-form D2 selected.
+template <int K> __global__ void knn_rescore_kernel(KnnArgs a) {
+    const int64_t ql = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (ql >= a.nq) return;
+    const int64_t q = a.q0 + ql;
+    TopK<K> L;
+    L.clear();
+    for (int t = 0; t < a.k_out; ++t) {
+        const int32_t j = a.out_idx[q * a.k_out + t];
+        float s = 0.f;
+        for (int f = 0; f < a.d; ++f) {
+            const float v = a.Q[(int64_t)f * a.ldq + q] - a.B[(int64_t)f * a.ldb + j];
+            s = fmaf(v, v, s);
+        }
+        L.push_any(s, j);
+    }
+#pragma unroll
+    for (int t = 0; t < K; ++t) {
+        if (t < a.k_out) {
+            a.out_idx[q * a.k_out + t] = L.i[t];
+            if (a.out_dist) a.out_dist[q * a.k_out + t] = sqrt_rn(L.d[t]);
+        }
+    }
+}
+
 template <int K> hipError_t launch_knn_tile_k(int QM, const KnnArgs &a, hipStream_t s);
+template <int K> hipError_t launch_knn_rescore_k(const KnnArgs &a, hipStream_t s);
 template <int K> hipError_t launch_knn_merge_k(const KnnArgs &a, hipStream_t s);
 
 } // namespace ekh

@@ -50,6 +50,19 @@ hipError_t launch_knn_tile(int K, int QM, const KnnArgs &a, hipStream_t s) {
     }
 }
 
+hipError_t launch_knn_rescore(int K, const KnnArgs &a, hipStream_t s) {
+    if (a.nq <= 0) return hipSuccess;
+    switch (K) {
+    case 2: return launch_knn_rescore_k<2>(a, s);
+    case 4: return launch_knn_rescore_k<4>(a, s);
+    case 8: return launch_knn_rescore_k<8>(a, s);
+    case 11: return launch_knn_rescore_k<11>(a, s);
+    case 16: return launch_knn_rescore_k<16>(a, s);
+    case 32: return launch_knn_rescore_k<32>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_knn_merge(int K, const KnnArgs &a, hipStream_t s) {
     if (a.nq <= 0) return hipSuccess;
     switch (K) {

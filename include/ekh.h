@@ -81,8 +81,12 @@ size_t ekh_knn_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t k, int64
  *      (same pointer, ld and size) the set is its own database and the pair
  *      (i, i) has D2 = 0 exactly; otherwise no pair is special.
  *  k: 1 <= k <= min(m, EKH_MAX_K).  d: 1 <= d <= EKH_MAX_DIM.
- *  out_idx [n, k] int32 (row-major): indices into Y, rows ascending under
- *      (D2, index).  out_dist [n, k] float32: sqrt_rn(D2).  Either may be NULL.
+ *  out_idx [n, k] int32 (row-major): indices into Y.  out_dist [n, k]
+ *      float32.  Either may be NULL.  The k neighbours are the k smallest under
+ *      (D2, index) with D2 in the GEMM form above; their reported distance is
+ *      sqrt_rn of D2 recomputed by direct differences, sum_f (x_f - y_f)^2 with
+ *      fmaf in feature order (free of the GEMM form's cancellation error), and
+ *      each row is ascending under (that D2, index).
  *  max_chunk_dots: if > 0, the rows go in chunks of at most
  *      max_chunk_dots / m rows (at least one row tile), each chunk a separate
  *      launch sequence whose scratch is sized for that chunk (MAX_CHUNK_DOTS on

@@ -49,9 +49,11 @@ def true_sqdist(X, rows, Y, idx):
     return out
 
 
-def check_knn(X, Y, k, gi, gd, rows=None, report=None):
+def check_knn(X, Y, k, gi, gd, rows=None, report=None, rescored=False):
     """gi, gd: GPU [n, k] (indices into Y, float32 distances) for all rows of X
-    (or for ``rows`` only, in that order)."""
+    (or for ``rows`` only, in that order).  ``rescored``: the distances were
+    recomputed by direct differences (ekh_knn), so they must meet the 1e-5
+    relative bound with no floor, and each row must ascend in them."""
     d, n = X.shape
     m = Y.shape[1]
     rows = np.arange(n) if rows is None else np.asarray(rows)
@@ -90,6 +92,11 @@ def check_knn(X, Y, k, gi, gd, rows=None, report=None):
     derr = np.abs(g2 - t2)
     bad = derr > 2 * REL_D * t2 + eps_g
     assert not bad.any(), "distance error beyond tolerance at %d entries" % bad.sum()
+    if rescored:
+        dt = np.sqrt(t2)
+        bad = np.abs(gd.astype(np.float64) - dt) > REL_D * dt
+        assert not bad.any(), "direct-difference distance beyond 1e-5 relative at %d entries" % bad.sum()
+        assert np.all(np.diff(gd, axis=1) >= 0), "rows must ascend in the reported distance"
     if report is not None:
         rel = np.abs(gd.astype(np.float64) - np.sqrt(t2)) / np.maximum(np.sqrt(t2), 1e-300)
         report.update(isolated=int(iso.sum()), entries=int(iso.size), max_rel_dist=float(rel[t2 > 0].max(initial=0)),

@@ -63,7 +63,7 @@ def test_knn_sections_full_size(name):
     knn_properties(i, dd, Y.shape[1])
     rows = sample_rows(X.shape[1], 300, 1)
     rep = {}
-    check_knn(X, Y, k, i[rows], dd[rows], rows=rows, report=rep)
+    check_knn(X, Y, k, i[rows], dd[rows], rows=rows, report=rep, rescored=True)
     say("report", rep)
     # subset members (every 10th point) find themselves first, within the floor
     own = i[::10, 0] == np.arange(Y.shape[1])
@@ -79,7 +79,7 @@ def test_knn_section_reverse_orientation():
     i, dd = host(i), host(dd)
     knn_properties(i, dd, X.shape[1])
     rows = sample_rows(Y.shape[1], 300, 2)
-    check_knn(Y, X, 10, i[rows], dd[rows], rows=rows)
+    check_knn(Y, X, 10, i[rows], dd[rows], rows=rows, rescored=True)
 
 
 def _golden(name):

@@ -15,13 +15,13 @@ def test_knn_tiny_self():
     X = datagen.make("tiny_2000x60")["X"]
     say("knn tiny 2000x60 k=10, X and Y separate copies")
     i, dd = ekh.knn(dev(X), dev(X), 10)
-    check_knn(X, X, 10, host(i), host(dd))
+    check_knn(X, X, 10, host(i), host(dd), rescored=True)
     say("knn tiny 2000x60 self k=10")
     # the same tensor as X and Y makes the set its own database
     Xg = dev(X)
     i, dd = ekh.knn(Xg, Xg, 10)
     rep = {}
-    check_knn(X, X, 10, host(i), host(dd), report=rep)
+    check_knn(X, X, 10, host(i), host(dd), report=rep, rescored=True)
     say("report", rep)
     assert np.all(host(i)[:, 0] == np.arange(2000))
     assert np.all(host(dd)[:, 0] == 0)
@@ -33,7 +33,7 @@ def test_knn_odd_sizes_and_leading_dimension():
     Y = datagen.gaussian_mixture(777, 61, 7, seed=2)
     say("knn odd n=2001 m=777 d=61 ld padded")
     i, dd = ekh.knn(dev(X, ld=2011), dev(Y, ld=781), 10)
-    check_knn(X, Y, 10, host(i), host(dd))
+    check_knn(X, Y, 10, host(i), host(dd), rescored=True)
 
 
 @pytest.mark.parametrize("d", [1, 3, 17, 60, 64, 65, 102, 128, 129, 200, 256])
@@ -42,7 +42,7 @@ def test_knn_dimensions(d):
     Y = datagen.gaussian_mixture(517, d, 5, seed=d + 1000)
     say("knn d=%d" % d)
     i, dd = ekh.knn(dev(X), dev(Y), 10)
-    check_knn(X, Y, 10, host(i), host(dd))
+    check_knn(X, Y, 10, host(i), host(dd), rescored=True)
 
 
 @pytest.mark.parametrize("k", [1, 2, 3, 8, 10, 11, 12, 16, 17, 32])
@@ -51,7 +51,7 @@ def test_knn_k_values(k):
     say("knn self k=%d" % k)
     Xg = dev(X)
     i, dd = ekh.knn(Xg, Xg, k)
-    check_knn(X, X, k, host(i), host(dd))
+    check_knn(X, X, k, host(i), host(dd), rescored=True)
 
 
 @pytest.mark.parametrize("d", [5, 61, 100, 200])
@@ -79,11 +79,11 @@ def test_knn_k_equals_m_and_n():
     Y = datagen.random_uniform(20, 9, seed=4)
     say("knn k = m")
     i, dd = ekh.knn(dev(X), dev(Y), 20)
-    check_knn(X, Y, 20, host(i), host(dd))
+    check_knn(X, Y, 20, host(i), host(dd), rescored=True)
     assert all(sorted(r) == list(range(20)) for r in host(i).tolist())
     Xg = dev(X)
     i, dd = ekh.knn(Xg, Xg, 31)
-    check_knn(X, X, 31, host(i), host(dd))
+    check_knn(X, X, 31, host(i), host(dd), rescored=True)
 
 
 def test_knn_duplicates():
@@ -92,7 +92,7 @@ def test_knn_duplicates():
     Xg = dev(X)
     i, dd = ekh.knn(Xg, Xg, 12)
     hi = host(i)
-    check_knn(X, X, 12, hi, host(dd))
+    check_knn(X, X, 12, hi, host(dd), rescored=True)
     for r in range(9):
         assert sorted(hi[r, :9].tolist()) == list(range(9))
 
@@ -104,7 +104,7 @@ def test_knn_chunk_and_split_invariance():
     say("knn chunking invariance")
     ref_i, ref_d = ekh.knn(Xg, Yg, 10)
     ref_i, ref_d = host(ref_i), host(ref_d)
-    check_knn(X, Y, 10, ref_i, ref_d)
+    check_knn(X, Y, 10, ref_i, ref_d, rescored=True)
     for dots in (1, 2500 * 128, 2500 * 1000, 2500 * 4096):
         i, dd = ekh.knn(Xg, Yg, 10, max_chunk_dots=dots)
         np.testing.assert_array_equal(host(i), ref_i)
