@@ -24,7 +24,30 @@ sys.path.insert(0, ROOT)
 
 METRIC = "kNN pair-distances/s + Borůvka MST time at 500k×61; % fp32 MFMA peak"
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X published dense fp32 matrix peak
+COPY_BYTES = 1 << 30  # size of the calibration copy of --pmc-probe
 HBM_PEAK_GBS = 8000.0
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "knn_tile_traffic_clips_500000x61.md")
+KNN_SOURCES = ["exact_knn_hdbscan_amd/csrc/tile_common.h", "exact_knn_hdbscan_amd/csrc/knn_inst.hip",
+               "exact_knn_hdbscan_amd/csrc/ekh_internal.h"]
+
+
+def stored_traffic():
+    """HBM bytes per kNN-tile launch from the committed counter summary, or None
+    if the kernel sources have changed since the counters were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        h = hashlib.sha256(b"".join(open(os.path.join(ROOT, f), "rb").read() for f in KNN_SOURCES)).hexdigest()
+    except OSError:
+        return None
+    m_t = re.search(r"^traffic_bytes_per_launch: (\d+)", text, re.M)
+    m_h = re.search(r"^kernel_source_sha256: ([0-9a-f]+)", text, re.M)
+    if not m_t or not m_h or m_h.group(1) != h:
+        return None
+    return int(m_t.group(1))
 
 
 def cpu_baseline(X, k, budget_s=15.0):
@@ -59,6 +82,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="clips_500000x61")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="for counter runs: one plain copy of COPY_BYTES (calibration) and one pass of the path")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -86,6 +111,19 @@ def main():
         t_knn_end.record()
         out = ekh.mst_boruvka(Xg, core, ms, ni, nd2, return_stats=True, workspace=ws_mst)
         return out, t_knn_end
+
+    if args.pmc_probe:
+        # calibration: a device-to-device copy that reads and writes COPY_BYTES each
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        step()
+        torch.cuda.synchronize()
+        print("pmc probe done: copy of %d bytes, one pass of %s" % (COPY_BYTES, args.workload), flush=True)
+        return
 
     for _ in range(args.warmup):
         step()
@@ -145,7 +183,9 @@ def main():
         "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
                      "launches": dom["launches"], "avg_launch_ms": dom["ms"] / max(dom["launches"], 1),
-                     "traffic": None},
+                     "traffic": (stored_traffic() if dom_name == "knn_tile_kernel"
+                                 and args.workload == "clips_500000x61" else None),
+                     "traffic_unit": "bytes per launch (HBM, counters scaled by a copy of known size)"},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(X, ms + 1)
