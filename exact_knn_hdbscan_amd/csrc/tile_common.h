@@ -47,7 +47,8 @@ template <int QM> struct Tile {
 // (row-major: [row][feature]) and hands each tile's accumulator blocks to
 // epi.tile().  The loop is software-pipelined: while the MFMAs of tile t run
 // into one accumulator set, the epilogue consumes tile t - 1 from the other,
-// and the global loads of tile t + 2 are in flight.  Per-row norms (and, with
+// and the global loads of tile t + 2 are in flight.  Slots: tile t's norms are
+// in slot (t - t_begin) mod 3.  Per-row norms (and, with
 // PAYLOAD, component labels and core distances) live in a three-slot ring so
 // that tile t - 1's stay valid while tile t + 1's are stored.  FULL: the
 // dimension fills all QM k-steps, so the k-loop has no runtime guard.
@@ -72,36 +73,43 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
         float v[T::PF];
         float n, core;
         int32_t comp;
+        bool jv, nv; // row in range (data, per-row payload)
     };
+    // Loads are unconditional and straight-line (addresses clamped into range);
+    // the range masks are applied when the values are stored, so the loads of
+    // the next tiles stay in flight and the compiler can wait for exactly the
+    // loads a store needs.
     auto load = [&](Pref &P, int64_t t) {
-        const int64_t j = t * T::TR + lrow;
-        const bool jv = j < m;
+        const int64_t tt = t < t_end ? t : t_end - 1;
+        const int64_t j = tt * T::TR + lrow;
+        P.jv = j < m;
+        const int64_t jc = P.jv ? j : m - 1;
 #pragma unroll
         for (int p = 0; p < T::PF; ++p) {
             const int f = lf0 + p * T::FSTEP;
-            P.v[p] = (jv && f < d) ? B[(int64_t)f * ldb + j] : 0.f;
+            const int fc = f < d ? f : d - 1;
+            P.v[p] = B[(int64_t)fc * ldb + jc];
         }
-        if (tid < T::TR) {
-            const int64_t jj = t * T::TR + tid;
-            const bool v = jj < m;
-            P.n = v ? nrm_b[jj] : INFINITY; // padding rows never qualify
-            if (PAYLOAD) {
-                P.comp = v ? comp_b[jj] : -1;
-                P.core = v ? core_b[jj] : INFINITY;
-            }
+        const int64_t jj = tt * T::TR + (tid % T::TR);
+        P.nv = jj < m;
+        const int64_t jjc = P.nv ? jj : m - 1;
+        P.n = nrm_b[jjc];
+        if (PAYLOAD) {
+            P.comp = comp_b[jjc];
+            P.core = core_b[jjc];
         }
     };
     auto store = [&](const Pref &P, int buf, int slot) {
 #pragma unroll
         for (int p = 0; p < T::PF; ++p) {
             const int f = lf0 + p * T::FSTEP;
-            if (FULL || f < fused) sm_tile[buf][lrow * T::RS + f] = P.v[p];
+            if (FULL || f < fused) sm_tile[buf][lrow * T::RS + f] = (P.jv && f < d) ? P.v[p] : 0.f;
         }
         if (tid < T::TR) {
-            sm_nrm[slot][tid] = P.n;
+            sm_nrm[slot][tid] = P.nv ? P.n : INFINITY; // padding rows never qualify
             if (PAYLOAD) {
-                sm_comp[slot][tid] = P.comp;
-                sm_core[slot][tid] = P.core;
+                sm_comp[slot][tid] = P.nv ? P.comp : -1;
+                sm_core[slot][tid] = P.nv ? P.core : INFINITY;
             }
         }
     };
@@ -158,33 +166,34 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
     // ring slot of tile t is (t - t_begin) mod 3, tracked without division
     auto next3 = [](int x) { return x == 2 ? 0 : x + 1; };
     Pref P0, P1;
-    P0.n = P1.n = 0.f;
-    P0.core = P1.core = 0.f;
-    P0.comp = P1.comp = -1;
     load(P0, t_begin);
     store(P0, 0, 0);
-    if (t_begin + 1 < t_end) load(P1, t_begin + 1);
+    load(P1, t_begin + 1);
     __syncthreads();
     f4 accA[T::RB][CB], accB[T::RB][CB];
-    int buf = 0;
-    int sl = 0; // slot of tile t
-    for (int64_t t = t_begin; t < t_end; t += 2) {
-        // slots of tiles t + 1 and t + 2; tile t - 1 shares t + 2's slot (its
-        // epilogue runs before t + 2 is stored there, with a barrier between)
-        const int sl1 = next3(sl), sl2 = next3(sl1), slp = sl2;
-        // tile t into accA; epilogue of tile t - 1 (accB)
-        if (t + 2 < t_end) load(P0, t + 2);
-        mma(buf, accA);
-        if (t > t_begin) finish(accB, t - 1, slp);
-        if (t + 1 < t_end) store(P1, buf ^ 1, sl1);
+    // first tile: no previous epilogue
+    load(P0, t_begin + 2);
+    mma(0, accA);
+    if (t_begin + 1 < t_end) store(P1, 1, 1);
+    __syncthreads();
+    int buf = 1;
+    int sl = 1; // slot of tile t below
+    // Steady state, two tiles per trip (the accumulator and prefetch sets
+    // alternate): the MFMAs of tile t and the epilogue of tile t - 1 are
+    // straight-line neighbours, so the scheduler can interleave them.
+    for (int64_t t = t_begin + 1; t < t_end; t += 2) {
+        const int sl1 = next3(sl), sl2 = next3(sl1), slp = sl2; // t + 1, t + 2, t - 1
+        load(P1, t + 2);
+        mma(buf, accB);
+        finish(accA, t - 1, slp);
+        if (t + 1 < t_end) store(P0, buf ^ 1, sl1);
         __syncthreads();
         buf ^= 1;
         if (t + 1 >= t_end) break;
-        // tile t + 1 into accB; epilogue of tile t (accA)
-        if (t + 3 < t_end) load(P1, t + 3);
-        mma(buf, accB);
-        finish(accA, t, sl);
-        if (t + 2 < t_end) store(P0, buf ^ 1, sl2);
+        load(P0, t + 3);
+        mma(buf, accA);
+        finish(accB, t, sl);
+        if (t + 2 < t_end) store(P1, buf ^ 1, sl2);
         __syncthreads();
         buf ^= 1;
         sl = sl2;
