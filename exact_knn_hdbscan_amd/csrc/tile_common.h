@@ -38,9 +38,9 @@ template <int QM> struct Tile {
     static constexpr int RB = TR / 16;          // 16-row blocks per tile
     static constexpr int FD = QM * 4;           // features held (d <= FD)
     static constexpr int RS = FD + 4;           // LDS row stride in floats: 16-byte reads of 8 rows hit distinct banks
-    static constexpr int FSTEP = kThreads / TR; // feature rows per load pass
+    static constexpr int FSTEP = kThreads / TR; // threads per row: thread q of a row holds feature chunks q, q + FSTEP, ...
     static constexpr int PF = FD / FSTEP;       // prefetch registers per thread
-    static_assert(FD % FSTEP == 0, "tile shape");
+    static_assert(FD % (4 * FSTEP) == 0, "tile shape");
 };
 
 // Streams database tiles [t_begin, t_end) through a double-buffered LDS tile
@@ -65,7 +65,11 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, g = lane >> 4, li = lane & 15;
-    const int lrow = tid % T::TR, lf0 = tid / T::TR;
+    // loader: thread (lrow, lq) reads 4-feature chunks lq, lq + FSTEP, ... of row
+    // lrow; a wave's loads cover 32 consecutive rows of two feature rows each
+    // (coalesced), and each chunk goes to LDS as one 16-byte store (eight
+    // consecutive rows of one chunk lie in distinct banks, RS = 4 mod 32).
+    const int lrow = tid % T::TR, lq = tid / T::TR;
     const int qs = FULL ? QM : 4 * chunks; // k-steps run
     const int fused = 4 * qs;
 
@@ -86,7 +90,7 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
         const int64_t jc = P.jv ? j : m - 1;
 #pragma unroll
         for (int p = 0; p < T::PF; ++p) {
-            const int f = lf0 + p * T::FSTEP;
+            const int f = 4 * (lq + (p >> 2) * T::FSTEP) + (p & 3);
             const int fc = f < d ? f : d - 1;
             P.v[p] = B[(int64_t)fc * ldb + jc];
         }
@@ -101,9 +105,14 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
     };
     auto store = [&](const Pref &P, int buf, int slot) {
 #pragma unroll
-        for (int p = 0; p < T::PF; ++p) {
-            const int f = lf0 + p * T::FSTEP;
-            if (FULL || f < fused) sm_tile[buf][lrow * T::RS + f] = (P.jv && f < d) ? P.v[p] : 0.f;
+        for (int h = 0; h < T::PF / 4; ++h) {
+            const int f0 = 4 * (lq + h * T::FSTEP);
+            if (FULL || f0 < fused) {
+                f4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (P.jv && f0 + e < d) ? P.v[4 * h + e] : 0.f;
+                *reinterpret_cast<f4 *>(sm_tile[buf] + lrow * T::RS + f0) = v;
+            }
         }
         if (tid < T::TR) {
             sm_nrm[slot][tid] = P.nv ? P.n : INFINITY; // padding rows never qualify
