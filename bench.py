@@ -7,7 +7,9 @@ shortcuts, edges sorted).  Inputs are resident in HBM before the timed region.
 
 Prints one JSON line.  ``value`` is distance pairs (n^2, the exact self-kNN's
 pair count) per second of the WHOLE step; the kNN-only rate, MST time and the
-per-kernel roofline of the dominant kernel are reported beside it.
+per-kernel roofline of the dominant kernel are reported beside it, and so is
+the host HDBSCAN tail (condensed tree, excess of mass, labels) on the last
+step's tree, which is not part of the step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -26,6 +28,7 @@ METRIC = "kNN pair-distances/s + Borůvka MST time at 500k×61; % fp32 MFMA peak
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X published dense fp32 matrix peak
 COPY_BYTES = 1 << 30  # size of the calibration copy of --pmc-probe
 HBM_PEAK_GBS = 8000.0
+TAIL_MIN_CLUSTER_SIZE = 20  # the HDBSCAN page's results use min_cluster_size = 20
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "knn_tile_traffic_clips_500000x61.md")
@@ -187,8 +190,23 @@ def main():
                                  and args.workload == "clips_500000x61" else None),
                      "traffic_unit": "bytes per launch (HBM, counters scaled by a copy of known size)"},
     }
+    # HDBSCAN tail on the host (outside the step): the last step's tree copied to
+    # the host and condensed with min_cluster_size 20 (the page's setting)
+    t0 = time.perf_counter()
+    lo_h, hi_h, w_h = lo.cpu().numpy(), hi.cpu().numpy(), w.cpu().numpy()
+    labels = ekh.hdbscan_tail(lo_h, hi_h, w_h, TAIL_MIN_CLUSTER_SIZE)
+    tail_ms = 1000.0 * (time.perf_counter() - t0)
+    result["hdbscan_tail"] = {
+        "ms": tail_ms, "min_cluster_size": TAIL_MIN_CLUSTER_SIZE, "clusters": int(labels.max()) + 1,
+        "noise": int((labels < 0).sum()), "where": "host C++ (ekh_hdbscan_tail), device-to-host copy of the tree included",
+        "end_to_end_ms": ms_step + tail_ms}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(X, ms + 1)
+        from oracle import hdbscan_tail as otail
+        t0 = time.perf_counter()
+        otail.hdbscan_tail(lo_h.astype(np.int64), hi_h.astype(np.int64), w_h.astype(np.float64), n,
+                           TAIL_MIN_CLUSTER_SIZE)
+        result["hdbscan_tail"]["oracle_ms"] = 1000.0 * (time.perf_counter() - t0)
     print(json.dumps(result), flush=True)
 
 

@@ -1,4 +1,4 @@
-"""Exact kNN, HDBSCAN core distances and Boruvka MST on MI355X (gfx950).
+"""Exact kNN, HDBSCAN core distances, Boruvka MST and the HDBSCAN tail on MI355X (gfx950).
 
 The compute lives in the HIP library ``libekh.so`` (C ABI declared in
 ``include/ekh.h``); ``exact_knn_hdbscan_amd.binding`` marshals torch tensors
@@ -6,7 +6,7 @@ to it.  The binding is loaded on first use of one of the entry points below so
 that ``exact_knn_hdbscan_amd.datagen`` can be imported without a GPU.
 """
 _ENTRY_POINTS = ("knn", "core_distances", "mst_boruvka", "knn_workspace_bytes", "core_workspace_bytes",
-                 "mst_workspace_bytes", "library", "MstStats", "EkhError", "kernel_timer")
+                 "mst_workspace_bytes", "hdbscan_tail", "library", "MstStats", "EkhError", "kernel_timer")
 
 __all__ = list(_ENTRY_POINTS)
 

@@ -62,6 +62,10 @@ class MstStats(ctypes.Structure):
         }
 
 
+class HdbscanInfo(ctypes.Structure):
+    _fields_ = [("n_entries", ctypes.c_int64), ("n_clusters", ctypes.c_int32), ("n_selected", ctypes.c_int32)]
+
+
 class EkhError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__("ekh error %d: %s" % (code, msg))
@@ -92,6 +96,7 @@ def library() -> ctypes.CDLL:
             lib.ekh_mst_workspace_bytes.restype = _sz
             lib.ekh_mst_boruvka.argtypes = [_p, _i64, _i64, _i32, _p, _i32, _p, _p, _u32, _p, _p, _p, _p, _p, _sz,
                                             _p]
+            lib.ekh_hdbscan_tail.argtypes = [_p, _p, _p, _i64, _i32, _p, _p, _p, _p, _p, _p, _p]
             lib.ekh_timer_enable.argtypes = [ctypes.c_int]
             lib.ekh_timer_read.argtypes = [ctypes.c_int, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double),
                                            ctypes.POINTER(ctypes.c_double)]
@@ -211,6 +216,47 @@ def mst_boruvka(X: torch.Tensor, core: torch.Tensor, min_samples: int, nbr_idx: 
     if return_stats:
         return lo, hi, w, stats.as_dict()
     return lo, hi, w
+
+
+def hdbscan_tail(lo, hi, w, min_cluster_size: int, return_tree: bool = False):
+    """Cluster labels from a spanning tree (ekh_hdbscan_tail, host code).
+
+    ``lo``, ``hi`` (int32) and ``w`` (float32) are the n - 1 tree edges, e.g.
+    the outputs of mst_boruvka (torch tensors on any device, or numpy arrays;
+    device tensors are copied to the host here).  Returns labels (numpy int32
+    [n], -1 = noise); with ``return_tree`` also a dict with the condensed tree
+    (parent, child, lambda, size), the stability of every cluster and the
+    counts.
+    """
+    import numpy as np
+
+    def host(a, dt):
+        if isinstance(a, torch.Tensor):
+            a = a.detach().to("cpu").numpy()
+        return np.ascontiguousarray(a, dtype=dt)
+
+    lo, hi, w = host(lo, np.int32), host(hi, np.int32), host(w, np.float32)
+    if not (lo.ndim == hi.ndim == w.ndim == 1 and lo.shape == hi.shape == w.shape):
+        raise ValueError("lo, hi and w must be 1-D arrays of equal length")
+    n = lo.shape[0] + 1
+    labels = np.empty(n, np.int32)
+    info = HdbscanInfo()
+    if return_tree:
+        par = np.empty(2 * n, np.int64)
+        chi = np.empty(2 * n, np.int64)
+        lam = np.empty(2 * n, np.float64)
+        siz = np.empty(2 * n, np.int64)
+        st = np.empty(n, np.float64)
+        ptrs = [par.ctypes.data, chi.ctypes.data, lam.ctypes.data, siz.ctypes.data, st.ctypes.data]
+    else:
+        ptrs = [None] * 5
+    _check(library().ekh_hdbscan_tail(lo.ctypes.data, hi.ctypes.data, w.ctypes.data, n, min_cluster_size,
+                                      labels.ctypes.data, *ptrs, ctypes.byref(info)))
+    if not return_tree:
+        return labels
+    ne, nc = info.n_entries, info.n_clusters
+    return labels, {"parent": par[:ne], "child": chi[:ne], "lambda": lam[:ne], "size": siz[:ne],
+                    "stability": st[:nc], "n_clusters": nc, "n_selected": info.n_selected}
 
 
 class kernel_timer:

@@ -19,6 +19,9 @@ LIB = os.path.join(PKG, "libekh.so")
 KNN_KS = [2, 4, 8, 11, 16, 32]
 SOURCES = [("tile_kernels.hip", "tile_kernels", []), ("boruvka_kernels.hip", "boruvka_kernels", []),
            ("api.hip", "api", [])] + [("knn_inst.hip", "knn_k%d" % k, ["-DEKH_KNN_K=%d" % k]) for k in KNN_KS]
+# host-only C++ (no device code), built with g++; -ffp-contract=off keeps every
+# float64 expression as written (no fused multiply-adds)
+HOST_SOURCES = [("hdbscan_tail.cpp", "hdbscan_tail")]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no v_pk_*_f32 in generated code.
@@ -37,17 +40,21 @@ def hipcc() -> str:
 def _compile(job) -> str:
     src, name, extra = job
     obj = os.path.join(BUILD, name + ".o")
-    cmd = [hipcc()] + COMMON + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-ffp-contract=off", "-I", os.path.join(ROOT, "include"),
+               "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+    else:
+        cmd = [hipcc()] + COMMON + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr[-6000:]))
+        raise RuntimeError("compile failed for %s:\n%s" % (src, r.stderr[-6000:]))
     return obj
 
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), max(2, os.cpu_count() or 2))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(_compile, SOURCES + [(src, name, []) for src, name in HOST_SOURCES]))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

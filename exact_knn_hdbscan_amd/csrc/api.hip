@@ -5,6 +5,7 @@
 // is enqueued on the caller's stream; nothing here allocates device memory.
 #include "ekh.h"
 #include "ekh_internal.h"
+#include "host_error.h"
 
 #include <hip/hip_runtime.h>
 
@@ -33,6 +34,16 @@ int fail(int code, const char *fmt, ...) {
     g_err = buf;
     return code;
 }
+
+} // namespace
+
+// Sets the thread-local message for host-only sources of the library.
+int ekh::report_error(int code, const char *msg) {
+    g_err = msg;
+    return code;
+}
+
+namespace {
 
 #define EKH_HIP(call)                                                                                                  \
     do {                                                                                                               \

@@ -159,6 +159,55 @@ int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const flo
 /* ------------------------------------------------------------------ kernel timer (measurement) */
 
 /*
+ * HDBSCAN tail, on the HOST: spanning tree -> single-linkage hierarchy ->
+ * condensed tree -> excess-of-mass selection -> cluster labels.
+ * Source: "HDBSCAN", section "The algorithm on the device", last item (the
+ * hierarchy, its condensed tree and the excess-of-mass selection run on the
+ * host, in linear time) with the edge order of the same section; the steps
+ * are the standard HDBSCAN* definitions, with these conventions:
+ *  - the n - 1 edges are merged in ascending (w, lo, hi) order, one union each
+ *    (equal weights thus merge in index order, like the tree's own tie rule);
+ *  - lambda = 1 / w (float64; +inf for w = 0);
+ *  - walking the hierarchy down inside a cluster, a merge's child with at least
+ *    min_cluster_size points is large: both large -> two clusters are born at
+ *    that lambda; one large -> the other child's points leave at lambda; none
+ *    -> all points leave at lambda;
+ *  - clusters are numbered n (root), n + 1, ... breadth-first, the two children
+ *    of a split by ascending smallest point index;
+ *  - stability(c) = sum of size * (lambda - birth(c)) over c's condensed-tree
+ *    entries in ascending (parent, child) order, a term being 0 when lambda ==
+ *    birth(c);
+ *  - excess of mass, children first: a non-root cluster is kept when its
+ *    stability is >= the sum of its two children's best values (ties keep the
+ *    parent); the root is never selected; the selection is the kept clusters
+ *    with no kept ancestor, labelled 0, 1, ... in ascending id;
+ *  - a point's label is that of the selected cluster above it, else -1 (noise).
+ *
+ * lo, hi [n-1] int32 (lo < hi), w [n-1] float32: a spanning tree, e.g. the
+ *   output of ekh_mst_boruvka copied to the host (any edge order is accepted;
+ *   sorted input is used as is).  Host pointers, caller-owned, read only.
+ * out_labels [n] int32: host, written.
+ * ct_parent, ct_child, ct_size [2n] int64 and ct_lambda [2n] float64: the
+ *   condensed tree (children: point indices < n or cluster ids >= n), rows in
+ *   ascending (parent, child) order; all four NULL to skip.
+ * out_stability [n] float64 (nullable): stability of cluster n + i at [i].
+ * info (nullable): entries written, clusters in the condensed tree (root
+ *   included), clusters selected.
+ * Errors: EKH_EINVAL for n < 1, min_cluster_size < 2, a NULL array, lo >= hi
+ *   or out of range, a weight that is negative, NaN or infinite, or edges that
+ *   do not form a spanning tree.  No GPU work; thread-safe.
+ */
+typedef struct {
+    int64_t n_entries;  /* rows of the condensed tree */
+    int32_t n_clusters; /* clusters in the condensed tree, root included */
+    int32_t n_selected; /* clusters selected (labels 0 .. n_selected - 1) */
+} ekh_hdbscan_info;
+
+int ekh_hdbscan_tail(const int32_t *lo, const int32_t *hi, const float *w, int64_t n, int32_t min_cluster_size,
+                     int32_t *out_labels, int64_t *ct_parent, int64_t *ct_child, double *ct_lambda, int64_t *ct_size,
+                     double *out_stability, ekh_hdbscan_info *info);
+
+/*
  * Optional per-kernel timing with HIP events recorded on the launch stream
  * around every launch of the two dense kernels, for roofline figures.
  * kernel id: 0 = the kNN tile kernel, 1 = the Boruvka scan tile kernel.

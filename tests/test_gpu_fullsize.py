@@ -10,7 +10,10 @@ check is one of:
     edge on the path between its ends, up to the near-tie tolerance);
   * stored oracle summaries (tests/golden/*_oracle.json, written by
     tests/golden/make_golden.py from the oracle alone): total tree weight and
-    weight quantiles, core-distance sum and quantiles.
+    weight quantiles, core-distance sum and quantiles, and the HDBSCAN tail's
+    cluster count, noise count and cluster sizes on the oracle's own tree;
+  * the HDBSCAN tail of the library on the GPU's tree against the oracle's tail
+    on the same tree, exactly (the oracle's tail is linear and runs in seconds).
 """
 import json
 import os
@@ -24,6 +27,8 @@ import oracle
 from exact_knn_hdbscan_amd import datagen
 from gpu_util import dev, host, say
 from parity import REL_D, REL_GAP, check_core, check_knn, check_tree_shape, dist_floor, floor_sq, sq_norms
+from oracle import hdbscan_tail as otail
+from test_hdbscan_tail import assert_same
 from treecheck import PathMax
 
 pytestmark = [pytest.mark.gpu, pytest.mark.fullsize]
@@ -148,6 +153,38 @@ def test_core_and_mst_clips_full_size(name):
     np.testing.assert_allclose(cq, g["core_quantiles"], rtol=1e-4, atol=1e-4)
     eps_core = dist_floor(floor_sq(d, nx, nx.max()), core, core)
     assert abs(core.sum() - g["core_sum"]) <= REL_D * g["core_sum"] + eps_core.sum()
+
+
+@pytest.mark.parametrize("name", ["clips_100000x61", "clips_500000x61"])
+def test_hdbscan_tail_clips_full_size(name):
+    """Core distances and tree on the GPU, then the tail (min_cluster_size 20, the
+    page's setting): exactly the oracle's tail on the same tree; and close to the
+    oracle's tail on the oracle's own tree, which may differ where the two trees
+    take different, equally light edges (the page's "ties" section)."""
+    wl = workload(name)
+    X, ms = wl["X"], wl["min_samples"]
+    n = X.shape[1]
+    say("tail %s full size" % name)
+    Xg = dev(X)
+    core, ni, nd2 = ekh.core_distances(Xg, ms, return_neighbours=True)
+    lo, hi, w = ekh.mst_boruvka(Xg, core, ms, ni, nd2)
+    lo, hi, w = host(lo), host(hi), host(w)
+    labels, tree = ekh.hdbscan_tail(lo, hi, w, 20, return_tree=True)
+    ref = otail.hdbscan_tail(lo.astype(np.int64), hi.astype(np.int64), w.astype(np.float64), n, 20)
+    assert_same(labels, tree, ref, n)
+    sizes = np.sort(np.bincount(labels[labels >= 0]))
+    noise = int((labels < 0).sum())
+    say("clusters %d noise %d sizes %s" % (len(sizes), noise, sizes.tolist()[:8]))
+    assert len(sizes) >= 2
+    g = _golden(name)
+    if "hdbscan_n_clusters" not in g:
+        pytest.skip("stored oracle summary has no tail figures")
+    gs = np.array(g["hdbscan_cluster_sizes_sorted"])
+    say("oracle tree: clusters %d noise %d sizes %s" % (len(gs), g["hdbscan_noise"], gs.tolist()[:8]))
+    assert len(sizes) == g["hdbscan_n_clusters"]
+    tol = max(20, int(2e-3 * n))
+    assert abs(noise - g["hdbscan_noise"]) <= tol
+    assert np.abs(sizes - gs).max() <= tol
 
 
 def test_mst_tiny_workload_matches_prim():
