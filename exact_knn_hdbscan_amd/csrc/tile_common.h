@@ -337,6 +337,9 @@ template <int K, int CB, int RB> struct EpiKnn {
     float thr[CB]; // this lane's last entry
     float qj[CB];  // this lane's J-th entry
     float nq[CB];
+    float adm[CB];  // admission bound on D2 shared by the column's four lanes
+    float admq[CB]; // the same bound moved to nb - 2 s, widened by the rounding margin
+    bool dirty;     // this lane changed a list since adm was last formed
     int32_t qrow[CB];
     int g;
     int tid;
@@ -350,7 +353,10 @@ template <int K, int CB, int RB> struct EpiKnn {
             for (int t = 0; t < K; ++t) at(cb, t) = Entry{INFINITY, 0x7fffffff};
             thr[cb] = INFINITY;
             qj[cb] = INFINITY;
+            adm[cb] = INFINITY;
+            admq[cb] = INFINITY;
         }
+        dirty = false;
     }
     __device__ __forceinline__ void load(int cb, TopK<K> &L) {
 #pragma unroll
@@ -370,27 +376,39 @@ template <int K, int CB, int RB> struct EpiKnn {
     }
     // D2 of the pair (i, i) needs no special case: the norms come from the same
     // MFMA chain as the dot products, so it is fma(-2, n_i, 2 n_i) = 0 exactly.
+    //
+    // Fast test per element: t = fma(-2, s, nb) against admq = adm - nq, widened.
+    // If D2 = fma(-2, s, nq + nb) (two roundings) is <= adm, the point lies within
+    // sqrt(adm) of the query, so nb <= 2 nq + 2 adm, and every rounding error
+    // between D2 and t + nq is at most a few units of 2^-24 (nq + nb + adm); the
+    // widening by 2^-20 (adm + nq) covers it with room to spare.  The test only
+    // decides whether a lane looks at its candidates: those are then taken with
+    // the exact D2 and the exact bound, so results do not depend on the margin.
     __device__ __forceinline__ void tile(const f4 (&acc)[RB][CB], const float *nrm, const int32_t *, const float *,
                                          int64_t j0) {
+        constexpr float kWiden = 1.0f / 1048576.0f;
         f4 nb4[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) nb4[rb] = *reinterpret_cast<const f4 *>(nrm + rb * 16 + 4 * g);
-        float adm[CB]; // admission bound shared by the four lanes of the column
-        bool hit[CB];
+        // the bound changes only when a list of the wave changed (wave-uniform test)
+        if (__builtin_amdgcn_ballot_w64(dirty)) {
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            // list entries are >= 0 or +inf (clamped on insertion)
-            adm[cb] = fminf(group_min_nonneg(thr[cb]), group_max_nonneg(qj[cb]));
-            hit[cb] = false;
+            for (int cb = 0; cb < CB; ++cb) {
+                // list entries are >= 0 or +inf (clamped on insertion)
+                adm[cb] = fminf(group_min_nonneg(thr[cb]), group_max_nonneg(qj[cb]));
+                admq[cb] = fmaf(adm[cb], 1.0f + kWiden, -nq[cb] * (1.0f - kWiden));
+            }
+            dirty = false;
         }
+        bool hit[CB];
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             float mn = INFINITY;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) mn = fminf(mn, dist2(acc, nb4, rb, r, cb));
-            hit[cb] = mn <= adm[cb];
+                for (int r = 0; r < 4; ++r) mn = fminf(mn, fmaf(-2.f, acc[rb][cb][r], nb4[rb][r]));
+            hit[cb] = mn <= admq[cb];
         }
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
@@ -408,6 +426,7 @@ template <int K, int CB, int RB> struct EpiKnn {
             store(cb, L);
             thr[cb] = L.d[K - 1];
             qj[cb] = L.d[J];
+            dirty = true;
         }
     }
 };
