@@ -104,6 +104,7 @@ struct KnnPlan {
     int64_t tiles;  // database tiles
 };
 
+constexpr int64_t kMaxLd = int64_t(1) << 27;
 constexpr int64_t kTargetGroups = 1024; // workgroups per launch to aim for (256 CUs)
 constexpr int64_t kMinTilesPerSplit = 4;
 
@@ -142,6 +143,8 @@ int check_points(const float *X, int64_t ld, int64_t n, int d, const char *name)
     if (n < 1 || n > INT32_MAX) return fail(EKH_EINVAL, "%s: number of points %lld out of range", name, (long long)n);
     if (d < 1 || d > EKH_MAX_DIM) return fail(EKH_EINVAL, "%s: d = %d out of range [1, %d]", name, d, EKH_MAX_DIM);
     if (ld < n) return fail(EKH_EINVAL, "%s: leading dimension %lld < n = %lld", name, (long long)ld, (long long)n);
+    // the tile loads address four feature rows with a 32-bit byte offset
+    if (ld >= kMaxLd) return fail(EKH_EINVAL, "%s: leading dimension %lld >= 2^27 is not supported", name, (long long)ld);
     return EKH_OK;
 }
 

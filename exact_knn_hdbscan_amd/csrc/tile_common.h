@@ -77,42 +77,72 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
         float v[T::PF];
         float n, core;
         int32_t comp;
-        bool jv, nv; // row in range (data, per-row payload)
+        bool nv; // row in range
     };
-    // Loads are unconditional and straight-line (addresses clamped into range);
-    // the range masks are applied when the values are stored, so the loads of
-    // the next tiles stay in flight and the compiler can wait for exactly the
-    // loads a store needs.
+    // Loads: raw buffer loads whose resource is a wave-uniform base per feature
+    // row (scalar registers, advanced per tile) and whose per-lane 32-bit offset
+    // never changes, so a tile's loads take no vector address arithmetic.  The
+    // two half-waves read rows lrow of feature rows f and f + 4 (lq = 2 w and
+    // 2 w + 1), so an offset is at most 16 ldb + 124 bytes (the host keeps ld
+    // below 2^27).  A feature >= d reads feature d - 1 instead: finite values
+    // that meet zero-padded query features, so their products are exactly 0 and
+    // no mask is needed.  Rows at or past m occur only in the last tile; they
+    // read row m - 1 and get an infinite norm, so they never qualify.
+    static_assert(T::TR == 32, "the half-wave feature split assumes 32-row tiles");
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const float *fbase[T::PF];
+    uint32_t foff[T::PF];
+#pragma unroll
+    for (int p = 0; p < T::PF; ++p) {
+        const int f_lo = 4 * (2 * wv + (p >> 2) * T::FSTEP) + (p & 3);
+        const int fl = f_lo < d ? f_lo : d - 1, fh = f_lo + 4 < d ? f_lo + 4 : d - 1;
+        fbase[p] = B + (int64_t)fl * ldb;
+        foff[p] = (uint32_t)(((lq & 1) ? (int64_t)(fh - fl) * ldb : 0) + lrow) * 4u;
+    }
+    const uint32_t noff = (uint32_t)lrow * 4u; // lrow == tid % TR: the thread also loads row lrow's norm
+    // the tile's base address as an explicit scalar, so that it is not folded
+    // into per-lane 64-bit pointers (the load then adds the 32-bit lane offset)
+    typedef const char __attribute__((address_space(1))) *gchar;
+    auto sbase = [](const void *ptr) {
+        const uint64_t x = reinterpret_cast<uint64_t>(ptr);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+        return (gchar)(((uint64_t)hi << 32) | lo);
+    };
+    // raw buffer load: resource from the scalar base (2^31 bytes of range), the
+    // 32-bit lane offset in voffset; a full tile never leaves the buffer
+    auto ld32 = [](gchar base, uint32_t off) {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(const char *)base, (short)0, 0x7fffffff, 0x00020000);
+        return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    };
+    // One load sequence for every tile (so that the wait counts stay exact): in
+    // the last tile a row at or past m moves its byte offsets back to row m - 1.
     auto load = [&](Pref &P, int64_t t) {
         const int64_t tt = t < t_end ? t : t_end - 1;
-        const int64_t j = tt * T::TR + lrow;
-        P.jv = j < m;
-        const int64_t jc = P.jv ? j : m - 1;
-#pragma unroll
-        for (int p = 0; p < T::PF; ++p) {
-            const int f = 4 * (lq + (p >> 2) * T::FSTEP) + (p & 3);
-            const int fc = f < d ? f : d - 1;
-            P.v[p] = B[(int64_t)fc * ldb + jc];
+        const int64_t row0 = tt * T::TR;
+        uint32_t back = 0;
+        P.nv = true;
+        if (row0 + T::TR > m) {
+            const int64_t j = row0 + lrow;
+            P.nv = j < m;
+            back = P.nv ? 0u : (uint32_t)(j - (m - 1)) * 4u;
         }
-        const int64_t jj = tt * T::TR + (tid % T::TR);
-        P.nv = jj < m;
-        const int64_t jjc = P.nv ? jj : m - 1;
-        P.n = nrm_b[jjc];
+#pragma unroll
+        for (int p = 0; p < T::PF; ++p) P.v[p] = __uint_as_float(ld32(sbase(fbase[p] + row0), foff[p] - back));
+        P.n = __uint_as_float(ld32(sbase(nrm_b + row0), noff - back));
         if (PAYLOAD) {
-            P.comp = comp_b[jjc];
-            P.core = core_b[jjc];
+            P.comp = (int32_t)ld32(sbase(comp_b + row0), noff - back);
+            P.core = __uint_as_float(ld32(sbase(core_b + row0), noff - back));
         }
     };
     auto store = [&](const Pref &P, int buf, int slot) {
 #pragma unroll
         for (int h = 0; h < T::PF / 4; ++h) {
             const int f0 = 4 * (lq + h * T::FSTEP);
-            if (FULL || f0 < fused) {
-                f4 v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = (P.jv && f0 + e < d) ? P.v[4 * h + e] : 0.f;
-                *reinterpret_cast<f4 *>(sm_tile[buf] + lrow * T::RS + f0) = v;
-            }
+            if (FULL || f0 < fused)
+                *reinterpret_cast<f4 *>(sm_tile[buf] + lrow * T::RS + f0) =
+                    f4{P.v[4 * h], P.v[4 * h + 1], P.v[4 * h + 2], P.v[4 * h + 3]};
         }
         if (tid < T::TR) {
             sm_nrm[slot][tid] = P.nv ? P.n : INFINITY; // padding rows never qualify
