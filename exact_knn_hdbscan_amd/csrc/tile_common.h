@@ -274,20 +274,29 @@ template <int K> struct TopK {
             i[t] = 0x7fffffff;
         }
     }
-    // Candidate from a stream whose indices ascend: it is larger than every
-    // entry in index, so a strict '<' on d2 keeps equal distances in index order.
+    // Candidate from a stream whose indices ascend (v < d[K - 1] required): it is
+    // larger than every entry in index, so a strict '<' on d2 keeps equal
+    // distances in index order.  The new list is a fixed network with no serial
+    // chain: slot t takes the median of (old t - 1, v, old t), which is old t
+    // before v's place, v at it and old t - 1 after it; the indices follow the
+    // same two comparisons.  Same result as moving v down by compare-and-swaps.
     __device__ __forceinline__ void push_ascending(float v, int32_t j) {
-        d[K - 1] = v;
-        i[K - 1] = j;
+        bool lt[K];
 #pragma unroll
-        for (int t = K - 1; t > 0; --t) {
-            const bool sw = d[t] < d[t - 1];
-            const float a = sw ? d[t] : d[t - 1], b = sw ? d[t - 1] : d[t];
-            const int32_t ia = sw ? i[t] : i[t - 1], ib = sw ? i[t - 1] : i[t];
-            d[t - 1] = a;
-            d[t] = b;
-            i[t - 1] = ia;
-            i[t] = ib;
+        for (int t = 0; t < K; ++t) lt[t] = v < d[t];
+        float nd[K];
+        int32_t ni[K];
+        nd[0] = lt[0] ? v : d[0];
+        ni[0] = lt[0] ? j : i[0];
+#pragma unroll
+        for (int t = 1; t < K; ++t) {
+            nd[t] = __builtin_amdgcn_fmed3f(d[t - 1], v, d[t]);
+            ni[t] = lt[t - 1] ? i[t - 1] : (lt[t] ? j : i[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < K; ++t) {
+            d[t] = nd[t];
+            i[t] = ni[t];
         }
     }
     __device__ __forceinline__ static bool less(float a, int32_t ia, float b, int32_t ib) {
