@@ -350,6 +350,23 @@ __device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
     const auto b = __builtin_amdgcn_permlane32_swap(m, m, false, false);
     return b[0] > b[1] ? b[0] : b[1];
 }
+// Second largest of the eight values (a_g, b_g), a_g >= b_g, held by the four
+// lanes of a column: merge (largest, second largest) pairs across lane ^ 16 and
+// lane ^ 32.  The merge of (x1, x2) and (y1, y2) is (max(x1, y1),
+// max(min(x1, y1), x2, y2)), symmetric, so the swap order does not matter.
+__device__ __forceinline__ uint32_t group_second_u32(uint32_t a, uint32_t b) {
+    auto pa = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+    auto pb = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    uint32_t t1 = pa[0] > pa[1] ? pa[0] : pa[1];
+    uint32_t t2 = pa[0] < pa[1] ? pa[0] : pa[1];
+    uint32_t b2 = pb[0] > pb[1] ? pb[0] : pb[1];
+    t2 = t2 > b2 ? t2 : b2;
+    pa = __builtin_amdgcn_permlane32_swap(t1, t1, false, false);
+    pb = __builtin_amdgcn_permlane32_swap(t2, t2, false, false);
+    const uint32_t m = pa[0] < pa[1] ? pa[0] : pa[1];
+    b2 = pb[0] > pb[1] ? pb[0] : pb[1];
+    return m > b2 ? m : b2;
+}
 // For non-negative floats (and +inf) the bit patterns order like the values.
 __device__ __forceinline__ float group_min_nonneg(float v) { return __uint_as_float(group_min_u32(__float_as_uint(v))); }
 __device__ __forceinline__ float group_max_nonneg(float v) { return __uint_as_float(group_max_u32(__float_as_uint(v))); }
@@ -364,17 +381,21 @@ __device__ __forceinline__ float group_max_nonneg(float v) { return __uint_as_fl
 // The four lanes of a query column see disjoint rows and keep separate lists
 // that are merged at the end.  Any K real candidates bound the query's final
 // K-th D2 from above, and two such bounds are cheap to share between the four
-// lanes: the smallest of their last entries (one full list), and the largest of
-// their J-th entries, J = ceil(K / 4) - 1 (four lists with J + 1 entries each
-// hold at least K candidates).  A candidate above the smaller bound can never
+// lanes: the smallest of their last entries (one full list), and the K-th
+// smallest of their first J + 1 entries, J = ceil(K / 4) - 1 (four lists with
+// J + 1 entries each hold at least K candidates).  That is the largest of the
+// four J-th entries, or, when 4 (J + 1) = K + 1 (K = 11), the second largest of
+// the eight J-th and (J - 1)-th entries.  A candidate above the smaller bound can never
 // reach the final list and is not admitted (on equality it is, since a lower
 // index can still win the tie).  Without this, each lane would keep filling its
 // own list with candidates that the final merge drops.
 template <int K, int CB, int RB> struct EpiKnn {
     static constexpr int J = (K + 3) / 4 - 1;
+    static constexpr bool kSecond = 4 * (J + 1) == K + 1 && J >= 1;
     Entry *lists; // LDS, [CB][K][kThreads]
     float thr[CB]; // this lane's last entry
     float qj[CB];  // this lane's J-th entry
+    float qj1[CB]; // this lane's (J - 1)-th entry (used when kSecond)
     float nq[CB];
     float adm[CB];  // admission bound on D2 shared by the column's four lanes
     float admq[CB]; // the same bound moved to nb - 2 s, widened by the rounding margin
@@ -392,6 +413,7 @@ template <int K, int CB, int RB> struct EpiKnn {
             for (int t = 0; t < K; ++t) at(cb, t) = Entry{INFINITY, 0x7fffffff};
             thr[cb] = INFINITY;
             qj[cb] = INFINITY;
+            qj1[cb] = INFINITY;
             adm[cb] = INFINITY;
             admq[cb] = INFINITY;
         }
@@ -434,7 +456,10 @@ template <int K, int CB, int RB> struct EpiKnn {
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
                 // list entries are >= 0 or +inf (clamped on insertion)
-                adm[cb] = fminf(group_min_nonneg(thr[cb]), group_max_nonneg(qj[cb]));
+                const float gq = kSecond ? __uint_as_float(group_second_u32(__float_as_uint(qj[cb]),
+                                                                             __float_as_uint(qj1[cb])))
+                                         : group_max_nonneg(qj[cb]);
+                adm[cb] = fminf(group_min_nonneg(thr[cb]), gq);
                 admq[cb] = fmaf(adm[cb], 1.0f + kWiden, -nq[cb] * (1.0f - kWiden));
             }
             dirty = false;
@@ -465,6 +490,7 @@ template <int K, int CB, int RB> struct EpiKnn {
             store(cb, L);
             thr[cb] = L.d[K - 1];
             qj[cb] = L.d[J];
+            if (kSecond) qj1[cb] = L.d[J - 1];
             dirty = true;
         }
     }
