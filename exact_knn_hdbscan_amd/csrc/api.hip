@@ -129,12 +129,16 @@ KnnPlan plan_knn(int64_t n, int64_t m, int d, int k, int64_t max_chunk_dots) {
     return p;
 }
 
+inline int padded_dim(int d) { return (d + 3) & ~3; }
+
+// bt (kNN outputs only): point-major copy of the database for the rescore
 size_t knn_ws(const KnnPlan &p, int64_t n, int64_t m, bool self, Carver &c, float **nx, float **ny, Entry **part,
-              int32_t **idx_scratch = nullptr, int k = 0) {
+              int32_t **idx_scratch = nullptr, int k = 0, float **bt = nullptr, int d = 0) {
     *nx = c.take<float>(n);
     *ny = self ? *nx : c.take<float>(m);
     *part = p.splits > 1 ? c.take<Entry>((size_t)p.rows * p.splits * p.K) : nullptr;
     if (idx_scratch) *idx_scratch = c.take<int32_t>((size_t)n * k);
+    if (bt) *bt = c.take<float>((size_t)m * padded_dim(d));
     return c.used;
 }
 
@@ -151,9 +155,10 @@ int check_points(const float *X, int64_t ld, int64_t n, int d, const char *name)
 // Runs the dense kNN over all chunks.  out_mode: kOutKnn or kOutCore.
 int run_knn(const KnnPlan &p, const float *X, int64_t ldx, int64_t n, const float *Y, int64_t ldy, int64_t m, int d,
             bool self, int out_mode, int k_out, int min_samples, int32_t *out_idx, float *out_dist, float *out_core,
-            float *nx, float *ny, Entry *part, hipStream_t s) {
+            float *nx, float *ny, Entry *part, float *bt, hipStream_t s) {
     EKH_HIP(launch_norms(X, ldx, n, d, nx, s));
     if (!self) EKH_HIP(launch_norms(Y, ldy, m, d, ny, s));
+    if (out_mode == kOutKnn) EKH_HIP(launch_point_major(Y, ldy, m, d, padded_dim(d), bt, s));
     for (int64_t q0 = 0; q0 < n; q0 += p.rows) {
         KnnArgs a{};
         a.Q = X;
@@ -184,10 +189,21 @@ int run_knn(const KnnPlan &p, const float *X, int64_t ldx, int64_t n, const floa
             a.out_mode = out_mode;
             EKH_HIP(launch_knn_merge(p.K, a, s));
         }
-        if (out_mode == kOutKnn) {
-            a.out_mode = out_mode;
-            EKH_HIP(launch_knn_rescore(p.K, a, s));
-        }
+    }
+    if (out_mode == kOutKnn) {
+        // reported distances, over all rows at once (no rows x m scratch involved)
+        KnnArgs a{};
+        a.Q = X;
+        a.ldq = ldx;
+        a.q0 = 0;
+        a.nq = n;
+        a.d = d;
+        a.k_out = k_out;
+        a.out_idx = out_idx;
+        a.out_dist = out_dist;
+        a.Bt = bt;
+        a.dp = padded_dim(d);
+        EKH_HIP(launch_knn_rescore(p.K, a, s));
     }
     return EKH_OK;
 }
@@ -270,7 +286,8 @@ size_t ekh_knn_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t k, int64
     float *nx, *ny;
     Entry *part;
     int32_t *idx;
-    return knn_ws(p, n, m, false, c, &nx, &ny, &part, &idx, k);
+    float *bt;
+    return knn_ws(p, n, m, false, c, &nx, &ny, &part, &idx, k, &bt, d);
 }
 
 int ekh_knn(const float *X, int64_t ldx, int64_t n, const float *Y, int64_t ldy, int64_t m, int32_t d, int32_t k,
@@ -290,10 +307,11 @@ int ekh_knn(const float *X, int64_t ldx, int64_t n, const float *Y, int64_t ldy,
     float *nx, *ny;
     Entry *part;
     int32_t *idx_scratch;
-    knn_ws(p, n, m, false, c, &nx, &ny, &part, &idx_scratch, k);
+    float *bt;
+    knn_ws(p, n, m, false, c, &nx, &ny, &part, &idx_scratch, k, &bt, d);
     if (self) ny = nx;
     return run_knn(p, X, ldx, n, Y, ldy, m, d, self, kOutKnn, k, 0, out_idx ? out_idx : idx_scratch, out_dist,
-                   nullptr, nx, ny, part, (hipStream_t)stream);
+                   nullptr, nx, ny, part, bt, (hipStream_t)stream);
 }
 
 size_t ekh_core_workspace_bytes(int64_t n, int32_t d, int32_t min_samples) {
@@ -324,7 +342,7 @@ int ekh_core_distances(const float *X, int64_t ldx, int64_t n, int32_t d, int32_
     Entry *part;
     knn_ws(p, n, n, true, c, &nx, &ny, &part);
     return run_knn(p, X, ldx, n, X, ldx, n, d, true, kOutCore, K, min_samples, out_nbr_idx, out_nbr_d2, out_core, nx,
-                   nx, part, (hipStream_t)stream);
+                   nx, part, nullptr, (hipStream_t)stream);
 }
 
 size_t ekh_mst_workspace_bytes(int64_t n, int32_t d, int32_t min_samples, int with_neighbours) {
@@ -364,7 +382,7 @@ int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const flo
         const KnnPlan p = plan_knn(n, n, d, K, 0);
         float *scratch_core = (float *)w.sa; // core as computed here is not used: the caller's core rules
         if ((rc = run_knn(p, X, ldx, n, X, ldx, n, d, true, kOutCore, K, min_samples, w.nbr_idx, w.nbr_d2,
-                          scratch_core, w.knn_nx, w.knn_nx, w.knn_part, s)) != EKH_OK)
+                          scratch_core, w.knn_nx, w.knn_nx, w.knn_part, nullptr, s)) != EKH_OK)
             return rc;
         nbr_idx = w.nbr_idx;
         nbr_d2 = w.nbr_d2;

@@ -87,6 +87,8 @@ struct KnnArgs {
     int32_t *out_idx; // [n, k_out] absolute rows
     float *out_dist;  // [n, k_out] (kOutKnn) or d2 lists (kOutCore)
     float *out_core;  // [n]
+    const float *Bt;  // database point-major [m, dp] (rescore only)
+    int dp;           // row stride of Bt: d rounded up to a multiple of 4, zero padded
 };
 
 // host launchers (return hipError_t of the launch)
@@ -94,6 +96,7 @@ hipError_t launch_norms(const float *X, int64_t ldx, int64_t n, int d, float *ou
 hipError_t launch_knn_tile(int K, int QM, const KnnArgs &a, hipStream_t s);
 hipError_t launch_knn_merge(int K, const KnnArgs &a, hipStream_t s);
 hipError_t launch_knn_rescore(int K, const KnnArgs &a, hipStream_t s);
+hipError_t launch_point_major(const float *B, int64_t ldb, int64_t m, int d, int dp, float *Bt, hipStream_t s);
 
 // ---- Boruvka ---------------------------------------------------------------
 constexpr uint64_t kNoEdge = ~0ull;

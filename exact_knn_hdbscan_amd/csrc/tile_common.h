@@ -587,22 +587,43 @@ template <int K> __global__ void knn_merge_kernel(KnnArgs a) {
 // Reported kNN distances: the selected neighbours' D2 recomputed by direct
 // differences, sum_f (q_f - y_f)^2 with fmaf in feature order, which carries no
 // cancellation error; each row is then sorted by (that D2, index).  The
-// neighbour set itself is the one the GEMM-form D2 selected.
+// neighbour set itself is the one the GEMM-form D2 selected.  One thread per
+// query row: the query's features are read once, feature by feature (adjacent
+// threads, adjacent rows: coalesced), and each neighbour's from the
+// point-major copy Bt, four features per 16-byte load; the padding features
+// (zero on both sides) add exact zeros.
 template <int K> __global__ void knn_rescore_kernel(KnnArgs a) {
     const int64_t ql = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (ql >= a.nq) return;
     const int64_t q = a.q0 + ql;
+    int32_t jr[K];
+    float s[K];
+#pragma unroll
+    for (int t = 0; t < K; ++t) {
+        jr[t] = t < a.k_out ? a.out_idx[q * a.k_out + t] : 0;
+        s[t] = 0.f;
+    }
+    for (int f = 0; f < a.dp; f += 4) {
+        float qv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qv[e] = f + e < a.d ? a.Q[(int64_t)(f + e) * a.ldq + q] : 0.f;
+#pragma unroll
+        for (int t = 0; t < K; ++t) {
+            if (t < a.k_out) {
+                const f4 y = *reinterpret_cast<const f4 *>(a.Bt + (int64_t)jr[t] * a.dp + f);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float v = qv[e] - y[e];
+                    s[t] = fmaf(v, v, s[t]);
+                }
+            }
+        }
+    }
     TopK<K> L;
     L.clear();
-    for (int t = 0; t < a.k_out; ++t) {
-        const int32_t j = a.out_idx[q * a.k_out + t];
-        float s = 0.f;
-        for (int f = 0; f < a.d; ++f) {
-            const float v = a.Q[(int64_t)f * a.ldq + q] - a.B[(int64_t)f * a.ldb + j];
-            s = fmaf(v, v, s);
-        }
-        L.push_any(s, j);
-    }
+#pragma unroll
+    for (int t = 0; t < K; ++t)
+        if (t < a.k_out) L.push_any(s[t], jr[t]);
 #pragma unroll
     for (int t = 0; t < K; ++t) {
         if (t < a.k_out) {

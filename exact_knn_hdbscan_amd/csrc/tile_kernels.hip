@@ -36,6 +36,35 @@ hipError_t launch_norms(const float *X, int64_t ldx, int64_t n, int d, float *ou
     return hipGetLastError();
 }
 
+// Point-major copy of a feature-major point set, for gathers of whole points:
+// Bt[j * dp + f] = B[f * ldb + j] for f < d, 0 for d <= f < dp.  32 x 32 tiles
+// through LDS (one padding column), coalesced on both sides.
+__global__ void point_major_kernel(const float *__restrict__ B, int64_t ldb, int64_t m, int d, int dp,
+                                   float *__restrict__ Bt) {
+    __shared__ float t[32][33];
+    const int64_t j0 = (int64_t)blockIdx.x * 32;
+    const int f0 = blockIdx.y * 32;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    for (int r = ty; r < 32; r += 8) {
+        const int f = f0 + r;
+        const int64_t j = j0 + tx;
+        t[r][tx] = (f < d && j < m) ? B[(int64_t)f * ldb + j] : 0.f;
+    }
+    __syncthreads();
+    for (int r = ty; r < 32; r += 8) {
+        const int64_t j = j0 + r;
+        const int f = f0 + tx;
+        if (j < m && f < dp) Bt[j * dp + f] = t[tx][r];
+    }
+}
+
+hipError_t launch_point_major(const float *B, int64_t ldb, int64_t m, int d, int dp, float *Bt, hipStream_t s) {
+    if (m <= 0) return hipSuccess;
+    hipLaunchKernelGGL(point_major_kernel, dim3((unsigned)((m + 31) / 32), (unsigned)((dp + 31) / 32)), dim3(256), 0,
+                       s, B, ldb, m, d, dp, Bt);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- kNN dispatch
 hipError_t launch_knn_tile(int K, int QM, const KnnArgs &a, hipStream_t s) {
     if (a.nq <= 0) return hipSuccess;
