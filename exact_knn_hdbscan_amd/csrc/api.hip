@@ -104,9 +104,20 @@ struct KnnPlan {
     int64_t tiles;  // database tiles
 };
 
-constexpr int64_t kMaxLd = int64_t(1) << 27;
-constexpr int64_t kTargetGroups = 1024; // workgroups per launch to aim for (256 CUs)
+constexpr int64_t kMaxLd = int64_t(1) << 25;
+constexpr int64_t kTargetGroups = 1024; // scan launches: workgroups to aim for (256 CUs)
 constexpr int64_t kMinTilesPerSplit = 4;
+constexpr int64_t kCUs = 256;             // MI355X compute units (fixed, so that a workspace
+                                          // query and the run always plan alike)
+constexpr int64_t kLdsPerCu = 160 * 1024;
+constexpr int64_t kWarmupWork = 12000;    // warm-up of fresh lists, in tiles x k-steps (measured)
+
+// kNN workgroups resident per CU: two unless the LDS tile and lists need more than half
+int64_t knn_groups_per_cu(int K, int QM) {
+    const int64_t tr = tile_rows(QM), rs = 4 * QM + 4;
+    const int64_t lds = 2 * tr * rs * 4 + 9 * tr * 4 + (int64_t)knn_col_blocks(K, QM) * K * kThreads * 8;
+    return 2 * lds <= kLdsPerCu ? 2 : 1;
+}
 
 KnnPlan plan_knn(int64_t n, int64_t m, int d, int k, int64_t max_chunk_dots) {
     KnnPlan p{};
@@ -121,11 +132,24 @@ KnnPlan plan_knn(int64_t n, int64_t m, int d, int k, int64_t max_chunk_dots) {
         p.rows = std::min<int64_t>(n, std::max<int64_t>(r, p.QT));
     }
     p.tiles = (m + p.TR - 1) / p.TR;
+    // Database splits: the launch runs in rounds of resident workgroups, and
+    // every split starts its lists empty (the first tiles insert nearly every
+    // row, a cost of about kWarmupWork / k-steps tiles).  Take the split count
+    // that minimises rounds x (tiles per split + that warm-up).
     const int64_t qtiles = std::max<int64_t>(1, (p.rows + p.QT - 1) / p.QT);
-    int64_t s = (kTargetGroups + qtiles - 1) / qtiles;
-    s = std::min<int64_t>(s, std::max<int64_t>(1, p.tiles / kMinTilesPerSplit));
-    s = std::max<int64_t>(1, std::min<int64_t>(s, 65535));
-    p.splits = (int)s;
+    const int64_t slots = kCUs * knn_groups_per_cu(p.K, p.QM);
+    const int64_t warm = kWarmupWork / (4 * p.chunks);
+    const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(64, p.tiles / kMinTilesPerSplit));
+    int64_t best_s = 1, best = -1;
+    for (int64_t s = 1; s <= smax; ++s) {
+        const int64_t rounds = (qtiles * s + slots - 1) / slots;
+        const int64_t cost = rounds * ((p.tiles + s - 1) / s + warm);
+        if (best < 0 || cost < best) {
+            best = cost;
+            best_s = s;
+        }
+    }
+    p.splits = (int)best_s;
     return p;
 }
 
@@ -148,7 +172,7 @@ int check_points(const float *X, int64_t ld, int64_t n, int d, const char *name)
     if (d < 1 || d > EKH_MAX_DIM) return fail(EKH_EINVAL, "%s: d = %d out of range [1, %d]", name, d, EKH_MAX_DIM);
     if (ld < n) return fail(EKH_EINVAL, "%s: leading dimension %lld < n = %lld", name, (long long)ld, (long long)n);
     // the tile loads address four feature rows with a 32-bit byte offset
-    if (ld >= kMaxLd) return fail(EKH_EINVAL, "%s: leading dimension %lld >= 2^27 is not supported", name, (long long)ld);
+    if (ld >= kMaxLd) return fail(EKH_EINVAL, "%s: leading dimension %lld >= 2^25 is not supported", name, (long long)ld);
     return EKH_OK;
 }
 

@@ -24,7 +24,9 @@ constexpr int kThreads = kWaves * 64; // 256 threads
 template <int QM> struct TileGeo;
 template <> struct TileGeo<16> { static constexpr int TR = 32; };
 template <> struct TileGeo<32> { static constexpr int TR = 32; };
-template <> struct TileGeo<64> { static constexpr int TR = 32; };
+// d > 128: 16-row tiles keep the prefetch registers and the LDS tile small
+// enough for two workgroups per CU
+template <> struct TileGeo<64> { static constexpr int TR = 16; };
 
 // instantiated list lengths; a request for k uses the smallest K >= k
 constexpr int kNumK = 6;
@@ -35,7 +37,7 @@ inline int pick_k(int k) {
     return -1;
 }
 inline int pick_qm(int d) { return d <= 64 ? 16 : (d <= 128 ? 32 : 64); }
-inline int tile_rows(int qm) { return 32; }
+inline int tile_rows(int qm) { return qm == 64 ? 16 : 32; }
 // 16-column query blocks per wave: two when the registers allow it
 constexpr int knn_col_blocks(int K, int QM) { return (K > 11 || QM > 16) ? 1 : 2; }
 constexpr int scan_col_blocks(int QM) { return QM > 16 ? 1 : 2; }

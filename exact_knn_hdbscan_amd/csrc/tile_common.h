@@ -82,22 +82,25 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
     // Loads: raw buffer loads whose resource is a wave-uniform base per feature
     // row (scalar registers, advanced per tile) and whose per-lane 32-bit offset
     // never changes, so a tile's loads take no vector address arithmetic.  The
-    // two half-waves read rows lrow of feature rows f and f + 4 (lq = 2 w and
-    // 2 w + 1), so an offset is at most 16 ldb + 124 bytes (the host keeps ld
-    // below 2^27).  A feature >= d reads feature d - 1 instead: finite values
-    // that meet zero-padded query features, so their products are exactly 0 and
-    // no mask is needed.  Rows at or past m occur only in the last tile; they
-    // read row m - 1 and get an infinite norm, so they never qualify.
-    static_assert(T::TR == 32, "the half-wave feature split assumes 32-row tiles");
+    // 64 / TR lane groups of a wave read rows lrow of feature rows f, f + 4,
+    // f + 8, ... (lq = (64 / TR) w + group), so an offset is at most
+    // 4 (64 / TR - 1) ld + TR - 1 floats (the host keeps ld below 2^25).  A
+    // feature >= d reads feature d - 1 instead: finite values that meet
+    // zero-padded query features, so their products are exactly 0 and no mask
+    // is needed.  Rows at or past m occur only in the last tile; they read row
+    // m - 1 and get an infinite norm, so they never qualify.
+    static_assert(64 % T::TR == 0, "a wave covers whole rows of lane groups");
+    constexpr int kGroups = 64 / T::TR;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = (tid & 63) / T::TR; // lq == kGroups * wv + grp
     const float *fbase[T::PF];
     uint32_t foff[T::PF];
 #pragma unroll
     for (int p = 0; p < T::PF; ++p) {
-        const int f_lo = 4 * (2 * wv + (p >> 2) * T::FSTEP) + (p & 3);
-        const int fl = f_lo < d ? f_lo : d - 1, fh = f_lo + 4 < d ? f_lo + 4 : d - 1;
+        const int f_lo = 4 * (kGroups * wv + (p >> 2) * T::FSTEP) + (p & 3);
+        const int fl = f_lo < d ? f_lo : d - 1, fa = f_lo + 4 * grp < d ? f_lo + 4 * grp : d - 1;
         fbase[p] = B + (int64_t)fl * ldb;
-        foff[p] = (uint32_t)(((lq & 1) ? (int64_t)(fh - fl) * ldb : 0) + lrow) * 4u;
+        foff[p] = (uint32_t)((int64_t)(fa - fl) * ldb + lrow) * 4u;
     }
     const uint32_t noff = (uint32_t)lrow * 4u; // lrow == tid % TR: the thread also loads row lrow's norm
     // the tile's base address as an explicit scalar, so that it is not folded

@@ -22,7 +22,7 @@
  *
  * Conventions shared by every entry point
  *  - Point sets are feature-major: point i of X has feature f at
- *    X[f * ldx + i], with n <= ldx < 2^27 (any n, m, d, ld, odd values
+ *    X[f * ldx + i], with n <= ldx < 2^25 (any n, m, d, ld, odd values
  *    included; the bound keeps the tile loads' byte offsets within 32 bits).
  *    X, Y, outputs and the workspace are DEVICE pointers owned by the caller;
  *    the library never allocates or frees caller memory and keeps no state
