@@ -78,6 +78,43 @@ def cpu_baseline(X, k, budget_s=15.0):
     }
 
 
+def time_sections(ekh, datagen, reps=5):
+    """ekh_knn on the two section workloads (50,000 x 5,000 at d = 102, k = 10; and
+    200,000 x 20,000 at d = 200, k = 10, in chunks of max_chunk_dots = 64e6): median
+    time per call with inputs resident, the tile kernel's rate, and the pair rate."""
+    import numpy as np
+    import torch
+
+    out = {}
+    for name in ("ks4_section_50000x102", "wide_section_200000x200"):
+        wl = datagen.make(name)
+        X, Y, k = torch.from_numpy(wl["X"]).cuda(), torch.from_numpy(wl["Y"]).cuda(), wl["k"]
+        dots = wl.get("max_chunk_bytes", 0) // 4
+        ws = torch.empty(ekh.knn_workspace_bytes(X.shape[1], Y.shape[1], X.shape[0], k, dots), dtype=torch.uint8,
+                         device=X.device)
+        ekh.knn(X, Y, k, max_chunk_dots=dots, workspace=ws)
+        torch.cuda.synchronize()
+        timer = ekh.kernel_timer()
+        timer.__enter__()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            ekh.knn(X, Y, k, max_chunk_dots=dots, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        tk = timer.read(timer.KNN_TILE)
+        timer.stop()
+        ms_call = float(np.median(ts))
+        pairs = float(X.shape[1]) * float(Y.shape[1])
+        out[name] = {"ms": ms_call, "pairs_per_s": pairs / (ms_call / 1e3), "k": k, "max_chunk_dots": dots,
+                     "tile_launches": tk["launches"] // reps, "tile_ms": tk["ms"] / reps,
+                     "tile_tflops": tk["flop"] / (tk["ms"] / 1e3) / 1e12 if tk["ms"] else None}
+        del X, Y, ws
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -85,6 +122,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="clips_500000x61")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sections", action="store_true", help="skip the ekh_knn section workloads")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for counter runs: one plain copy of COPY_BYTES (calibration) and one pass of the path")
     args = ap.parse_args()
@@ -200,6 +238,8 @@ def main():
         "ms": tail_ms, "min_cluster_size": TAIL_MIN_CLUSTER_SIZE, "clusters": int(labels.max()) + 1,
         "noise": int((labels < 0).sum()), "where": "host C++ (ekh_hdbscan_tail), device-to-host copy of the tree included",
         "end_to_end_ms": ms_step + tail_ms}
+    if not args.no_sections:
+        result["knn_sections"] = time_sections(ekh, datagen)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(X, ms + 1)
         from oracle import hdbscan_tail as otail
