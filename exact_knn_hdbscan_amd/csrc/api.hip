@@ -221,6 +221,7 @@ int run_knn(const KnnPlan &p, const float *X, int64_t ldx, int64_t n, const floa
         a.ldq = ldx;
         a.q0 = 0;
         a.nq = n;
+        a.m = m;
         a.d = d;
         a.k_out = k_out;
         a.out_idx = out_idx;

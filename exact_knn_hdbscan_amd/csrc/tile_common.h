@@ -599,11 +599,14 @@ template <int K> __global__ void knn_rescore_kernel(KnnArgs a) {
     const int64_t ql = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (ql >= a.nq) return;
     const int64_t q = a.q0 + ql;
-    int32_t jr[K];
+    int32_t jr[K], jo[K]; // row read (always in range) and row reported
     float s[K];
 #pragma unroll
     for (int t = 0; t < K; ++t) {
-        jr[t] = t < a.k_out ? a.out_idx[q * a.k_out + t] : 0;
+        jo[t] = t < a.k_out ? a.out_idx[q * a.k_out + t] : 0;
+        // a list entry outside [0, m) cannot come from a finished search (k <= m);
+        // it is never used as an address: row 0 is read and the entry ranks last
+        jr[t] = (jo[t] >= 0 && jo[t] < a.m) ? jo[t] : 0;
         s[t] = 0.f;
     }
     for (int f = 0; f < a.dp; f += 4) {
@@ -626,7 +629,7 @@ template <int K> __global__ void knn_rescore_kernel(KnnArgs a) {
     L.clear();
 #pragma unroll
     for (int t = 0; t < K; ++t)
-        if (t < a.k_out) L.push_any(s[t], jr[t]);
+        if (t < a.k_out) L.push_any(jr[t] == jo[t] ? s[t] : INFINITY, jo[t]);
 #pragma unroll
     for (int t = 0; t < K; ++t) {
         if (t < a.k_out) {
