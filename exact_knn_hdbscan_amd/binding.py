@@ -97,6 +97,10 @@ def library() -> ctypes.CDLL:
             lib.ekh_mst_boruvka.argtypes = [_p, _i64, _i64, _i32, _p, _i32, _p, _p, _u32, _p, _p, _p, _p, _p, _sz,
                                             _p]
             lib.ekh_hdbscan_tail.argtypes = [_p, _p, _p, _i64, _i32, _p, _p, _p, _p, _p, _p, _p]
+            lib.ekh_bipartite_workspace_bytes.argtypes = [_i64, _i32]
+            lib.ekh_bipartite_workspace_bytes.restype = _sz
+            lib.ekh_bipartite_assign.argtypes = [_p, _i64, _i32, _i64, _i32, _p, ctypes.c_double, _i32, _p, _p, _p, _p,
+                                                 _sz, _p]
             lib.ekh_timer_enable.argtypes = [ctypes.c_int]
             lib.ekh_timer_read.argtypes = [ctypes.c_int, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double),
                                            ctypes.POINTER(ctypes.c_double)]
@@ -257,6 +261,33 @@ def hdbscan_tail(lo, hi, w, min_cluster_size: int, return_tree: bool = False):
     ne, nc = info.n_entries, info.n_clusters
     return labels, {"parent": par[:ne], "child": chi[:ne], "lambda": lam[:ne], "size": siz[:ne],
                     "stability": st[:nc], "n_clusters": nc, "n_selected": info.n_selected}
+
+
+def bipartite_workspace_bytes(m: int, n_clusters: int) -> int:
+    return int(library().ekh_bipartite_workspace_bytes(m, n_clusters))
+
+
+def bipartite_assign(nbr: torch.Tensor, m: int, n_clusters: int, init_right: torch.Tensor, gamma: float = 1.0,
+                     max_rounds: int = 200, workspace: torch.Tensor = None):
+    """Bipartite kNN-graph assignment (ekh_bipartite_assign).  nbr: int32 [n, k]
+    on the GPU (row-major, each row a spike's neighbours among the m right
+    nodes); init_right: int32 [m] labels in [0, n_clusters).  Returns (left
+    labels [n], right labels [m], rounds run)."""
+    if nbr.dtype != torch.int32 or nbr.dim() != 2 or not nbr.is_contiguous() or not nbr.is_cuda:
+        raise ValueError("nbr must be a contiguous int32 [n, k] CUDA tensor")
+    if init_right.dtype != torch.int32 or init_right.shape != (m,) or not init_right.is_cuda:
+        raise ValueError("init_right must be an int32 [m] CUDA tensor")
+    lib = library()
+    n, k = nbr.shape
+    dev = nbr.device
+    left = torch.empty(n, dtype=torch.int32, device=dev)
+    right = torch.empty(m, dtype=torch.int32, device=dev)
+    ws = workspace if workspace is not None else _workspace(bipartite_workspace_bytes(m, n_clusters), dev)
+    rounds = ctypes.c_int32(0)
+    _check(lib.ekh_bipartite_assign(nbr.data_ptr(), n, k, m, n_clusters, init_right.contiguous().data_ptr(),
+                                    float(gamma), max_rounds, left.data_ptr(), right.data_ptr(), ctypes.byref(rounds),
+                                    ws.data_ptr(), ws.numel(), _stream(dev)))
+    return left, right, int(rounds.value)
 
 
 class kernel_timer:

@@ -123,6 +123,22 @@ def duplicates(n_copies: int, d: int, seed: int = 0, n_other: int = 0) -> np.nda
 
 
 # name -> (description, factory returning a dict of arrays and parameters)
+def random_labels(m: int, n_clusters: int, seed: int = 0) -> np.ndarray:
+    """Starting labels for the right nodes of the bipartite assignment: uniform
+    in [0, n_clusters), int32 (the page's pipeline seeds them; here they are
+    drawn)."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, n_clusters, m).astype(np.int32)
+
+
+def random_neighbour_lists(n: int, m: int, k: int, seed: int = 0) -> np.ndarray:
+    """n rows of k distinct indices in [0, m), int32 [n, k]: a kNN-shaped graph
+    without the geometry."""
+    rng = np.random.default_rng(seed)
+    keys = rng.random((n, m))
+    return np.argsort(keys, axis=1)[:, :k].astype(np.int32)
+
+
 def _tiny(seed=0):
     X = gaussian_mixture(2000, 60, 8, seed, means="uniform5", sigma="one")
     return {"X": X, "Y": X, "k": 10, "min_samples": 10, "self": True}

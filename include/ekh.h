@@ -160,6 +160,40 @@ int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const flo
 /* ------------------------------------------------------------------ kernel timer (measurement) */
 
 /*
+ * Bipartite kNN-graph assignment (device).  Source: "Kilosort4 clustering and
+ * matching", section "Assignment in parallel: why the graph is bipartite".
+ * Left nodes are n spikes, right nodes m subset points; nbr [n, k] (row-major
+ * int32, each row a spike's neighbours among the subset, e.g. the out_idx of
+ * ekh_knn(X = spikes, Y = subset, k)) gives the edges.  Rounds alternate a left
+ * step (every spike takes the best label among its neighbours' right labels)
+ * and a right step (integer atomic counts[r, label] over the edges, then every
+ * right node takes the best label among its neighbours' left labels).  Score of
+ * label c for node v: n_vc - gamma k_v K_c / (2 m_e), float64 in that order,
+ * with n_vc the neighbours of v labelled c, k_v the degree of v (k for a spike,
+ * the number of spikes listing r for a right node), m_e = n k, and K_c the total
+ * degree of the OTHER side's nodes labelled c.  Readings where the page is
+ * silent: candidates are the labels present among the node's neighbours; ties
+ * keep the current label if it is among the best, else take the smallest;
+ * spikes start unlabelled; right nodes start from init_right; the loop stops
+ * after a left step that moves no spike, or after max_rounds rounds (the page:
+ * a 200-round cap); a right node that no spike lists keeps its label.
+ *
+ * init_right [m] int32 labels in [0, n_clusters); out_left [n], out_right [m]
+ * int32 (device, caller-owned); out_rounds (HOST, nullable) receives the rounds
+ * run.  Workspace: ekh_bipartite_workspace_bytes(m, n_clusters) bytes
+ * (4 (m + 2 C + m C) plus alignment).  Blocks: one 4-byte read-back per round.
+ * Errors: EKH_EINVAL for a NULL array, n, m < 1, k outside [1, 32],
+ * n_clusters < 1, n k or m n_clusters >= 2^31, gamma negative or not finite,
+ * max_rounds < 1, or (checked on the device before any step) a neighbour index
+ * outside [0, m) or a starting label outside [0, n_clusters); EKH_EWORKSPACE;
+ * EKH_EHIP.
+ */
+size_t ekh_bipartite_workspace_bytes(int64_t m, int32_t n_clusters);
+int ekh_bipartite_assign(const int32_t *nbr, int64_t n, int32_t k, int64_t m, int32_t n_clusters,
+                         const int32_t *init_right, double gamma, int32_t max_rounds, int32_t *out_left,
+                         int32_t *out_right, int32_t *out_rounds, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * HDBSCAN tail, on the HOST: spanning tree -> single-linkage hierarchy ->
  * condensed tree -> excess-of-mass selection -> cluster labels.
  * Source: "HDBSCAN", section "The algorithm on the device", last item (the

@@ -76,3 +76,19 @@ def test_core_and_mst_reject_bad_arguments(lib):
     assert lib.ekh_mst_boruvka(BOGUS, 10, 10, 3, BOGUS, 3, None, None, 0, BOGUS, BOGUS, BOGUS, None, BOGUS,
                                16, None) == -2
     assert lib.ekh_timer_read(7, None, None, None) == -1
+
+
+def test_bipartite_rejects_bad_arguments(lib):
+    f = lib.ekh_bipartite_assign
+    ok = dict(nbr=BOGUS, n=10, k=3, m=5, C=4, init=BOGUS, gamma=1.0, rounds=200, ws=BOGUS, ws_bytes=1 << 30)
+    for change in (dict(k=0), dict(k=33), dict(n=0), dict(m=0), dict(C=0), dict(gamma=-1.0), dict(rounds=0),
+                   dict(nbr=None), dict(ws=None), dict(n=1 << 30, k=2)):
+        a = dict(ok, **change)
+        rc = f(a["nbr"], a["n"], a["k"], a["m"], a["C"], a["init"], a["gamma"], a["rounds"], BOGUS, BOGUS, None, a["ws"],
+               a["ws_bytes"], None)
+        assert rc == -1, change
+    a = dict(ok, ws_bytes=16)
+    assert f(a["nbr"], a["n"], a["k"], a["m"], a["C"], a["init"], a["gamma"], a["rounds"], BOGUS, BOGUS, None, a["ws"],
+             a["ws_bytes"], None) == -2
+    assert lib.ekh_bipartite_workspace_bytes(5000, 40) >= 4 * (5000 * 40)
+    assert lib.ekh_bipartite_workspace_bytes(0, 40) == 0

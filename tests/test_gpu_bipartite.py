@@ -1,0 +1,102 @@
+"""GPU parity of the bipartite kNN-graph assignment (ekh_bipartite_assign) with the oracle.
+
+The result is integer work decided by float64 scores computed in the same
+order on both sides, so the bar is exact: identical left labels, right labels
+and round counts.  Cases: the oracle's hand-worked graphs, random kNN-shaped
+graphs over several sizes, k, cluster counts and gamma (including ragged sizes
+and isolated right nodes), the round cap, the Kilosort4-section graph at full
+size (the GPU's own knn(X, Y, 10) over 50,000 x 5,000), and argument errors.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_knn_hdbscan_amd as ekh
+from exact_knn_hdbscan_amd import binding, datagen
+from gpu_util import say
+from oracle import bipartite as obip
+
+import test_bipartite_oracle as pins
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(nbr, m, C, init, gamma=1.0, cap=200):
+    nbr_t = torch.from_numpy(np.ascontiguousarray(nbr, np.int32)).cuda()
+    init_t = torch.from_numpy(np.ascontiguousarray(init, np.int32)).cuda()
+    left, right, rounds = ekh.bipartite_assign(nbr_t, m, C, init_t, gamma=gamma, max_rounds=cap)
+    return left.cpu().numpy(), right.cpu().numpy(), rounds
+
+
+def same_as_oracle(nbr, m, C, init, gamma=1.0, cap=200):
+    gl, gr, grounds = run_gpu(nbr, m, C, init, gamma, cap)
+    ol, orr, orounds = obip.assign(np.asarray(nbr), m, C, np.asarray(init), gamma, cap)
+    assert grounds == orounds, "rounds %d vs %d" % (grounds, orounds)
+    np.testing.assert_array_equal(gl, ol)
+    np.testing.assert_array_equal(gr, orr)
+    return gl, gr, grounds
+
+
+def test_hand_worked_graphs():
+    cases = [
+        ([[0, 1], [0, 1], [2, 3], [2, 3]], 4, 2, [0, 0, 1, 1], 1.0, 200, ([0, 0, 1, 1], [0, 0, 1, 1], 2)),
+        ([[0, 1], [0, 1], [2, 3], [2, 3]], 4, 2, [0, 0, 1, 1], 1.0, 1, ([0, 0, 1, 1], [0, 0, 1, 1], 1)),
+        ([[0, 1], [1, 2], [1, 2]], 3, 2, [1, 0, 0], 1.0, 200, ([1, 0, 0], [1, 0, 0], 2)),
+        ([[0, 1], [1, 2], [1, 2]], 3, 2, [1, 0, 0], 0.0, 200, ([0, 0, 0], [0, 0, 0], 2)),
+        ([[0, 1], [1, 2], [1, 2]], 3, 2, [1, 1, 0], 0.0, 200, ([1, 0, 0], [1, 0, 0], 2)),
+        ([[1, 2], [1, 2], [0, 2]], 3, 2, [1, 0, 1], 1.0, 200, ([0, 0, 1], [1, 0, 0], 2)),
+        ([[0, 1], [0, 1]], 3, 6, [0, 0, 5], 1.0, 200, ([0, 0], [0, 0, 5], 2)),
+    ]
+    for nbr, m, C, init, gamma, cap, want in cases:
+        gl, gr, rounds = run_gpu(np.array(nbr), m, C, np.array(init), gamma, cap)
+        assert (gl.tolist(), gr.tolist(), rounds) == want
+
+
+@pytest.mark.parametrize("n,m,k,C,gamma,seed", [
+    (3000, 400, 10, 17, 1.0, 0), (2001, 777, 5, 40, 1.0, 1), (1000, 50, 3, 7, 0.5, 2), (4096, 256, 32, 3, 1.0, 3),
+    (513, 1000, 10, 200, 1.0, 4), (800, 120, 10, 12, 0.0, 5), (1, 5, 3, 2, 1.0, 6)])
+def test_random_graphs(n, m, k, C, gamma, seed):
+    nbr = datagen.random_neighbour_lists(n, m, k, seed)
+    init = datagen.random_labels(m, C, seed + 100)
+    _, _, rounds = same_as_oracle(nbr, m, C, init, gamma)
+    say("n %d m %d k %d C %d gamma %g: %d rounds" % (n, m, k, C, gamma, rounds))
+
+
+def test_round_cap_and_repeatability():
+    nbr = datagen.random_neighbour_lists(2000, 300, 10, 9)
+    init = datagen.random_labels(300, 25, 9)
+    for cap in (1, 2, 3):
+        same_as_oracle(nbr, 300, 25, init, 1.0, cap)
+    a = run_gpu(nbr, 300, 25, init)
+    b = run_gpu(nbr, 300, 25, init)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_kilosort4_section_graph_full_size():
+    """The page's use: the kNN of every spike among the subset (50,000 x 5,000,
+    k = 10) from the GPU's own ekh_knn, 40 starting labels."""
+    wl = datagen.make("ks4_section_50000x102")
+    X, Y = torch.from_numpy(wl["X"]).cuda(), torch.from_numpy(wl["Y"]).cuda()
+    idx, _ = ekh.knn(X, Y, 10)
+    nbr = idx.cpu().numpy()
+    m = Y.shape[1]
+    init = datagen.random_labels(m, 40, 0)
+    gl, gr, rounds = same_as_oracle(nbr, m, 40, init)
+    say("section graph: %d rounds, %d left labels in use" % (rounds, len(np.unique(gl))))
+    assert rounds < 200
+
+
+def test_bad_arguments():
+    nbr = torch.zeros((4, 2), dtype=torch.int32, device="cuda")
+    init = torch.zeros(3, dtype=torch.int32, device="cuda")
+    with pytest.raises(binding.EkhError) as e:  # neighbour index == m: found before any step
+        ekh.bipartite_assign(torch.tensor([[0, 3]] * 4, dtype=torch.int32, device="cuda"), 3, 2, init)
+    assert e.value.code == binding.EKH_EINVAL
+    with pytest.raises(binding.EkhError) as e:  # starting label outside [0, C)
+        ekh.bipartite_assign(nbr, 3, 2, torch.tensor([0, 2, 1], dtype=torch.int32, device="cuda"))
+    assert e.value.code == binding.EKH_EINVAL
+    with pytest.raises(binding.EkhError):
+        ekh.bipartite_assign(nbr, 3, 2, init, gamma=-1.0)
+    with pytest.raises(binding.EkhError):
+        ekh.bipartite_assign(nbr, 3, 2, init, max_rounds=0)
