@@ -78,7 +78,36 @@ def cpu_baseline(X, k, budget_s=15.0):
     }
 
 
-def time_sections(ekh, datagen, reps=5):
+def time_bipartite(ekh, datagen, idx, m, oracle_too, n_clusters=40, reps=5):
+    """ekh_bipartite_assign on the section's kNN graph (every spike's 10 nearest
+    subset points), 40 starting labels drawn uniformly: median time per call,
+    rounds, and (with the CPU baseline) the oracle on the same graph."""
+    import numpy as np
+    import torch
+
+    init = torch.from_numpy(datagen.random_labels(m, n_clusters, 0)).cuda()
+    ws = torch.empty(ekh.bipartite_workspace_bytes(m, n_clusters), dtype=torch.uint8, device=idx.device)
+    ekh.bipartite_assign(idx, m, n_clusters, init, workspace=ws)
+    ts = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        left, right, rounds = ekh.bipartite_assign(idx, m, n_clusters, init, workspace=ws)
+        torch.cuda.synchronize()
+        ts.append(1000.0 * (time.perf_counter() - t0))
+    ms_call = float(np.median(ts))
+    res = {"ms": ms_call, "rounds": rounds, "ms_per_round": ms_call / rounds, "n": int(idx.shape[0]), "m": m,
+           "k": int(idx.shape[1]), "n_clusters": n_clusters, "labels_in_use": int(torch.unique(left).numel()),
+           "where": "device, one 4-byte read-back per round (host clock around the call)"}
+    if oracle_too:
+        from oracle import bipartite as obip
+        t0 = time.perf_counter()
+        obip.assign(idx.cpu().numpy(), m, n_clusters, init.cpu().numpy())
+        res["oracle_ms"] = 1000.0 * (time.perf_counter() - t0)
+    return res
+
+
+def time_sections(ekh, datagen, oracle_too=False, reps=5):
     """ekh_knn on the two section workloads (50,000 x 5,000 at d = 102, k = 10; and
     200,000 x 20,000 at d = 200, k = 10, in chunks of max_chunk_dots = 64e6): median
     time per call with inputs resident, the tile kernel's rate, and the pair rate."""
@@ -111,6 +140,9 @@ def time_sections(ekh, datagen, reps=5):
         out[name] = {"ms": ms_call, "pairs_per_s": pairs / (ms_call / 1e3), "k": k, "max_chunk_dots": dots,
                      "tile_launches": tk["launches"] // reps, "tile_ms": tk["ms"] / reps,
                      "tile_tflops": tk["flop"] / (tk["ms"] / 1e3) / 1e12 if tk["ms"] else None}
+        if name == "ks4_section_50000x102":
+            idx, _ = ekh.knn(X, Y, k, workspace=ws)
+            out["bipartite_assignment"] = time_bipartite(ekh, datagen, idx, Y.shape[1], oracle_too)
         del X, Y, ws
     return out
 
@@ -239,7 +271,7 @@ def main():
         "noise": int((labels < 0).sum()), "where": "host C++ (ekh_hdbscan_tail), device-to-host copy of the tree included",
         "end_to_end_ms": ms_step + tail_ms}
     if not args.no_sections:
-        result["knn_sections"] = time_sections(ekh, datagen)
+        result["knn_sections"] = time_sections(ekh, datagen, oracle_too=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(X, ms + 1)
         from oracle import hdbscan_tail as otail
