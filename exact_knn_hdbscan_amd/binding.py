@@ -97,6 +97,8 @@ def library() -> ctypes.CDLL:
             lib.ekh_mst_boruvka.argtypes = [_p, _i64, _i64, _i32, _p, _i32, _p, _p, _u32, _p, _p, _p, _p, _p, _sz,
                                             _p]
             lib.ekh_hdbscan_tail.argtypes = [_p, _p, _p, _i64, _i32, _p, _p, _p, _p, _p, _p, _p]
+            lib.ekh_cluster_edge_counts.argtypes = [_p, _i64, _i32, _i64, _p, _p, _i32, _p, _p, _sz, _p]
+            lib.ekh_merge_tree.argtypes = [_p, _i32, ctypes.c_double, _p, _p, _p]
             lib.ekh_bipartite_workspace_bytes.argtypes = [_i64, _i32]
             lib.ekh_bipartite_workspace_bytes.restype = _sz
             lib.ekh_bipartite_assign.argtypes = [_p, _i64, _i32, _i64, _i32, _p, ctypes.c_double, _i32, _p, _p, _p, _p,
@@ -288,6 +290,42 @@ def bipartite_assign(nbr: torch.Tensor, m: int, n_clusters: int, init_right: tor
                                     float(gamma), max_rounds, left.data_ptr(), right.data_ptr(), ctypes.byref(rounds),
                                     ws.data_ptr(), ws.numel(), _stream(dev)))
     return left, right, int(rounds.value)
+
+
+def cluster_edge_counts(nbr: torch.Tensor, left: torch.Tensor, right: torch.Tensor, n_clusters: int):
+    """Edge counts between clusters (ekh_cluster_edge_counts): uint32-valued
+    int64 tensor [C, C] on the GPU, counts[a, b] = edges (i, r) with left[i] = a
+    and right[r] = b."""
+    for t, name in ((nbr, "nbr"), (left, "left"), (right, "right")):
+        if t.dtype != torch.int32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(name + " must be a contiguous int32 CUDA tensor")
+    n, k = nbr.shape
+    m = right.shape[0]
+    dev = nbr.device
+    out = torch.empty((n_clusters, n_clusters), dtype=torch.int32, device=dev)
+    ws = _workspace(256, dev)
+    _check(library().ekh_cluster_edge_counts(nbr.data_ptr(), n, k, m, left.data_ptr(), right.data_ptr(), n_clusters,
+                                             out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev)))
+    return out.to(torch.int64) & 0xFFFFFFFF
+
+
+def merge_tree(counts, gamma: float = 1.0):
+    """Merging tree of the clusters (ekh_merge_tree, host code): counts [C, C]
+    (torch tensor on any device, or numpy; non-negative) -> list of (a, b, dQ)
+    for the C - 1 merges."""
+    import numpy as np
+
+    if isinstance(counts, torch.Tensor):
+        counts = counts.detach().to("cpu").numpy()
+    c = np.ascontiguousarray(counts, dtype=np.uint32)
+    C = c.shape[0]
+    if c.shape != (C, C):
+        raise ValueError("counts must be square")
+    a = np.empty(max(C - 1, 0), np.int32)
+    b = np.empty(max(C - 1, 0), np.int32)
+    g = np.empty(max(C - 1, 0), np.float64)
+    _check(library().ekh_merge_tree(c.ctypes.data, C, float(gamma), a.ctypes.data, b.ctypes.data, g.ctypes.data))
+    return [(int(x), int(y), float(z)) for x, y, z in zip(a, b, g)]
 
 
 class kernel_timer:

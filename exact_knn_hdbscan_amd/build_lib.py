@@ -21,7 +21,7 @@ SOURCES = [("tile_kernels.hip", "tile_kernels", []), ("boruvka_kernels.hip", "bo
            ("api.hip", "api", []), ("bipartite.hip", "bipartite", [])] + [("knn_inst.hip", "knn_k%d" % k, ["-DEKH_KNN_K=%d" % k]) for k in KNN_KS]
 # host-only C++ (no device code), built with g++; -ffp-contract=off keeps every
 # float64 expression as written (no fused multiply-adds)
-HOST_SOURCES = [("hdbscan_tail.cpp", "hdbscan_tail")]
+HOST_SOURCES = [("hdbscan_tail.cpp", "hdbscan_tail"), ("merge_tree.cpp", "merge_tree")]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no v_pk_*_f32 in generated code.

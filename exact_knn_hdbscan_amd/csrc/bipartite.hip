@@ -156,6 +156,23 @@ __global__ void bp_right_step(const uint32_t *counts, int64_t m, int64_t C, cons
     right[r] = (cur_present && cur_s == best_s) ? cur : best_c;
 }
 
+// counts[left(i) * C + right(r)] += 1 for every edge (i, r)
+__global__ void bp_edge_counts(const int32_t *nbr, int64_t n, int k, const int32_t *left, const int32_t *right,
+                               int64_t C, uint32_t *counts) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e < n * (int64_t)k) atomicAdd(&counts[(int64_t)left[e / k] * C + right[nbr[e]]], 1u);
+}
+
+// bad[0]: neighbour indices outside [0, m); bad[1]: left labels outside [0, C);
+// bad[2]: right labels outside [0, C)
+__global__ void bp_check_labels(const int32_t *nbr, int64_t edges, int64_t m, const int32_t *left, int64_t n,
+                                const int32_t *right, int64_t C, uint32_t *bad) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    count_wave(i < edges && (nbr[i] < 0 || nbr[i] >= m), &bad[0]);
+    count_wave(i < n && (left[i] < 0 || left[i] >= C), &bad[1]);
+    count_wave(i < m && (right[i] < 0 || right[i] >= C), &bad[2]);
+}
+
 struct Ws {
     uint32_t *deg, *K_right, *cnt_left, *counts, *ctr; // ctr: [0] moved, [1..2] bad
     size_t bytes;
@@ -246,5 +263,38 @@ extern "C" int ekh_bipartite_assign(const int32_t *nbr, int64_t n, int32_t k, in
         BP_HIP(hipGetLastError());
     }
     if (out_rounds) *out_rounds = rounds;
+    return EKH_OK;
+}
+
+// Edge counts between clusters ("Merges and splits": one more atomic kernel,
+// read back once by the caller).  Blocks: the range check reads back three
+// counters before any count is added.
+extern "C" int ekh_cluster_edge_counts(const int32_t *nbr, int64_t n, int32_t k, int64_t m, const int32_t *left,
+                                       const int32_t *right, int32_t n_clusters, uint32_t *out_counts, void *ws,
+                                       size_t ws_bytes, void *stream) {
+    if (!nbr || !left || !right || !out_counts) return fail(EKH_EINVAL, "NULL array");
+    if (n < 1 || m < 1) return fail(EKH_EINVAL, "n = %lld and m = %lld must be >= 1", (long long)n, (long long)m);
+    if (k < 1 || k > kMaxK) return fail(EKH_EINVAL, "k = %d out of range [1, %d]", k, kMaxK);
+    if (n_clusters < 1 || n_clusters > 46340) return fail(EKH_EINVAL, "n_clusters = %d out of range", n_clusters);
+    if (n * (int64_t)k >= (int64_t(1) << 31)) return fail(EKH_EINVAL, "n k = %lld edges >= 2^31", (long long)(n * k));
+    if (!ws) return fail(EKH_EINVAL, "workspace is NULL");
+    if (ws_bytes < 16) return fail(EKH_EWORKSPACE, "workspace %zu bytes < 16 needed", ws_bytes);
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t edges = n * (int64_t)k, C = n_clusters;
+    int64_t span = edges > m ? edges : m;
+    span = span > n ? span : n;
+    uint32_t *bad = (uint32_t *)ws;
+    uint32_t host[3];
+    hipLaunchKernelGGL(bp_fill, grid_for(3), dim3(kBs), 0, s, bad, (int64_t)3, 0u);
+    hipLaunchKernelGGL(bp_check_labels, grid_for(span), dim3(kBs), 0, s, nbr, edges, m, left, n, right, C, bad);
+    BP_HIP(hipGetLastError());
+    BP_HIP(hipMemcpyAsync(host, bad, sizeof host, hipMemcpyDeviceToHost, s));
+    BP_HIP(hipStreamSynchronize(s));
+    if (host[0]) return fail(EKH_EINVAL, "%u neighbour indices outside [0, m = %lld)", host[0], (long long)m);
+    if (host[1] || host[2])
+        return fail(EKH_EINVAL, "%u left and %u right labels outside [0, %d)", host[1], host[2], n_clusters);
+    hipLaunchKernelGGL(bp_fill, grid_for(C * C), dim3(kBs), 0, s, out_counts, C * C, 0u);
+    hipLaunchKernelGGL(bp_edge_counts, grid_for(edges), dim3(kBs), 0, s, nbr, n, k, left, right, C, out_counts);
+    BP_HIP(hipGetLastError());
     return EKH_OK;
 }

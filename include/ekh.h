@@ -194,6 +194,42 @@ int ekh_bipartite_assign(const int32_t *nbr, int64_t n, int32_t k, int64_t m, in
                          int32_t *out_right, int32_t *out_rounds, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Edge counts between clusters (device).  Source: "Kilosort4 clustering and
+ * matching", section "Merges and splits": the merging tree needs only the edge
+ * counts between clusters, counted on the device with one more atomic kernel
+ * and read back once.  out_counts [C, C] u32 (device, row-major, written
+ * whole): out_counts[a * C + b] = number of edges (spike i, subset point r) of
+ * nbr [n, k] with left[i] = a and right[r] = b.  ws: at least 16 bytes of device
+ * memory.  Blocks: three range counters are read back before any count is
+ * added.  Errors: EKH_EINVAL for a NULL array, sizes out of range
+ * (n_clusters > 46340, n k >= 2^31), neighbour indices outside [0, m) or labels
+ * outside [0, n_clusters); EKH_EWORKSPACE; EKH_EHIP.
+ */
+int ekh_cluster_edge_counts(const int32_t *nbr, int64_t n, int32_t k, int64_t m, const int32_t *left,
+                            const int32_t *right, int32_t n_clusters, uint32_t *out_counts, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/*
+ * Merging tree of the clusters, on the HOST (same section: building it is host
+ * work).  The page does not give the rule; this is greedy modularity
+ * agglomeration in the terms of the assignment above:
+ *  - the cluster graph is undirected, W[a, b] = counts[a, b] + counts[b, a];
+ *    M = total edges; K[a] = row sum + column sum of a (every edge adds one end
+ *    to its left label and one to its right label);
+ *  - each step merges the live pair a < b with the largest
+ *    dQ = W[a, b] / M - gamma K[a] K[b] / (2 M^2) (float64 in that order; 0
+ *    when M = 0); ties go to the smallest (a, b); the merged cluster keeps the
+ *    id a (W[a, .] += W[b, .], W[., a] += W[., b], K[a] += K[b]);
+ *  - all C - 1 merges are made, so the result is a full binary tree.
+ * counts [C, C] u32 HOST (e.g. ekh_cluster_edge_counts copied back);
+ * out_a, out_b [C - 1] int32 and out_gain [C - 1] float64 HOST, in merge order.
+ * Errors: EKH_EINVAL for a NULL array, n_clusters outside [1, 46340], gamma
+ * negative or not finite.  No GPU work; thread-safe.
+ */
+int ekh_merge_tree(const uint32_t *counts, int32_t n_clusters, double gamma, int32_t *out_a, int32_t *out_b,
+                   double *out_gain);
+
+/*
  * HDBSCAN tail, on the HOST: spanning tree -> single-linkage hierarchy ->
  * condensed tree -> excess-of-mass selection -> cluster labels.
  * Source: "HDBSCAN", section "The algorithm on the device", last item (the

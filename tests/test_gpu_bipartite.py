@@ -16,7 +16,6 @@ from exact_knn_hdbscan_amd import binding, datagen
 from gpu_util import say
 from oracle import bipartite as obip
 
-import test_bipartite_oracle as pins
 
 pytestmark = pytest.mark.gpu
 
@@ -100,3 +99,45 @@ def test_bad_arguments():
         ekh.bipartite_assign(nbr, 3, 2, init, gamma=-1.0)
     with pytest.raises(binding.EkhError):
         ekh.bipartite_assign(nbr, 3, 2, init, max_rounds=0)
+
+
+@pytest.mark.parametrize("n,m,k,C,seed", [(3000, 400, 10, 17, 0), (1, 5, 3, 2, 6), (4096, 256, 32, 200, 3)])
+def test_edge_counts_random(n, m, k, C, seed):
+    from oracle import merge_tree as omt
+    rng = np.random.default_rng(seed)
+    nbr = datagen.random_neighbour_lists(n, m, k, seed)
+    left = rng.integers(0, C, n).astype(np.int32)
+    right = datagen.random_labels(m, C, seed + 7)
+    got = ekh.cluster_edge_counts(torch.from_numpy(nbr).cuda(), torch.from_numpy(left).cuda(),
+                                  torch.from_numpy(right).cuda(), C).cpu().numpy()
+    np.testing.assert_array_equal(got, omt.edge_counts(nbr, left, right, C))
+    assert got.sum() == n * k
+
+
+def test_section_graph_counts_and_tree():
+    """The page's chain on the section: kNN -> assignment -> edge counts between
+    clusters -> merging tree, against the oracle's chain on the same graph."""
+    from oracle import merge_tree as omt
+    wl = datagen.make("ks4_section_50000x102")
+    X, Y = torch.from_numpy(wl["X"]).cuda(), torch.from_numpy(wl["Y"]).cuda()
+    idx, _ = ekh.knn(X, Y, 10)
+    m, C = Y.shape[1], 40
+    init = torch.from_numpy(datagen.random_labels(m, C, 0)).cuda()
+    left, right, _ = ekh.bipartite_assign(idx, m, C, init)
+    counts = ekh.cluster_edge_counts(idx, left, right, C)
+    nbr, l_h, r_h = idx.cpu().numpy(), left.cpu().numpy(), right.cpu().numpy()
+    want = omt.edge_counts(nbr, l_h, r_h, C)
+    np.testing.assert_array_equal(counts.cpu().numpy(), want)
+    got_tree = ekh.merge_tree(counts)
+    want_tree = omt.merge_tree(want)
+    assert got_tree == want_tree
+    say("section: %d merges, first %s" % (len(got_tree), got_tree[:2]))
+
+
+def test_edge_counts_bad_labels():
+    nbr = torch.zeros((4, 2), dtype=torch.int32, device="cuda")
+    left = torch.tensor([0, 1, 0, 3], dtype=torch.int32, device="cuda")  # 3 >= C
+    right = torch.zeros(3, dtype=torch.int32, device="cuda")
+    with pytest.raises(binding.EkhError) as e:
+        ekh.cluster_edge_counts(nbr, left, right, 2)
+    assert e.value.code == binding.EKH_EINVAL
