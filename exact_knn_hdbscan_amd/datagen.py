@@ -12,6 +12,9 @@ measure on; the recordings themselves are not public, so these stand in):
 * ``tiny``      2,000 x 60, mixture of 8 isotropic Gaussians.
 * ``ks4_section`` 50,000 x 102, mixture of 40 Gaussians, subset = every 10th point.
 * ``wide_section`` 200,000 x 200, 200 Gaussians + 5 % uniform outliers, subset every 10th.
+* ``ks4_seeding`` 1,416 x 102, mixture of 40 Gaussians, 200 k-means++ seeds
+  (the page's seeding section), with 1 + 199 * 8 uniforms
+  (the seeding uses the first 1 + 199 * 7).
 * ``clips``     100,000 x 61 biphasic spike clips from 20 templates (HDBSCAN page).
 * ``clips_large`` 500,000 x 61 clips from 60 templates + 3 % pure-noise clips.
 
@@ -139,6 +142,13 @@ def random_neighbour_lists(n: int, m: int, k: int, seed: int = 0) -> np.ndarray:
     return np.argsort(keys, axis=1)[:, :k].astype(np.int32)
 
 
+def uniforms53(count: int, seed: int = 0) -> np.ndarray:
+    """Uniform integers in [0, 2^53), uint64 [count]: the host-made uniforms
+    that the k-means++ seeding consumes."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, 1 << 53, size=count, dtype=np.uint64)
+
+
 def _tiny(seed=0):
     X = gaussian_mixture(2000, 60, 8, seed, means="uniform5", sigma="one")
     return {"X": X, "Y": X, "k": 10, "min_samples": 10, "self": True}
@@ -152,6 +162,13 @@ def _ks4_section(seed=0):
 def _wide_section(seed=0):
     X = gaussian_mixture(200_000, 200, 200, seed, outlier_frac=0.05)
     return {"X": X, "Y": every_kth(X, 10), "k": 10, "self": False, "max_chunk_bytes": 256_000_000}
+
+
+def _ks4_seeding(seed=0):
+    X = gaussian_mixture(1416, 102, 40, seed)
+    k = 200
+    # enough uniforms for up to 8 candidates per seed (the seeding uses 7)
+    return {"X": X, "k": k, "uniforms": uniforms53(1 + (k - 1) * 8, seed + 1)}
 
 
 def _clips(seed=0):
@@ -168,6 +185,7 @@ WORKLOADS = {
     "tiny_2000x60": _tiny,
     "ks4_section_50000x102": _ks4_section,
     "wide_section_200000x200": _wide_section,
+    "ks4_seeding_1416x102": _ks4_seeding,
     "clips_100000x61": _clips,
     "clips_500000x61": _clips_large,
 }
