@@ -116,6 +116,44 @@ def time_bipartite(ekh, datagen, idx, m, oracle_too, n_clusters=40, reps=5):
     return res
 
 
+def time_seeding(ekh, datagen, oracle_too, reps=10):
+    """ekh_kmeanspp on the page's seeding section (1,416 points, 102 features,
+    200 seeds, 7 candidates each): median time per call on the host clock
+    (launch cost included) and on stream events, and (with the CPU baseline)
+    the oracle on the same section, whose seeds must agree."""
+    import numpy as np
+    import torch
+
+    wl = datagen.make("ks4_seeding_1416x102")
+    X = torch.from_numpy(wl["X"]).cuda()
+    u = torch.from_numpy(wl["uniforms"].astype(np.int64)).cuda()
+    k = wl["k"]
+    ws = torch.empty(ekh.kmeanspp_workspace_bytes(X.shape[1], k), dtype=torch.uint8, device=X.device)
+    seeds, pot = ekh.kmeanspp(X, k, u, workspace=ws)
+    torch.cuda.synchronize()
+    wall, gpu = [], []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        seeds, pot = ekh.kmeanspp(X, k, u, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        wall.append(1000.0 * (time.perf_counter() - t0))
+        gpu.append(e0.elapsed_time(e1))
+    res = {"ms": float(np.median(wall)), "stream_ms": float(np.median(gpu)), "n": int(X.shape[1]),
+           "d": int(X.shape[0]), "seeds": k, "launches": 2 * k,
+           "where": "device, no host sync inside the call (host clock around call + sync)"}
+    if oracle_too:
+        from oracle import kmeanspp as okm
+        t0 = time.perf_counter()
+        want, want_pot = okm.seed(wl["X"], k, wl["uniforms"])
+        res["oracle_ms"] = 1000.0 * (time.perf_counter() - t0)
+        res["matches_oracle"] = seeds.cpu().numpy().tolist() == want and int(pot.item()) == want_pot
+    return res
+
+
 def time_sections(ekh, datagen, oracle_too=False, reps=5):
     """ekh_knn on the two section workloads (50,000 x 5,000 at d = 102, k = 10; and
     200,000 x 20,000 at d = 200, k = 10, in chunks of max_chunk_dots = 64e6): median
@@ -281,6 +319,7 @@ def main():
         "end_to_end_ms": ms_step + tail_ms}
     if not args.no_sections:
         result["knn_sections"] = time_sections(ekh, datagen, oracle_too=not args.no_cpu_baseline)
+        result["kmeanspp_seeding"] = time_seeding(ekh, datagen, oracle_too=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(X, ms + 1)
         from oracle import hdbscan_tail as otail

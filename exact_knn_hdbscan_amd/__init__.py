@@ -7,7 +7,7 @@ that ``exact_knn_hdbscan_amd.datagen`` can be imported without a GPU.
 """
 _ENTRY_POINTS = ("knn", "core_distances", "mst_boruvka", "knn_workspace_bytes", "core_workspace_bytes",
                  "mst_workspace_bytes", "hdbscan_tail", "bipartite_assign", "bipartite_workspace_bytes",
-                 "cluster_edge_counts", "merge_tree", "library", "MstStats", "EkhError", "kernel_timer")
+                 "cluster_edge_counts", "merge_tree", "kmeanspp", "kmeanspp_workspace_bytes", "library", "MstStats", "EkhError", "kernel_timer")
 
 __all__ = list(_ENTRY_POINTS)
 

@@ -18,7 +18,8 @@ LIB = os.path.join(PKG, "libekh.so")
 # (source, object name, extra flags); the kNN kernels are instantiated once per list length
 KNN_KS = [2, 4, 8, 11, 16, 32]
 SOURCES = [("tile_kernels.hip", "tile_kernels", []), ("boruvka_kernels.hip", "boruvka_kernels", []),
-           ("api.hip", "api", []), ("bipartite.hip", "bipartite", [])] + [("knn_inst.hip", "knn_k%d" % k, ["-DEKH_KNN_K=%d" % k]) for k in KNN_KS]
+           ("api.hip", "api", []), ("bipartite.hip", "bipartite", []),
+           ("kmeanspp.hip", "kmeanspp", ["-ffp-contract=off"])] + [("knn_inst.hip", "knn_k%d" % k, ["-DEKH_KNN_K=%d" % k]) for k in KNN_KS]
 # host-only C++ (no device code), built with g++; -ffp-contract=off keeps every
 # float64 expression as written (no fused multiply-adds)
 HOST_SOURCES = [("hdbscan_tail.cpp", "hdbscan_tail"), ("merge_tree.cpp", "merge_tree")]

@@ -230,6 +230,43 @@ int ekh_merge_tree(const uint32_t *counts, int32_t n_clusters, double gamma, int
                    double *out_gain);
 
 /*
+ * Greedy k-means++ seeding of a section.  Source: "Kilosort4 clustering and
+ * matching", section "The measurement that changed the design: serial chains
+ * inside a thread": each new seed is the best of 2 + ln k candidates drawn by
+ * squared distance, from uniforms made on the host and uploaded once; every
+ * draw, score and pick runs on the device, with no host sync.  The page leaves
+ * the arithmetic open; the conventions here make every decision exact:
+ *  - L = 2 + floor(ln k) candidates per seed after the first (7 at k = 200);
+ *  - squared distances are float32, summed over features in order from 0,
+ *    every subtraction, product and sum rounded (nothing fused);
+ *  - with D1 the squared distances to the first seed and 2^(e-1) <= max D1
+ *    < 2^e, S = 40 - e (0 when max D1 = 0); a squared distance D has the
+ *    integer weight floor(D 2^S), and w(x) is point x's weight to its
+ *    nearest seed so far; all sums are exact 64-bit integers;
+ *  - only the low 53 bits of each uniform are used (u in [0, 2^53)), in order:
+ *    uniforms[0] gives the first seed, point floor(u n / 2^53); seed s >= 1
+ *    draws its candidates j = 0..L-1 from uniforms[1 + (s - 1) L + j];
+ *  - a candidate is the first point whose inclusive prefix sum of w exceeds
+ *    floor(u T / 2^53), T = sum of w (point 0 when T = 0);
+ *  - a candidate's potential is sum_x min(w(x), floor(D(x, cand) 2^S)); the
+ *    smallest wins, ties going to the candidate drawn first.
+ * X [d, n] float32 device, feature-major with leading dimension ldx >= n;
+ * uniforms [n_uniforms] device, n_uniforms >= 1 + (k - 1) L; out_seeds [k]
+ * int32 device (point indices in seed order; a seed repeats only when every
+ * weight is 0, e.g. fewer than k distinct points); out_potential (device, one
+ * int64, nullable): the final sum of w.  Workspace:
+ * ekh_kmeanspp_workspace_bytes(n, k) bytes of device memory.  Enqueued on
+ * `stream`, 2 k launches, no host sync.  Inputs must be finite (not checked).
+ * Errors: EKH_EINVAL for a NULL array, n outside [1, 2^22], d outside
+ * [1, 8192], k outside [1, 2^20], ldx < n or too few uniforms;
+ * EKH_EWORKSPACE; EKH_EHIP.
+ */
+size_t ekh_kmeanspp_workspace_bytes(int64_t n, int32_t k);
+int ekh_kmeanspp(const float *X, int64_t ldx, int64_t n, int32_t d, int32_t k, const uint64_t *uniforms,
+                 int64_t n_uniforms, int32_t *out_seeds, int64_t *out_potential, void *ws, size_t ws_bytes,
+                 void *stream);
+
+/*
  * HDBSCAN tail, on the HOST: spanning tree -> single-linkage hierarchy ->
  * condensed tree -> excess-of-mass selection -> cluster labels.
  * Source: "HDBSCAN", section "The algorithm on the device", last item (the
