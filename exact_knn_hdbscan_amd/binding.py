@@ -103,9 +103,9 @@ def library() -> ctypes.CDLL:
             lib.ekh_bipartite_workspace_bytes.restype = _sz
             lib.ekh_bipartite_assign.argtypes = [_p, _i64, _i32, _i64, _i32, _p, ctypes.c_double, _i32, _p, _p, _p, _p,
                                                  _sz, _p]
-            lib.ekh_kmeanspp_workspace_bytes.argtypes = [_i64, _i32]
+            lib.ekh_kmeanspp_workspace_bytes.argtypes = [_i64, _i32, _u32]
             lib.ekh_kmeanspp_workspace_bytes.restype = _sz
-            lib.ekh_kmeanspp.argtypes = [_p, _i64, _i64, _i32, _i32, _p, _i64, _p, _p, _p, _sz, _p]
+            lib.ekh_kmeanspp.argtypes = [_p, _i64, _i64, _i32, _i32, _p, _i64, _u32, _p, _p, _p, _sz, _p]
             lib.ekh_timer_enable.argtypes = [ctypes.c_int]
             lib.ekh_timer_read.argtypes = [ctypes.c_int, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double),
                                            ctypes.POINTER(ctypes.c_double)]
@@ -312,15 +312,22 @@ def cluster_edge_counts(nbr: torch.Tensor, left: torch.Tensor, right: torch.Tens
     return out.to(torch.int64) & 0xFFFFFFFF
 
 
-def kmeanspp_workspace_bytes(n: int, k: int) -> int:
-    return int(library().ekh_kmeanspp_workspace_bytes(n, k))
+EKH_KMEANSPP_PER_SEED_LAUNCHES = 1
 
 
-def kmeanspp(X: torch.Tensor, k: int, uniforms: torch.Tensor, workspace: torch.Tensor = None):
+def kmeanspp_workspace_bytes(n: int, k: int, per_seed_launches: bool = False) -> int:
+    return int(library().ekh_kmeanspp_workspace_bytes(n, k, EKH_KMEANSPP_PER_SEED_LAUNCHES if per_seed_launches
+                                                       else 0))
+
+
+def kmeanspp(X: torch.Tensor, k: int, uniforms: torch.Tensor, per_seed_launches: bool = False,
+             workspace: torch.Tensor = None):
     """Greedy k-means++ seeding (ekh_kmeanspp) of the columns of X [d, n]
     (float32 on the GPU).  uniforms: int64 or uint64 CUDA tensor of at least
-    1 + (k - 1) (2 + floor(ln k)) values in [0, 2^53).  Returns (seeds int32 [k],
-    potential int64 [1]), both on the GPU; nothing is read back."""
+    1 + (k - 1) (2 + floor(ln k)) values in [0, 2^53).  per_seed_launches
+    forces the two-launches-per-seed path (same results, less workspace).
+    Returns (seeds int32 [k], potential int64 [1]), both on the GPU; nothing is
+    read back."""
     Xp, ldx, n, d = _points(X, "X")
     if uniforms.dtype not in (torch.int64, torch.uint64) or uniforms.dim() != 1 or not uniforms.is_cuda \
             or not uniforms.is_contiguous():
@@ -328,8 +335,9 @@ def kmeanspp(X: torch.Tensor, k: int, uniforms: torch.Tensor, workspace: torch.T
     dev = X.device
     seeds = torch.empty(k, dtype=torch.int32, device=dev)
     pot = torch.empty(1, dtype=torch.int64, device=dev)
-    ws = workspace if workspace is not None else _workspace(kmeanspp_workspace_bytes(n, k), dev)
-    _check(library().ekh_kmeanspp(Xp, ldx, n, d, k, uniforms.data_ptr(), uniforms.numel(), seeds.data_ptr(),
+    flags = EKH_KMEANSPP_PER_SEED_LAUNCHES if per_seed_launches else 0
+    ws = workspace if workspace is not None else _workspace(kmeanspp_workspace_bytes(n, k, per_seed_launches), dev)
+    _check(library().ekh_kmeanspp(Xp, ldx, n, d, k, uniforms.data_ptr(), uniforms.numel(), flags, seeds.data_ptr(),
                                   pot.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev)))
     return seeds, pot
 

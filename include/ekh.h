@@ -254,17 +254,24 @@ int ekh_merge_tree(const uint32_t *counts, int32_t n_clusters, double gamma, int
  * uniforms [n_uniforms] device, n_uniforms >= 1 + (k - 1) L; out_seeds [k]
  * int32 device (point indices in seed order; a seed repeats only when every
  * weight is 0, e.g. fewer than k distinct points); out_potential (device, one
- * int64, nullable): the final sum of w.  Workspace:
- * ekh_kmeanspp_workspace_bytes(n, k) bytes of device memory.  Enqueued on
- * `stream`, 2 k launches, no host sync.  Inputs must be finite (not checked).
+ * int64, nullable): the final sum of w.
+ * Two paths with identical results: sections with n <= 4096,
+ * n <= 4 (1 + (k - 1) L) and L <= 7 (k <= 403) compute the n x n matrix of squared
+ * distances once (n^2 4 bytes of workspace) and seed in one persistent
+ * block (2 launches in all); otherwise, or with flags
+ * EKH_KMEANSPP_PER_SEED_LAUNCHES, two launches per seed (about 24 n bytes of
+ * workspace).  Workspace: ekh_kmeanspp_workspace_bytes(n, k, flags) bytes of
+ * device memory (0 for arguments out of range).  Enqueued on `stream`, no
+ * host sync.  Inputs must be finite (not checked).
  * Errors: EKH_EINVAL for a NULL array, n outside [1, 2^22], d outside
- * [1, 8192], k outside [1, 2^20], ldx < n or too few uniforms;
- * EKH_EWORKSPACE; EKH_EHIP.
+ * [1, 8192], k outside [1, 2^20], ldx outside [n, 2^25), unknown flags or
+ * too few uniforms; EKH_EWORKSPACE; EKH_EHIP.
  */
-size_t ekh_kmeanspp_workspace_bytes(int64_t n, int32_t k);
+#define EKH_KMEANSPP_PER_SEED_LAUNCHES 1u
+size_t ekh_kmeanspp_workspace_bytes(int64_t n, int32_t k, uint32_t flags);
 int ekh_kmeanspp(const float *X, int64_t ldx, int64_t n, int32_t d, int32_t k, const uint64_t *uniforms,
-                 int64_t n_uniforms, int32_t *out_seeds, int64_t *out_potential, void *ws, size_t ws_bytes,
-                 void *stream);
+                 int64_t n_uniforms, uint32_t flags, int32_t *out_seeds, int64_t *out_potential, void *ws,
+                 size_t ws_bytes, void *stream);
 
 /*
  * HDBSCAN tail, on the HOST: spanning tree -> single-linkage hierarchy ->

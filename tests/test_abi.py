@@ -97,17 +97,24 @@ def test_bipartite_rejects_bad_arguments(lib):
 def test_kmeanspp_rejects_bad_arguments(lib):
     f = lib.ekh_kmeanspp
     # k = 200 -> L = 7 candidates, 1 + 199 * 7 = 1394 uniforms
-    ok = dict(X=BOGUS, ldx=1416, n=1416, d=102, k=200, u=BOGUS, nu=1394, seeds=BOGUS, ws=BOGUS, ws_bytes=1 << 30)
+    ok = dict(X=BOGUS, ldx=1416, n=1416, d=102, k=200, u=BOGUS, nu=1394, fl=0, seeds=BOGUS, ws=BOGUS,
+              ws_bytes=1 << 30)
     for change in (dict(X=None), dict(u=None), dict(seeds=None), dict(ws=None), dict(n=0), dict(n=(1 << 22) + 1),
-                   dict(d=0), dict(d=8193), dict(ldx=1415), dict(k=0), dict(k=(1 << 20) + 1), dict(nu=1393)):
+                   dict(d=0), dict(d=8193), dict(ldx=1415), dict(ldx=1 << 25), dict(k=0), dict(k=(1 << 20) + 1),
+                   dict(nu=1393), dict(fl=2)):
         a = dict(ok, **change)
-        rc = f(a["X"], a["ldx"], a["n"], a["d"], a["k"], a["u"], a["nu"], a["seeds"], None, a["ws"], a["ws_bytes"],
-               None)
+        rc = f(a["X"], a["ldx"], a["n"], a["d"], a["k"], a["u"], a["nu"], a["fl"], a["seeds"], None, a["ws"],
+               a["ws_bytes"], None)
         assert rc == -1, change
         assert lib.ekh_last_error()
-    a = dict(ok, ws_bytes=64)
-    assert f(a["X"], a["ldx"], a["n"], a["d"], a["k"], a["u"], a["nu"], a["seeds"], None, a["ws"], a["ws_bytes"],
-             None) == -2
-    assert lib.ekh_kmeanspp_workspace_bytes(1416, 200) >= 8 * 1416 * 8
-    assert lib.ekh_kmeanspp_workspace_bytes(0, 200) == 0
-    assert lib.ekh_kmeanspp_workspace_bytes(1416, 0) == 0
+    for fl in (0, 1):
+        a = dict(ok, ws_bytes=64, fl=fl)
+        assert f(a["X"], a["ldx"], a["n"], a["d"], a["k"], a["u"], a["nu"], a["fl"], a["seeds"], None, a["ws"],
+                 a["ws_bytes"], None) == -2
+    # the section fits the distance-matrix path (n^2 floats); forced per-seed launches need ~24 n bytes
+    assert lib.ekh_kmeanspp_workspace_bytes(1416, 200, 0) >= 4 * 1416 * 1416
+    assert 8 * 1416 * 8 <= lib.ekh_kmeanspp_workspace_bytes(1416, 200, 1) < 4 * 1416 * 1416
+    assert lib.ekh_kmeanspp_workspace_bytes(100000, 200, 0) == lib.ekh_kmeanspp_workspace_bytes(100000, 200, 1)
+    assert lib.ekh_kmeanspp_workspace_bytes(0, 200, 0) == 0
+    assert lib.ekh_kmeanspp_workspace_bytes(1416, 0, 0) == 0
+    assert lib.ekh_kmeanspp_workspace_bytes(1416, 200, 4) == 0
