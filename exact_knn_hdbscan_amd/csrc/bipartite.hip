@@ -74,16 +74,73 @@ __global__ void bp_copy_labels(const int32_t *src, int64_t count, int32_t *dst) 
     if (i < count) dst[i] = src[i];
 }
 
+// Histograms with few bins (the label totals, the cluster edge counts) put
+// many atomics on few addresses.  With at most kLdsBins bins each block first
+// counts into LDS and then adds its non-zero bins once; the block count is set
+// so that a block sees several items per bin.  Integer sums: the result does
+// not depend on the order.
+constexpr int kLdsBins = 8192;   // 32 KB of LDS
+constexpr int kHistMaxBlocks = 256;
+
 // K_right[c] = total degree of the right nodes labelled c
-__global__ void bp_totals_right(const int32_t *right, const uint32_t *deg, int64_t m, uint32_t *K_right) {
-    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (r < m && deg[r]) atomicAdd(&K_right[right[r]], deg[r]);
-}
+struct RightTotals {
+    const int32_t *right;
+    const uint32_t *deg;
+    __device__ uint32_t bin(int64_t r) const { return (uint32_t)right[r]; }
+    __device__ uint32_t weight(int64_t r) const { return deg[r]; }
+};
 
 // cnt_left[c] = spikes labelled c (their total degree is k cnt_left[c])
-__global__ void bp_totals_left(const int32_t *left, int64_t n, uint32_t *cnt_left) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) atomicAdd(&cnt_left[left[i]], 1u);
+struct LeftCounts {
+    const int32_t *left;
+    __device__ uint32_t bin(int64_t i) const { return (uint32_t)left[i]; }
+    __device__ uint32_t weight(int64_t) const { return 1u; }
+};
+
+// counts[left(i) * C + right(r)] += 1 for every edge (i, r)
+struct EdgeBins {
+    const int32_t *nbr, *left, *right;
+    int k;
+    int64_t C;
+    __device__ uint32_t bin(int64_t e) const { return (uint32_t)((int64_t)left[e / k] * C + right[nbr[e]]); }
+    __device__ uint32_t weight(int64_t) const { return 1u; }
+};
+
+template <class F>
+__global__ __launch_bounds__(kBs) void bp_hist_lds(F f, int64_t items, int bins, uint32_t *out) {
+    __shared__ uint32_t h[kLdsBins];
+    for (int b = threadIdx.x; b < bins; b += kBs) h[b] = 0;
+    __syncthreads();
+    for (int64_t i = (int64_t)blockIdx.x * kBs + threadIdx.x; i < items; i += (int64_t)gridDim.x * kBs) {
+        const uint32_t w = f.weight(i);
+        if (w) atomicAdd(&h[f.bin(i)], w);
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < bins; b += kBs)
+        if (h[b]) atomicAdd(&out[b], h[b]);
+}
+
+template <class F>
+__global__ __launch_bounds__(kBs) void bp_hist_global(F f, int64_t items, uint32_t *out) {
+    const int64_t i = (int64_t)blockIdx.x * kBs + threadIdx.x;
+    if (i < items) {
+        const uint32_t w = f.weight(i);
+        if (w) atomicAdd(&out[f.bin(i)], w);
+    }
+}
+
+// out[f.bin(i)] += f.weight(i) for every item (out already cleared)
+template <class F>
+void histogram(F f, int64_t items, int64_t bins, uint32_t *out, hipStream_t s) {
+    if (bins <= kLdsBins) {
+        int64_t blocks = items / (8 * bins); // about eight items per bin and block
+        blocks = blocks < 1 ? 1 : blocks > kHistMaxBlocks ? kHistMaxBlocks : blocks;
+        const int64_t most = (items + kBs - 1) / kBs;
+        blocks = blocks > most ? (most < 1 ? 1 : most) : blocks;
+        hipLaunchKernelGGL(bp_hist_lds<F>, dim3((unsigned)blocks), dim3(kBs), 0, s, f, items, (int)bins, out);
+    } else {
+        hipLaunchKernelGGL(bp_hist_global<F>, grid_for(items), dim3(kBs), 0, s, f, items, out);
+    }
 }
 
 // Left step: one thread per spike; its k neighbours' labels are counted in
@@ -154,13 +211,6 @@ __global__ void bp_right_step(const uint32_t *counts, int64_t m, int64_t C, cons
         }
     }
     right[r] = (cur_present && cur_s == best_s) ? cur : best_c;
-}
-
-// counts[left(i) * C + right(r)] += 1 for every edge (i, r)
-__global__ void bp_edge_counts(const int32_t *nbr, int64_t n, int k, const int32_t *left, const int32_t *right,
-                               int64_t C, uint32_t *counts) {
-    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e < n * (int64_t)k) atomicAdd(&counts[(int64_t)left[e / k] * C + right[nbr[e]]], 1u);
 }
 
 // bad[0]: neighbour indices outside [0, m); bad[1]: left labels outside [0, C);
@@ -244,7 +294,7 @@ extern "C" int ekh_bipartite_assign(const int32_t *nbr, int64_t n, int32_t k, in
     for (int32_t rnd = 1; rnd <= max_rounds; ++rnd) {
         hipLaunchKernelGGL(bp_fill, grid_for(C), dim3(kBs), 0, s, w.K_right, C, 0u);
         hipLaunchKernelGGL(bp_fill, grid_for(1), dim3(kBs), 0, s, w.ctr, (int64_t)1, 0u);
-        hipLaunchKernelGGL(bp_totals_right, grid_for(m), dim3(kBs), 0, s, out_right, w.deg, m, w.K_right);
+        histogram(RightTotals{out_right, w.deg}, m, C, w.K_right, s);
         hipLaunchKernelGGL(bp_left_step, grid_for(n), dim3(kBs), 0, s, nbr, n, k, out_right, w.K_right, two_m, gamma,
                            out_left, w.ctr);
         BP_HIP(hipGetLastError());
@@ -256,7 +306,7 @@ extern "C" int ekh_bipartite_assign(const int32_t *nbr, int64_t n, int32_t k, in
         }
         hipLaunchKernelGGL(bp_fill, grid_for(C), dim3(kBs), 0, s, w.cnt_left, C, 0u);
         hipLaunchKernelGGL(bp_fill, grid_for(m * C), dim3(kBs), 0, s, w.counts, m * C, 0u);
-        hipLaunchKernelGGL(bp_totals_left, grid_for(n), dim3(kBs), 0, s, out_left, n, w.cnt_left);
+        histogram(LeftCounts{out_left}, n, C, w.cnt_left, s);
         hipLaunchKernelGGL(bp_count, grid_for(edges), dim3(kBs), 0, s, nbr, n, k, out_left, C, w.counts);
         hipLaunchKernelGGL(bp_right_step, grid_for(m), dim3(kBs), 0, s, w.counts, m, C, w.deg, w.cnt_left, k, two_m,
                            gamma, out_right);
@@ -294,7 +344,7 @@ extern "C" int ekh_cluster_edge_counts(const int32_t *nbr, int64_t n, int32_t k,
     if (host[1] || host[2])
         return fail(EKH_EINVAL, "%u left and %u right labels outside [0, %d)", host[1], host[2], n_clusters);
     hipLaunchKernelGGL(bp_fill, grid_for(C * C), dim3(kBs), 0, s, out_counts, C * C, 0u);
-    hipLaunchKernelGGL(bp_edge_counts, grid_for(edges), dim3(kBs), 0, s, nbr, n, k, left, right, C, out_counts);
+    histogram(EdgeBins{nbr, left, right, k, C}, edges, C * C, out_counts, s);
     BP_HIP(hipGetLastError());
     return EKH_OK;
 }
