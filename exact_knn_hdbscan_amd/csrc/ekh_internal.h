@@ -22,7 +22,8 @@ constexpr int kThreads = kWaves * 64; // 256 threads
 // QM = k-steps held in registers (4 features each): d <= 4 * QM.
 // CB = 16-column query blocks per wave; TR = database rows per LDS tile.
 template <int QM> struct TileGeo;
-template <> struct TileGeo<16> { static constexpr int TR = 32; };
+// d <= 64: 64-row tiles (128 MFMAs per wave between barriers)
+template <> struct TileGeo<16> { static constexpr int TR = 64; };
 template <> struct TileGeo<32> { static constexpr int TR = 32; };
 // d > 128: 16-row tiles keep the prefetch registers and the LDS tile small
 // enough for two workgroups per CU
@@ -37,7 +38,7 @@ inline int pick_k(int k) {
     return -1;
 }
 inline int pick_qm(int d) { return d <= 64 ? 16 : (d <= 128 ? 32 : 64); }
-inline int tile_rows(int qm) { return qm == 64 ? 16 : 32; }
+inline int tile_rows(int qm) { return qm == 64 ? 16 : qm == 16 ? 64 : 32; }
 // 16-column query blocks per wave: two when the registers allow it
 constexpr int knn_col_blocks(int K, int QM) { return (K > 11 || QM > 16) ? 1 : 2; }
 constexpr int scan_col_blocks(int QM) { return QM > 16 ? 1 : 2; }

@@ -44,11 +44,14 @@ template <int QM> struct Tile {
 };
 
 // Streams database tiles [t_begin, t_end) through a double-buffered LDS tile
-// (row-major: [row][feature]) and hands each tile's accumulator blocks to
-// epi.tile().  The loop is software-pipelined: while the MFMAs of tile t run
-// into one accumulator set, the epilogue consumes tile t - 1 from the other,
-// and the global loads of tile t + 2 are in flight.  Slots: tile t's norms are
-// in slot (t - t_begin) mod 3.  Per-row norms (and, with
+// (row-major: [row][feature]) and hands each tile's accumulator blocks to the
+// epilogue.  One trip per tile, one barrier: the global loads of tile t + 1
+// are in flight while the MFMAs of tile t run into one accumulator set and
+// the epilogue consumes tile t - 1 from the other.  An epilogue with a split
+// form (kSplitEpi) does its bound update before the MFMAs and its per-element
+// fast test right after them, in the same basic block, so the scheduler can
+// interleave that test with the MFMAs; its list insertions come last.  Slots:
+// tile t's norms are in slot (t - t_begin) mod 3.  Per-row norms (and, with
 // PAYLOAD, component labels and core distances) live in a three-slot ring so
 // that tile t - 1's stay valid while tile t + 1's are stored.  FULL: the
 // dimension fills all QM k-steps, so the k-loop has no runtime guard.
@@ -205,47 +208,51 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
     };
 
     if (t_begin >= t_end) return;
-    // ring slot of tile t is (t - t_begin) mod 3, tracked without division
-    auto next3 = [](int x) { return x == 2 ? 0 : x + 1; };
-    Pref P0, P1;
-    load(P0, t_begin);
-    store(P0, 0, 0);
-    load(P1, t_begin + 1);
+    constexpr bool kSplit = Epi::kSplitEpi;
+    Pref P;
+    load(P, t_begin);
+    store(P, 0, 0);
     __syncthreads();
+    if (t_begin + 1 < t_end) load(P, t_begin + 1);
     f4 accA[T::RB][CB], accB[T::RB][CB];
-    // first tile: no previous epilogue
-    load(P0, t_begin + 2);
     mma(0, accA);
-    if (t_begin + 1 < t_end) store(P1, 1, 1);
+    if (t_begin + 1 < t_end) store(P, 1, 1);
     __syncthreads();
-    int buf = 1;
-    int sl = 1; // slot of tile t below
-    // Steady state, two tiles per trip (the accumulator and prefetch sets
-    // alternate): the MFMAs of tile t and the epilogue of tile t - 1 are
-    // straight-line neighbours, so the scheduler can interleave them.
-    for (int64_t t = t_begin + 1; t < t_end; t += 2) {
-        const int sl1 = next3(sl), sl2 = next3(sl1), slp = sl2; // t + 1, t + 2, t - 1
-        load(P1, t + 2);
-        mma(buf, accB);
-        finish(accA, t - 1, slp);
-        if (t + 1 < t_end) store(P0, buf ^ 1, sl1);
+    int buf = 1, sl = 1; // tile t's buffer and norm slot
+    auto next3 = [](int x) { return x == 2 ? 0 : x + 1; };
+    // one trip: the MFMAs of tile t into `cur`, the epilogue of tile t - 1 from `prev`
+    auto trip = [&](int64_t t, f4 (&cur)[T::RB][CB], f4 (&prev)[T::RB][CB]) {
+        const int slp = sl == 0 ? 2 : sl - 1, sln = next3(sl);
+        if (t + 1 < t_end) load(P, t + 1);
+        if constexpr (kSplit) {
+            epi.prepare();
+            f4 nb4[T::RB];
+#pragma unroll
+            for (int rb = 0; rb < T::RB; ++rb) nb4[rb] = *reinterpret_cast<const f4 *>(sm_nrm[slp] + rb * 16 + 4 * g);
+            bool hit[CB];
+            mma(buf, cur);
+            epi.fast(prev, nb4, hit);
+            epi.slow(prev, nb4, hit, (t - 1) * T::TR);
+        } else {
+            mma(buf, cur);
+            finish(prev, t - 1, slp);
+        }
+        if (t + 1 < t_end) store(P, buf ^ 1, sln);
         __syncthreads();
         buf ^= 1;
-        if (t + 1 >= t_end) break;
-        load(P0, t + 3);
-        mma(buf, accA);
-        finish(accB, t, sl);
-        if (t + 2 < t_end) store(P1, buf ^ 1, sl2);
-        __syncthreads();
-        buf ^= 1;
-        sl = sl2;
+        sl = sln;
+    };
+    int64_t t = t_begin + 1;
+    for (; t + 1 < t_end; t += 2) {
+        trip(t, accB, accA);
+        trip(t + 1, accA, accB);
     }
-    const int64_t last = t_end - 1;
-    const int lsl = (int)((last - t_begin) % 3);
-    if (((last - t_begin) & 1) == 0)
-        finish(accA, last, lsl);
-    else
-        finish(accB, last, lsl);
+    if (t < t_end) { // one tile left: its MFMAs with tile t - 1's epilogue, then its own epilogue
+        trip(t, accB, accA);
+        finish(accB, t, sl == 0 ? 2 : sl - 1);
+    } else {
+        finish(accA, t - 1, sl == 0 ? 2 : sl - 1);
+    }
 }
 
 // Loads the register-resident query operand: lane (g, i) holds feature
@@ -448,17 +455,16 @@ template <int K, int CB, int RB> struct EpiKnn {
     // widening by 2^-20 (adm + nq) covers it with room to spare.  The test only
     // decides whether a lane looks at its candidates: those are then taken with
     // the exact D2 and the exact bound, so results do not depend on the margin.
-    __device__ __forceinline__ void tile(const f4 (&acc)[RB][CB], const float *nrm, const int32_t *, const float *,
-                                         int64_t j0) {
+    //
+    // Split form: prepare() re-forms the bound (only when a list of the wave
+    // changed: a wave-uniform test), fast() is the branch-free test, slow()
+    // inserts the candidates of the columns that passed; tile() runs all three.
+    static constexpr bool kSplitEpi = true;
+    __device__ __forceinline__ void prepare() {
         constexpr float kWiden = 1.0f / 1048576.0f;
-        f4 nb4[RB];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) nb4[rb] = *reinterpret_cast<const f4 *>(nrm + rb * 16 + 4 * g);
-        // the bound changes only when a list of the wave changed (wave-uniform test)
         if (__builtin_amdgcn_ballot_w64(dirty)) {
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
-                // list entries are >= 0 or +inf (clamped on insertion)
                 const float gq = kSecond ? __uint_as_float(group_second_u32(__float_as_uint(qj[cb]),
                                                                              __float_as_uint(qj1[cb])))
                                          : group_max_nonneg(qj[cb]);
@@ -467,7 +473,8 @@ template <int K, int CB, int RB> struct EpiKnn {
             }
             dirty = false;
         }
-        bool hit[CB];
+    }
+    __device__ __forceinline__ void fast(const f4 (&acc)[RB][CB], const f4 (&nb4)[RB], bool (&hit)[CB]) const {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             float mn = INFINITY;
@@ -477,6 +484,9 @@ template <int K, int CB, int RB> struct EpiKnn {
                 for (int r = 0; r < 4; ++r) mn = fminf(mn, fmaf(-2.f, acc[rb][cb][r], nb4[rb][r]));
             hit[cb] = mn <= admq[cb];
         }
+    }
+    __device__ __forceinline__ void slow(const f4 (&acc)[RB][CB], const f4 (&nb4)[RB], const bool (&hit)[CB],
+                                         int64_t j0) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             if (!hit[cb]) continue;
@@ -496,6 +506,16 @@ template <int K, int CB, int RB> struct EpiKnn {
             if (kSecond) qj1[cb] = L.d[J - 1];
             dirty = true;
         }
+    }
+    __device__ __forceinline__ void tile(const f4 (&acc)[RB][CB], const float *nrm, const int32_t *, const float *,
+                                         int64_t j0) {
+        f4 nb4[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) nb4[rb] = *reinterpret_cast<const f4 *>(nrm + rb * 16 + 4 * g);
+        prepare();
+        bool hit[CB];
+        fast(acc, nb4, hit);
+        slow(acc, nb4, hit, j0);
     }
 };
 
