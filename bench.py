@@ -69,12 +69,19 @@ def cpu_baseline(X, k, budget_s=15.0):
         oracle.knn(np.ascontiguousarray(X[:, rows:rows + b]), X, k)
         rows += b
     dt = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": rows * n / dt,
         "unit": "pairs/s",
         "cores": oracle.max_threads(),
         "kind": "oracle",
         "sample": "float64 exact %d-NN of the first %d of %d points against all %d (%.1f s)" % (k, rows, n, n, dt),
+        "cpu_model": model,
     }
 
 

@@ -184,11 +184,23 @@ int orc_prim(const float *X, int64_t ldx, int64_t n, int d, const double *core, 
     }
     int64_t u = 0; /* vertex just added */
     in_tree[0] = 1;
+    /* threads per step: one per 2^18 distance terms of the step (the step's
+       minimum is taken under a strict total order, so the result does not
+       depend on the thread count; small sets then avoid a parallel region's
+       start-up cost on each of their n - 1 steps) */
+    int nt_step = 1;
+#ifdef _OPENMP
+    {
+        const int64_t want = (n * (int64_t)d) >> 18;
+        const int maxt = omp_get_max_threads();
+        nt_step = want < 1 ? 1 : (want > maxt ? maxt : (int)want);
+    }
+#endif
     for (int64_t step = 0; step < n - 1; ++step) {
         int64_t best_v = -1;
         double best_w = INFINITY;
         int64_t best_lo = INT64_MAX, best_hi = INT64_MAX;
-#pragma omp parallel
+#pragma omp parallel num_threads(nt_step)
         {
             int nt = 1, tid = 0;
 #ifdef _OPENMP

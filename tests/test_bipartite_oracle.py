@@ -139,4 +139,5 @@ def test_pins_catch_bipartite_mutant(tmp_path, name):
             fn(mod)
         except Exception:
             caught.append(cname)
+            break  # one catching pin is enough
     assert caught, "no pin catches the planted mistake " + name

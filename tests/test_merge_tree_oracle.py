@@ -89,4 +89,5 @@ def test_pins_catch_merge_tree_mutant(tmp_path, name):
             fn(mod)
         except Exception:
             caught.append(cname)
+            break  # one catching pin is enough
     assert caught, "no pin catches the planted mistake " + name

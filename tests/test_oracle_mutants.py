@@ -59,7 +59,8 @@ def test_pins_catch_mutant(tmp_path, name):
             fn(mod)
         except Exception:
             caught.append(cname)
-    for kind in pins.KINDS:
+            break  # one catching pin is enough
+    for kind in pins.KINDS if not caught else ():
         try:
             pins.check_prim_equals_kruskal_exactly(mod, kind)
         except Exception:
