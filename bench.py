@@ -227,7 +227,7 @@ def main():
                     help="for counter runs: one plain copy of COPY_BYTES (calibration) and one pass of the path")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 

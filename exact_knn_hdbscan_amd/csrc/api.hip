@@ -112,11 +112,12 @@ constexpr int64_t kCUs = 256;             // MI355X compute units (fixed, so tha
 constexpr int64_t kLdsPerCu = 160 * 1024;
 constexpr int64_t kWarmupWork = 12000;    // warm-up of fresh lists, in tiles x k-steps (measured)
 
-// kNN workgroups resident per CU: two unless the double-buffered LDS tile, the
-// three-slot norm ring and the lists need more than half
-int64_t knn_groups_per_cu(int K, int QM) {
+// kNN workgroups resident per CU: two (the registers allow two waves per SIMD)
+// unless the double-buffered LDS tile and the three-slot norm ring need more
+// than half of the LDS (the lists live in registers)
+int64_t knn_groups_per_cu(int, int QM) {
     const int64_t tr = tile_rows(QM), rs = 4 * QM + 4;
-    const int64_t lds = 2 * tr * rs * 4 + 3 * tr * 4 + (int64_t)knn_col_blocks(K, QM) * K * kThreads * 8;
+    const int64_t lds = 2 * tr * rs * 4 + 3 * tr * 4;
     return 2 * lds <= kLdsPerCu ? 2 : 1;
 }
 

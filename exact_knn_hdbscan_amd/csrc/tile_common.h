@@ -382,11 +382,10 @@ __device__ __forceinline__ float group_min_nonneg(float v) { return __uint_as_fl
 __device__ __forceinline__ float group_max_nonneg(float v) { return __uint_as_float(group_max_u32(__float_as_uint(v))); }
 
 // ---------------------------------------------------------------- kNN epilogue
-// Each lane keeps CB lists (one per query column it owns) in a lane-private
-// region of LDS; only the last entry's D2 stays in a register.  Per tile every
-// D2 is computed and tested against an admission threshold in straight-line
-// code; a lane that has a candidate loads the list, inserts its candidates in
-// ascending row order (recomputing the same D2) and stores it back.
+// Each lane keeps CB lists (one per query column it owns) in registers.  Per
+// tile every D2 is computed and tested against an admission threshold in
+// straight-line code; a lane that has a candidate inserts its candidates in
+// ascending row order (recomputing the same D2).
 //
 // The four lanes of a query column see disjoint rows and keep separate lists
 // that are merged at the end.  Any K real candidates bound the query's final
@@ -402,7 +401,7 @@ __device__ __forceinline__ float group_max_nonneg(float v) { return __uint_as_fl
 template <int K, int CB, int RB> struct EpiKnn {
     static constexpr int J = (K + 3) / 4 - 1;
     static constexpr bool kSecond = 4 * (J + 1) == K + 1 && J >= 1;
-    Entry *lists; // LDS, [CB][K][kThreads]
+    TopK<K> lst[CB]; // this lane's lists, in registers
     float thr[CB]; // this lane's last entry
     float qj[CB];  // this lane's J-th entry
     float qj1[CB]; // this lane's (J - 1)-th entry (used when kSecond)
@@ -412,15 +411,11 @@ template <int K, int CB, int RB> struct EpiKnn {
     bool dirty;     // this lane changed a list since adm was last formed
     int32_t qrow[CB];
     int g;
-    int tid;
-
-    __device__ __forceinline__ Entry &at(int cb, int t) { return lists[(cb * K + t) * kThreads + tid]; }
 
     __device__ __forceinline__ void init() {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-#pragma unroll
-            for (int t = 0; t < K; ++t) at(cb, t) = Entry{INFINITY, 0x7fffffff};
+            lst[cb].clear();
             thr[cb] = INFINITY;
             qj[cb] = INFINITY;
             qj1[cb] = INFINITY;
@@ -429,18 +424,8 @@ template <int K, int CB, int RB> struct EpiKnn {
         }
         dirty = false;
     }
-    __device__ __forceinline__ void load(int cb, TopK<K> &L) {
-#pragma unroll
-        for (int t = 0; t < K; ++t) {
-            const Entry e = at(cb, t);
-            L.d[t] = e.d2;
-            L.i[t] = e.idx;
-        }
-    }
-    __device__ __forceinline__ void store(int cb, const TopK<K> &L) {
-#pragma unroll
-        for (int t = 0; t < K; ++t) at(cb, t) = Entry{L.d[t], L.i[t]};
-    }
+    __device__ __forceinline__ void load(int cb, TopK<K> &L) { L = lst[cb]; }
+    __device__ __forceinline__ void store(int cb, const TopK<K> &L) { lst[cb] = L; }
 
     __device__ __forceinline__ float dist2(const f4 (&acc)[RB][CB], const f4 (&nb4)[RB], int rb, int r, int cb) const {
         return fmaf(-2.f, acc[rb][cb][r], nq[cb] + nb4[rb][r]);
@@ -558,10 +543,7 @@ void knn_tile_kernel(KnnArgs a) {
     const int split = blockIdx.y;
     const int64_t qbase = (int64_t)blockIdx.x * QT; // local row of the workgroup's first query
 
-    __shared__ Entry sm_lists[CB * K * kThreads];
     EpiKnn<K, CB, T::RB> epi;
-    epi.lists = sm_lists;
-    epi.tid = tid;
     float bq[CB][QM];
     bool qv[CB];
 #pragma unroll
