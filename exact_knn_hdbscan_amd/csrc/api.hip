@@ -110,7 +110,7 @@ constexpr int64_t kMinTilesPerSplit = 4;
 constexpr int64_t kCUs = 256;             // MI355X compute units (fixed, so that a workspace
                                           // query and the run always plan alike)
 constexpr int64_t kLdsPerCu = 160 * 1024;
-constexpr int64_t kWarmupWork = 12000;    // warm-up of fresh lists, in tiles x k-steps (measured)
+constexpr int64_t kWarmupWork = 12000;    // warm-up of fresh lists, in 32-row tiles x k-steps (measured)
 
 // kNN workgroups resident per CU: two (the registers allow two waves per SIMD)
 // unless the double-buffered LDS tile and the three-slot norm ring need more
@@ -140,7 +140,7 @@ KnnPlan plan_knn(int64_t n, int64_t m, int d, int k, int64_t max_chunk_dots) {
     // that minimises rounds x (tiles per split + that warm-up).
     const int64_t qtiles = std::max<int64_t>(1, (p.rows + p.QT - 1) / p.QT);
     const int64_t slots = kCUs * knn_groups_per_cu(p.K, p.QM);
-    const int64_t warm = kWarmupWork / (4 * p.chunks);
+    const int64_t warm = kWarmupWork * 32 / (4 * p.chunks * p.TR); // measured at 32-row tiles
     const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(64, p.tiles / kMinTilesPerSplit));
     int64_t best_s = 1, best = -1;
     for (int64_t s = 1; s <= smax; ++s) {
