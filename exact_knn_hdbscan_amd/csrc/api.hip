@@ -112,13 +112,15 @@ constexpr int64_t kCUs = 256;             // MI355X compute units (fixed, so tha
 constexpr int64_t kLdsPerCu = 160 * 1024;
 constexpr int64_t kWarmupWork = 12000;    // warm-up of fresh lists, in 32-row tiles x k-steps (measured)
 
-// kNN workgroups resident per CU: two (the registers allow two waves per SIMD)
-// unless the double-buffered LDS tile and the three-slot norm ring need more
-// than half of the LDS (the lists live in registers)
-int64_t knn_groups_per_cu(int, int QM) {
+// kNN workgroups resident per CU: one per wave per SIMD that the registers
+// allow (four-wave workgroups), fewer if the double-buffered LDS tile and the
+// three-slot norm ring do not fit that many times (the lists live in registers)
+int64_t knn_groups_per_cu(int K, int QM) {
     const int64_t tr = tile_rows(QM), rs = 4 * QM + 4;
     const int64_t lds = 2 * tr * rs * 4 + 3 * tr * 4;
-    return 2 * lds <= kLdsPerCu ? 2 : 1;
+    const int64_t by_lds = kLdsPerCu / lds;
+    const int64_t want = knn_waves_per_simd(K, QM);
+    return by_lds < want ? (by_lds < 1 ? 1 : by_lds) : want;
 }
 
 KnnPlan plan_knn(int64_t n, int64_t m, int d, int k, int64_t max_chunk_dots) {

@@ -22,8 +22,7 @@ constexpr int kThreads = kWaves * 64; // 256 threads
 // QM = k-steps held in registers (4 features each): d <= 4 * QM.
 // CB = 16-column query blocks per wave; TR = database rows per LDS tile.
 template <int QM> struct TileGeo;
-// d <= 64: 64-row tiles (128 MFMAs per wave between barriers)
-template <> struct TileGeo<16> { static constexpr int TR = 64; };
+template <> struct TileGeo<16> { static constexpr int TR = 32; };
 template <> struct TileGeo<32> { static constexpr int TR = 32; };
 // d > 128: 16-row tiles keep the prefetch registers and the LDS tile small
 // enough for two workgroups per CU
@@ -38,7 +37,10 @@ inline int pick_k(int k) {
     return -1;
 }
 inline int pick_qm(int d) { return d <= 64 ? 16 : (d <= 128 ? 32 : 64); }
-inline int tile_rows(int qm) { return qm == 64 ? 16 : qm == 16 ? 64 : 32; }
+inline int tile_rows(int qm) { return qm == 64 ? 16 : 32; }
+// kNN tile kernel occupancy: three waves per SIMD for d <= 64 and K <= 16
+// (156 VGPRs at K = 11, no spills), two otherwise
+constexpr int knn_waves_per_simd(int K, int QM) { return QM == 16 && K <= 16 ? 3 : 2; }
 // 16-column query blocks per wave: two when the registers allow it
 constexpr int knn_col_blocks(int K, int QM) { return (K > 11 || QM > 16) ? 1 : 2; }
 constexpr int scan_col_blocks(int QM) { return QM > 16 ? 1 : 2; }

@@ -44,16 +44,14 @@ template <int QM> struct Tile {
 };
 
 // Streams database tiles [t_begin, t_end) through a double-buffered LDS tile
-// (row-major: [row][feature]) and hands each tile's accumulator blocks to the
-// epilogue.  One trip per tile, one barrier: the global loads of tile t + 1
-// are in flight while the MFMAs of tile t run into one accumulator set and
-// the epilogue consumes tile t - 1 from the other.  An epilogue with a split
-// form (kSplitEpi) does its bound update before the MFMAs and its per-element
-// fast test right after them, in the same basic block, so the scheduler can
-// interleave that test with the MFMAs; its list insertions come last.  Slots:
-// tile t's norms are in slot (t - t_begin) mod 3.  Per-row norms (and, with
-// PAYLOAD, component labels and core distances) live in a three-slot ring so
-// that tile t - 1's stay valid while tile t + 1's are stored.  FULL: the
+// (row-major: [row][feature]) and hands each tile's accumulator blocks to
+// epi.tile().  One trip and one barrier per tile: the global loads of tile
+// t + 1 are in flight while the MFMAs and the epilogue of tile t run.  One
+// accumulator set and one prefetch set keep the registers low enough for
+// three waves per SIMD (d <= 64), so that while one wave waits at its barrier
+// or works through its epilogue, the others keep the MFMA pipe busy.  Per-row
+// norms (and, with PAYLOAD, component labels and core distances) live in a
+// three-slot ring; tile t's are in slot (t - t_begin) mod 3.  FULL: the
 // dimension fills all QM k-steps, so the k-loop has no runtime guard.
 template <int QM, int CB, bool PAYLOAD, bool FULL, class Epi>
 __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t ldb, int64_t m,
@@ -166,7 +164,7 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
         // this lane's feature block of each row it reads
         const float *tl = sm_tile[buf] + li * T::RS + g * qs;
         if (FULL) {
-            constexpr int PRE = QM < 8 ? QM : 8; // k-steps whose A operands are read ahead
+            constexpr int PRE = QM < 4 ? QM : 4; // k-steps whose A operands are read ahead
 #pragma unroll
             for (int s0 = 0; s0 < QM; s0 += PRE) {
                 f4 a4[PRE / 4][T::RB];
@@ -208,50 +206,21 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
     };
 
     if (t_begin >= t_end) return;
-    constexpr bool kSplit = Epi::kSplitEpi;
     Pref P;
     load(P, t_begin);
     store(P, 0, 0);
     __syncthreads();
-    if (t_begin + 1 < t_end) load(P, t_begin + 1);
-    f4 accA[T::RB][CB], accB[T::RB][CB];
-    mma(0, accA);
-    if (t_begin + 1 < t_end) store(P, 1, 1);
-    __syncthreads();
-    int buf = 1, sl = 1; // tile t's buffer and norm slot
-    auto next3 = [](int x) { return x == 2 ? 0 : x + 1; };
-    // one trip: the MFMAs of tile t into `cur`, the epilogue of tile t - 1 from `prev`
-    auto trip = [&](int64_t t, f4 (&cur)[T::RB][CB], f4 (&prev)[T::RB][CB]) {
-        const int slp = sl == 0 ? 2 : sl - 1, sln = next3(sl);
+    f4 acc[T::RB][CB];
+    int buf = 0, sl = 0; // tile t's LDS buffer and norm slot
+    for (int64_t t = t_begin; t < t_end; ++t) {
+        const int sn = sl == 2 ? 0 : sl + 1;
         if (t + 1 < t_end) load(P, t + 1);
-        if constexpr (kSplit) {
-            epi.prepare();
-            f4 nb4[T::RB];
-#pragma unroll
-            for (int rb = 0; rb < T::RB; ++rb) nb4[rb] = *reinterpret_cast<const f4 *>(sm_nrm[slp] + rb * 16 + 4 * g);
-            bool hit[CB];
-            mma(buf, cur);
-            epi.fast(prev, nb4, hit);
-            epi.slow(prev, nb4, hit, (t - 1) * T::TR);
-        } else {
-            mma(buf, cur);
-            finish(prev, t - 1, slp);
-        }
-        if (t + 1 < t_end) store(P, buf ^ 1, sln);
+        mma(buf, acc);
+        finish(acc, t, sl);
+        if (t + 1 < t_end) store(P, buf ^ 1, sn);
         __syncthreads();
         buf ^= 1;
-        sl = sln;
-    };
-    int64_t t = t_begin + 1;
-    for (; t + 1 < t_end; t += 2) {
-        trip(t, accB, accA);
-        trip(t + 1, accA, accB);
-    }
-    if (t < t_end) { // one tile left: its MFMAs with tile t - 1's epilogue, then its own epilogue
-        trip(t, accB, accA);
-        finish(accB, t, sl == 0 ? 2 : sl - 1);
-    } else {
-        finish(accA, t - 1, sl == 0 ? 2 : sl - 1);
+        sl = sn;
     }
 }
 
@@ -441,10 +410,9 @@ template <int K, int CB, int RB> struct EpiKnn {
     // decides whether a lane looks at its candidates: those are then taken with
     // the exact D2 and the exact bound, so results do not depend on the margin.
     //
-    // Split form: prepare() re-forms the bound (only when a list of the wave
-    // changed: a wave-uniform test), fast() is the branch-free test, slow()
-    // inserts the candidates of the columns that passed; tile() runs all three.
-    static constexpr bool kSplitEpi = true;
+    // prepare() re-forms the bound (only when a list of the wave changed: a
+    // wave-uniform test), fast() is the branch-free test, slow() inserts the
+    // candidates of the columns that passed; tile() runs the three.
     __device__ __forceinline__ void prepare() {
         constexpr float kWiden = 1.0f / 1048576.0f;
         if (__builtin_amdgcn_ballot_w64(dirty)) {
@@ -534,7 +502,7 @@ __device__ __forceinline__ void write_list(const KnnArgs &a, const TopK<K> &L, i
 }
 
 template <int K, int QM, bool FULL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(knn_waves_per_simd(K, QM), knn_waves_per_simd(K, QM))))
 void knn_tile_kernel(KnnArgs a) {
     constexpr int CB = knn_col_blocks(K, QM);
     using T = Tile<QM>;

@@ -121,7 +121,6 @@ __device__ __forceinline__ float scan_threshold(float w) {
 }
 
 template <int CB, int RB> struct EpiScan {
-    static constexpr bool kSplitEpi = false; // one tile() call per tile
     uint64_t best[CB];
     uint64_t init[CB];
     float thr[CB];
