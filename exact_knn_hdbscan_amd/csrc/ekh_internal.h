@@ -41,6 +41,8 @@ inline int tile_rows(int qm) { return qm == 64 ? 16 : 32; }
 // kNN tile kernel occupancy: three waves per SIMD for d <= 64 and K <= 16
 // (156 VGPRs at K = 11, no spills), two otherwise
 constexpr int knn_waves_per_simd(int K, int QM) { return QM == 16 && K <= 16 ? 3 : 2; }
+// Boruvka scan kernel occupancy: three waves per SIMD for d <= 128, two otherwise
+constexpr int scan_waves_per_simd(int QM) { return QM <= 32 ? 3 : 2; }
 // 16-column query blocks per wave: two when the registers allow it
 constexpr int knn_col_blocks(int K, int QM) { return (K > 11 || QM > 16) ? 1 : 2; }
 constexpr int scan_col_blocks(int QM) { return QM > 16 ? 1 : 2; }

@@ -167,7 +167,8 @@ template <int CB, int RB> struct EpiScan {
 };
 
 template <int QM, bool FULL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(scan_waves_per_simd(QM), scan_waves_per_simd(QM))))
 void scan_tile_kernel(ScanArgs a) {
     constexpr int CB = scan_col_blocks(QM);
     using T = Tile<QM>;
