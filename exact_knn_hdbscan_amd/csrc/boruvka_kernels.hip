@@ -53,6 +53,32 @@ __device__ __forceinline__ void wave_count(bool pred, uint32_t *ctr) {
         atomicAdd(ctr, (uint32_t)__popcll(m));
 }
 
+// atomicMin(&base[c], v) for every lane with `active`.  Late in the run most
+// points of a wave belong to one component, so the lanes that share the
+// wave's first component combine with a wave minimum and issue one atomic; the
+// others issue their own.  The same minima land either way.
+template <class T>
+__device__ __forceinline__ void atomic_min_grouped(T *base, int32_t c, T v, bool active) {
+    const uint64_t act = __ballot(active);
+    if (!act) return;
+    const int lane = threadIdx.x & 63;
+    const int leader = __ffsll((long long)act) - 1;
+    const int32_t c0 = __shfl(c, leader);
+    const bool same = active && c == c0;
+    const uint64_t sm = __ballot(same);
+    if (__popcll(sm) > 1) {
+        T m = same ? v : ~T(0);
+        for (int o = 32; o > 0; o >>= 1) {
+            const T y = __shfl_xor(m, o);
+            m = y < m ? y : m;
+        }
+        if (lane == leader) atomicMin(&base[c0], m);
+        if (active && !same) atomicMin(&base[c], v);
+    } else if (active) {
+        atomicMin(&base[c], v);
+    }
+}
+
 // Neighbour-edge candidates ("Exact shortcuts", first item).  For point a with
 // list entries b (self included, ascending (D2, index)):
 //  - every entry in another component is a real edge W = max(core_a, core_b, D);
@@ -63,7 +89,9 @@ __device__ __forceinline__ void wave_count(bool pred, uint32_t *ctr) {
 //    index is in the list too).  Such a point is resolved without a scan.
 __global__ void bv_candidates_kernel(BvState st, int use_nb, int use_bound) {
     const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    bool res = false;
+    bool res = false, bnd = false;
+    uint32_t wb = 0;
+    int32_t cb = 0;
     if (a < st.n) {
         const int32_t ca = st.comp[a];
         const float corea = st.core[a];
@@ -85,8 +113,11 @@ __global__ void bv_candidates_kernel(BvState st, int use_nb, int use_bound) {
         res = use_nb && complete && nb != kNoEdge && (uint32_t)(nb >> 32) == __float_as_uint(corea);
         st.best[a] = nb;
         st.resolved[a] = res ? 1 : 0;
-        if (use_bound && nb != kNoEdge) atomicMin(&st.compW[ca], (uint32_t)(nb >> 32));
+        bnd = use_bound && nb != kNoEdge;
+        wb = (uint32_t)(nb >> 32);
+        cb = ca;
     }
+    atomic_min_grouped<uint32_t>(st.compW, cb, wb, bnd);
     wave_count(res, &st.ctr->n_resolved);
 }
 
@@ -130,12 +161,20 @@ hipError_t bv_select_active(const BvState &st, int use_bound, hipStream_t s) {
 // the edges that reach that minimum.
 __global__ void bv_cmin1_kernel(BvState st) {
     const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (a >= st.n) return;
-    const uint64_t k = st.best[a];
-    if (k == kNoEdge) return;
-    const uint32_t b = (uint32_t)k;
-    const uint32_t lo = (uint32_t)a < b ? (uint32_t)a : b;
-    atomicMin((unsigned long long *)&st.cmin1[st.comp[a]], (unsigned long long)((k & 0xffffffff00000000ull) | lo));
+    bool has = false;
+    unsigned long long key = 0;
+    int32_t c = 0;
+    if (a < st.n) {
+        const uint64_t k = st.best[a];
+        if (k != kNoEdge) {
+            const uint32_t b = (uint32_t)k;
+            const uint32_t lo = (uint32_t)a < b ? (uint32_t)a : b;
+            key = (unsigned long long)((k & 0xffffffff00000000ull) | lo);
+            c = st.comp[a];
+            has = true;
+        }
+    }
+    atomic_min_grouped<unsigned long long>((unsigned long long *)st.cmin1, c, key, has);
 }
 
 __global__ void bv_cmin2_kernel(BvState st) {
