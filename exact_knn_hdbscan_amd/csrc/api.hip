@@ -242,7 +242,7 @@ struct MstWs {
     float *nrm;
     int32_t *comp, *parent, *act;
     uint8_t *resolved;
-    uint64_t *best, *cmin1;
+    uint64_t *best, *cmin1, *cc;
     uint32_t *cmin2, *compW;
     int32_t *e_lo, *e_hi;
     float *e_w;
@@ -260,6 +260,7 @@ struct MstWs {
 size_t carve_mst(Carver &c, int64_t n, int d, int ms, bool with_nb, MstWs &w) {
     w.nrm = c.take<float>(n);
     w.comp = c.take<int32_t>(n);
+    w.cc = c.take<uint64_t>(n);
     w.parent = c.take<int32_t>(n);
     w.act = c.take<int32_t>(n);
     w.resolved = c.take<uint8_t>(n);
@@ -425,6 +426,7 @@ int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const flo
     st.nbr_d2 = nbr_d2;
     st.core = core;
     st.comp = w.comp;
+    st.cc = w.cc;
     st.parent = w.parent;
     st.act = w.act;
     st.resolved = w.resolved;

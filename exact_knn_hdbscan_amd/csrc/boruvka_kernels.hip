@@ -19,6 +19,7 @@ __global__ void bv_init_kernel(BvState st) {
     const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (a >= st.n) return;
     st.comp[a] = (int32_t)a;
+    st.cc[a] = ((uint64_t)(uint32_t)a << 32) | __float_as_uint(st.core[a]);
     st.parent[a] = (int32_t)a;
     st.cmin1[a] = kNoEdge;
     st.cmin2[a] = 0xffffffffu;
@@ -102,9 +103,10 @@ __global__ void bv_candidates_kernel(BvState st, int use_nb, int use_bound) {
             const float d2 = st.nbr_d2[a * st.K + t];
             last_d2 = d2;
             if (b < 0 || b >= st.n) continue; // malformed caller list: entry ignored
-            if (st.comp[b] != ca) {
+            const uint64_t x = st.cc[b];        // comp << 32 | core bits of b
+            if ((int32_t)(x >> 32) != ca) {
                 const float D = sqrt_rn(d2 > 0.f ? d2 : 0.f);
-                const float W = fmaxf(fmaxf(corea, st.core[b]), D);
+                const float W = fmaxf(fmaxf(corea, __uint_as_float((uint32_t)x)), D);
                 const uint64_t key = ((uint64_t)__float_as_uint(W) << 32) | (uint32_t)b;
                 nb = key < nb ? key : nb;
             }
@@ -253,6 +255,7 @@ __global__ void bv_relabel_kernel(BvState st) {
         const int32_t r = st.parent[c];
         root = (c == (int32_t)a) && (r == (int32_t)a);
         st.comp[a] = r;
+        st.cc[a] = ((uint64_t)(uint32_t)r << 32) | __float_as_uint(st.core[a]);
         st.cmin1[a] = kNoEdge;
         st.cmin2[a] = 0xffffffffu;
         st.compW[a] = kInfBits;

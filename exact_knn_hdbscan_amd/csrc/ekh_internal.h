@@ -146,6 +146,7 @@ struct BvState {
     const float *nbr_d2;
     const float *core;
     int32_t *comp;
+    uint64_t *cc;      // per point (comp << 32 | core bits): one gather per list entry
     int32_t *parent;
     int32_t *act;
     uint8_t *resolved;
