@@ -89,6 +89,7 @@ def library() -> ctypes.CDLL:
             lib.ekh_knn_workspace_bytes.argtypes = [_i64, _i64, _i32, _i32, _i64]
             lib.ekh_knn_workspace_bytes.restype = _sz
             lib.ekh_knn.argtypes = [_p, _i64, _i64, _p, _i64, _i64, _i32, _i32, _p, _p, _i64, _p, _sz, _p]
+            lib.ekh_knn_plan.argtypes = [_i64, _i64, _i32, _i32, _i64, ctypes.POINTER(_i64)]
             lib.ekh_core_workspace_bytes.argtypes = [_i64, _i32, _i32]
             lib.ekh_core_workspace_bytes.restype = _sz
             lib.ekh_core_distances.argtypes = [_p, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _sz, _p]
@@ -143,6 +144,14 @@ def _workspace(nbytes: int, dev):
 
 def knn_workspace_bytes(n: int, m: int, d: int, k: int, max_chunk_dots: int = 0) -> int:
     return int(library().ekh_knn_workspace_bytes(n, m, d, k, max_chunk_dots))
+
+
+def knn_plan(n: int, m: int, d: int, k: int, max_chunk_dots: int = 0) -> dict:
+    """Launch layout of the kNN tile kernel for these sizes (host only)."""
+    out = (_i64 * 7)()
+    _check(library().ekh_knn_plan(n, m, d, k, max_chunk_dots, out))
+    keys = ("chunk_rows", "tile_rows", "body_tiles", "splits", "slots", "last_body_tiles", "last_splits")
+    return dict(zip(keys, (int(v) for v in out)))
 
 
 def core_workspace_bytes(n: int, d: int, min_samples: int) -> int:

@@ -100,8 +100,17 @@ struct TimedLaunch {
 struct KnnPlan {
     int K, QM, TR, QT, chunks;
     int64_t rows;   // rows per chunk
-    int splits;
     int64_t tiles;  // database tiles
+    int64_t slots;  // workgroups resident at once
+    int64_t warm;   // warm-up of fresh lists, in tiles
+    int64_t part_entries; // split scratch (entries) of the largest chunk
+};
+
+// How one chunk of query tiles is laid out on the grid of one launch: the
+// first body_q tiles whole, the rest in `splits` database splits each.
+struct ChunkPlan {
+    int64_t body_q;
+    int splits;
 };
 
 constexpr int64_t kMaxLd = int64_t(1) << 25;
@@ -123,6 +132,51 @@ int64_t knn_groups_per_cu(int K, int QM) {
     return by_lds < want ? (by_lds < 1 ? 1 : by_lds) : want;
 }
 
+// Cost of running q query tiles in s database splits: the launch runs in
+// rounds of resident workgroups, and every split starts its lists empty (the
+// first tiles insert nearly every row, a cost of about kWarmupWork / k-steps
+// tiles), so rounds x (tiles per split + that warm-up).
+int64_t split_cost(const KnnPlan &p, int64_t q, int64_t s) {
+    return (q * s + p.slots - 1) / p.slots * ((p.tiles + s - 1) / s + p.warm);
+}
+
+int best_splits(const KnnPlan &p, int64_t q, int64_t *cost) {
+    const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(64, p.tiles / kMinTilesPerSplit));
+    int64_t best_s = 1, best = -1;
+    for (int64_t s = 1; s <= smax; ++s) {
+        const int64_t c = split_cost(p, q, s);
+        if (best < 0 || c < best) {
+            best = c;
+            best_s = s;
+        }
+    }
+    *cost = best;
+    return (int)best_s;
+}
+
+// Layout of a chunk of `rows` query rows.  Either every tile in the same number
+// of splits, or (when cheaper) the whole rounds of tiles unsplit and only the
+// tiles left over for a last, partly filled round split finely enough to fill
+// it: a ragged last round otherwise leaves most of the chip idle while a few
+// workgroups stream the whole database.
+ChunkPlan plan_chunk(const KnnPlan &p, int64_t rows) {
+    const int64_t q = std::max<int64_t>(1, (rows + p.QT - 1) / p.QT);
+    int64_t cu;
+    ChunkPlan c{0, best_splits(p, q, &cu)};
+    const int64_t body = q / p.slots * p.slots;
+    if (body > 0 && body < q) {
+        int64_t ct;
+        const int st = best_splits(p, q - body, &ct);
+        if (body / p.slots * (p.tiles + p.warm) + ct < cu) c = ChunkPlan{body, st};
+    }
+    return c;
+}
+
+int64_t chunk_part_entries(const KnnPlan &p, int64_t rows) {
+    const ChunkPlan c = plan_chunk(p, rows);
+    return c.splits > 1 ? (rows - c.body_q * p.QT) * c.splits * p.K : 0;
+}
+
 KnnPlan plan_knn(int64_t n, int64_t m, int d, int k, int64_t max_chunk_dots) {
     KnnPlan p{};
     p.K = pick_k(k);
@@ -136,24 +190,10 @@ KnnPlan plan_knn(int64_t n, int64_t m, int d, int k, int64_t max_chunk_dots) {
         p.rows = std::min<int64_t>(n, std::max<int64_t>(r, p.QT));
     }
     p.tiles = (m + p.TR - 1) / p.TR;
-    // Database splits: the launch runs in rounds of resident workgroups, and
-    // every split starts its lists empty (the first tiles insert nearly every
-    // row, a cost of about kWarmupWork / k-steps tiles).  Take the split count
-    // that minimises rounds x (tiles per split + that warm-up).
-    const int64_t qtiles = std::max<int64_t>(1, (p.rows + p.QT - 1) / p.QT);
-    const int64_t slots = kCUs * knn_groups_per_cu(p.K, p.QM);
-    const int64_t warm = kWarmupWork * 32 / (4 * p.chunks * p.TR); // measured at 32-row tiles
-    const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(64, p.tiles / kMinTilesPerSplit));
-    int64_t best_s = 1, best = -1;
-    for (int64_t s = 1; s <= smax; ++s) {
-        const int64_t rounds = (qtiles * s + slots - 1) / slots;
-        const int64_t cost = rounds * ((p.tiles + s - 1) / s + warm);
-        if (best < 0 || cost < best) {
-            best = cost;
-            best_s = s;
-        }
-    }
-    p.splits = (int)best_s;
+    p.slots = kCUs * knn_groups_per_cu(p.K, p.QM);
+    p.warm = kWarmupWork * 32 / (4 * p.chunks * p.TR); // measured at 32-row tiles
+    p.part_entries = chunk_part_entries(p, p.rows);
+    if (n % p.rows) p.part_entries = std::max(p.part_entries, chunk_part_entries(p, n % p.rows));
     return p;
 }
 
@@ -164,7 +204,7 @@ size_t knn_ws(const KnnPlan &p, int64_t n, int64_t m, bool self, Carver &c, floa
               int32_t **idx_scratch = nullptr, int k = 0, float **bt = nullptr, int d = 0) {
     *nx = c.take<float>(n);
     *ny = self ? *nx : c.take<float>(m);
-    *part = p.splits > 1 ? c.take<Entry>((size_t)p.rows * p.splits * p.K) : nullptr;
+    *part = p.part_entries ? c.take<Entry>((size_t)p.part_entries) : nullptr;
     if (idx_scratch) *idx_scratch = c.take<int32_t>((size_t)n * k);
     if (bt) *bt = c.take<float>((size_t)m * padded_dim(d));
     return c.used;
@@ -201,7 +241,9 @@ int run_knn(const KnnPlan &p, const float *X, int64_t ldx, int64_t n, const floa
         a.d = d;
         a.chunks = p.chunks;
         a.self = self ? 1 : 0;
-        a.splits = p.splits;
+        const ChunkPlan cp = plan_chunk(p, a.nq);
+        a.body_q = cp.body_q;
+        a.splits = cp.splits;
         a.tiles = p.tiles;
         a.k_out = k_out;
         a.min_samples = min_samples;
@@ -209,12 +251,14 @@ int run_knn(const KnnPlan &p, const float *X, int64_t ldx, int64_t n, const floa
         a.out_idx = out_idx;
         a.out_dist = out_dist;
         a.out_core = out_core;
-        a.out_mode = p.splits > 1 ? kOutPartial : out_mode;
+        a.out_mode = out_mode;
         TimedLaunch tl(0, 2.0 * d * (double)a.nq * (double)m, s);
         EKH_HIP(launch_knn_tile(p.K, p.QM, a, s));
         tl.done();
-        if (p.splits > 1) {
-            a.out_mode = out_mode;
+        if (cp.splits > 1) {
+            // the split tiles' rows only
+            a.q0 += cp.body_q * p.QT;
+            a.nq -= cp.body_q * p.QT;
             EKH_HIP(launch_knn_merge(p.K, a, s));
         }
     }
@@ -318,6 +362,24 @@ size_t ekh_knn_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t k, int64
     int32_t *idx;
     float *bt;
     return knn_ws(p, n, m, false, c, &nx, &ny, &part, &idx, k, &bt, d);
+}
+
+int ekh_knn_plan(int64_t n, int64_t m, int32_t d, int32_t k, int64_t max_chunk_dots, int64_t out[7]) {
+    if (!out) return fail(EKH_EINVAL, "out is NULL");
+    if (n < 1 || n > INT32_MAX || m < 1 || m > INT32_MAX || d < 1 || d > EKH_MAX_DIM || k < 1 || k > EKH_MAX_K ||
+        k > m)
+        return fail(EKH_EINVAL, "sizes out of range (n %lld, m %lld, d %d, k %d)", (long long)n, (long long)m, d, k);
+    const KnnPlan p = plan_knn(n, m, d, k, max_chunk_dots);
+    const ChunkPlan first = plan_chunk(p, std::min(p.rows, n));
+    const ChunkPlan last = plan_chunk(p, n % p.rows ? n % p.rows : p.rows);
+    out[0] = p.rows;
+    out[1] = p.QT;
+    out[2] = first.body_q;
+    out[3] = first.splits;
+    out[4] = p.slots;
+    out[5] = last.body_q;
+    out[6] = last.splits;
+    return EKH_OK;
 }
 
 int ekh_knn(const float *X, int64_t ldx, int64_t n, const float *Y, int64_t ldy, int64_t m, int32_t d, int32_t k,

@@ -68,7 +68,6 @@ struct __align__(8) Entry {
 
 // ---- kNN -----------------------------------------------------------------
 enum KnnOut : int {
-    kOutPartial = 0, // write the K-list to part[split][row][K]
     kOutKnn = 1,     // final: out_idx / out_dist, first k entries
     kOutCore = 2,    // final: core = sqrt(d2[ms-1]); optional nbr lists (K = ms + 1)
 };
@@ -86,12 +85,13 @@ struct KnnArgs {
     int d;
     int chunks;       // feature_chunks(d)
     int self;         // Q == B: the pair (i, i) is forced to D2 = 0
-    int splits;       // database splits (grid.y)
+    int64_t body_q;   // leading query tiles run whole (one workgroup, final lists)
+    int splits;       // database splits of every later query tile
     int64_t tiles;    // ceil(m / TR)
-    int out_mode;
+    int out_mode;     // final form; split tiles write part[split][row - tail start][K]
     int k_out;        // entries written per row (k, or ms + 1 for core)
     int min_samples;  // core mode
-    Entry *part;      // partial lists [splits][nq][K]
+    Entry *part;      // partial lists [splits][split-tile rows][K]
     int32_t *out_idx; // [n, k_out] absolute rows
     float *out_dist;  // [n, k_out] (kOutKnn) or d2 lists (kOutCore)
     float *out_core;  // [n]

@@ -13,8 +13,10 @@ namespace {
 template <int K, int QM, bool FULL> hipError_t knn_tile_launch(const KnnArgs &a, hipStream_t s) {
     constexpr int CB = knn_col_blocks(K, QM);
     constexpr int QT = kWaves * 16 * CB;
-    const dim3 grid((unsigned)((a.nq + QT - 1) / QT), (unsigned)a.splits);
-    hipLaunchKernelGGL((knn_tile_kernel<K, QM, FULL>), grid, dim3(kThreads), 0, s, a);
+    const int64_t tail_q = (a.nq - a.body_q * QT + QT - 1) / QT;
+    const int64_t groups = a.body_q + tail_q * a.splits;
+    if (a.body_q < 0 || tail_q < 0 || a.splits < 1 || groups > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((knn_tile_kernel<K, QM, FULL>), dim3((unsigned)groups), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 template <int K, int QM> hipError_t knn_tile_full(const KnnArgs &a, hipStream_t s) {

@@ -472,11 +472,11 @@ template <int K, int CB, int RB> struct EpiKnn {
     }
 };
 
-// Writes a finished list for absolute row q.
+// Writes a finished list for absolute row q: to the split scratch at dst when
+// it is one split's partial list, else in the final form a.out_mode names.
 template <int K>
-__device__ __forceinline__ void write_list(const KnnArgs &a, const TopK<K> &L, int64_t q, int split) {
-    if (a.out_mode == kOutPartial) {
-        Entry *dst = a.part + ((int64_t)split * a.nq + (q - a.q0)) * K;
+__device__ __forceinline__ void write_list(const KnnArgs &a, const TopK<K> &L, int64_t q, Entry *dst) {
+    if (dst) {
 #pragma unroll
         for (int t = 0; t < K; ++t) dst[t] = Entry{L.d[t], L.i[t]};
     } else if (a.out_mode == kOutKnn) {
@@ -508,8 +508,16 @@ void knn_tile_kernel(KnnArgs a) {
     using T = Tile<QM>;
     constexpr int QT = kWaves * 16 * CB;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, li = lane & 15;
-    const int split = blockIdx.y;
-    const int64_t qbase = (int64_t)blockIdx.x * QT; // local row of the workgroup's first query
+    // one-dimensional grid: the first body_q query tiles each take the whole
+    // database in one workgroup, then every remaining query tile takes one
+    // workgroup per database split (split-major order)
+    const int64_t tail0 = a.body_q * QT;              // local row of the first split tile
+    const int64_t tail_q = (a.nq - tail0 + QT - 1) / QT;
+    const bool body = (int64_t)blockIdx.x < a.body_q;
+    const int64_t h = body ? 0 : (int64_t)blockIdx.x - a.body_q;
+    const int split = body ? 0 : (int)(h / tail_q);
+    const int nsplit = body ? 1 : a.splits;
+    const int64_t qbase = body ? (int64_t)blockIdx.x * QT : tail0 + (h % tail_q) * QT; // local row of the first query
 
     EpiKnn<K, CB, T::RB> epi;
     float bq[CB][QM];
@@ -526,7 +534,7 @@ void knn_tile_kernel(KnnArgs a) {
     epi.init();
     epi.g = g;
 
-    const int64_t tb = a.tiles * split / a.splits, te = a.tiles * (split + 1) / a.splits;
+    const int64_t tb = a.tiles * split / nsplit, te = a.tiles * (split + 1) / nsplit;
     run_tiles<QM, CB, false, FULL>(a.B, a.ldb, a.m, a.nrm_b, nullptr, nullptr, a.d, a.chunks, tb, te, bq, epi);
 
     // merge the four lane groups that share each query column
@@ -536,11 +544,14 @@ void knn_tile_kernel(KnnArgs a) {
         epi.load(cb, L);
         L.merge_xor(16);
         L.merge_xor(32);
-        if (g == 0 && qv[cb]) write_list<K>(a, L, epi.qrow[cb], split);
+        Entry *dst = nullptr;
+        if (nsplit > 1) dst = a.part + ((int64_t)split * (a.nq - tail0) + (epi.qrow[cb] - a.q0 - tail0)) * K;
+        if (g == 0 && qv[cb]) write_list<K>(a, L, epi.qrow[cb], dst);
     }
 }
 
-// One thread per row: merges the split lists in split order.
+// One thread per row of the split tiles (a.q0, a.nq name them): merges the split
+// lists in split order.
 template <int K> __global__ void knn_merge_kernel(KnnArgs a) {
     const int64_t ql = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (ql >= a.nq) return;
@@ -554,7 +565,7 @@ template <int K> __global__ void knn_merge_kernel(KnnArgs a) {
             L.push_any(e.d2, e.idx);
         }
     }
-    write_list<K>(a, L, a.q0 + ql, 0); // a.out_mode is the final mode here
+    write_list<K>(a, L, a.q0 + ql, nullptr);
 }
 
 // Reported kNN distances: the selected neighbours' D2 recomputed by direct

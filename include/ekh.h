@@ -97,6 +97,22 @@ size_t ekh_knn_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t k, int64
 int ekh_knn(const float *X, int64_t ldx, int64_t n, const float *Y, int64_t ldy, int64_t m, int32_t d, int32_t k,
             int32_t *out_idx, float *out_dist, int64_t max_chunk_dots, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Launch layout the kNN tile kernel takes for these sizes (host only, no GPU
+ * call; ekh_knn, ekh_core_distances and ekh_mst_boruvka plan through the same
+ * function, the last two with m = n and max_chunk_dots = 0).  The query rows go
+ * in chunks; each chunk is one launch whose query tiles (64 or 128 rows) either
+ * all read the database in the same number of splits, or (when a last round of
+ * resident workgroups would be ragged) the first body tiles read the whole
+ * database and only the rest are split.  Split lists are merged by one more
+ * launch; results never depend on the layout.
+ *  out[0] rows per chunk, out[1] query rows per tile, out[2] body tiles of the
+ *  first chunk, out[3] database splits of its other tiles, out[4] resident
+ *  workgroups assumed, out[5] body tiles of the last chunk, out[6] its splits.
+ * Returns EKH_OK, or EKH_EINVAL for sizes ekh_knn rejects or a NULL out.
+ */
+int ekh_knn_plan(int64_t n, int64_t m, int32_t d, int32_t k, int64_t max_chunk_dots, int64_t out[7]);
+
 /* ------------------------------------------------------------------ core distances */
 
 size_t ekh_core_workspace_bytes(int64_t n, int32_t d, int32_t min_samples);

@@ -43,9 +43,66 @@ def test_workspace_queries(lib):
     a = lib.ekh_mst_workspace_bytes(100000, 61, 10, 1)
     b = lib.ekh_mst_workspace_bytes(100000, 61, 10, 0)
     assert 0 < a < b
-    # chunking bounds the split scratch
-    assert lib.ekh_knn_workspace_bytes(200000, 20000, 200, 10, 64_000_000) < lib.ekh_knn_workspace_bytes(
-        200000, 20000, 200, 10, 0) or True
+
+
+def plan(lib, n, m, d, k, dots=0):
+    out = (ctypes.c_int64 * 7)()
+    rc = lib.ekh_knn_plan(n, m, d, k, dots, out)
+    return rc, list(out)
+
+
+def test_knn_plan_of_the_clip_and_section_workloads(lib):
+    # clips 500,000 x 61, lists of K = 11: 3,907 query tiles of 128 rows, 768
+    # workgroups resident (256 CUs x 3): five whole rounds unsplit, the 67 tiles
+    # left over in 11 database splits (737 workgroups: one more round)
+    assert plan(lib, 500000, 500000, 61, 11) == (0, [500000, 128, 3840, 11, 768, 3840, 11])
+    # clips 100,000 x 61: 782 tiles, one whole round + 14 tiles in 54 splits
+    assert plan(lib, 100000, 100000, 61, 11) == (0, [100000, 128, 768, 54, 768, 768, 54])
+    # Kilosort4 section, 50,000 queries x 5,000 (d = 102, 64-row tiles): 782 tiles
+    rc, p = plan(lib, 50000, 5000, 102, 10)
+    assert rc == 0 and p[1] == 64 and p[2] == 768 and p[3] > 1
+    # fewer tiles than one round: every tile in the same number of splits
+    rc, p = plan(lib, 5000, 50000, 102, 10)
+    assert rc == 0 and p[2] == 0 and p[3] > 1
+    # wide section in chunks of 64e6 dots: 3,200-row chunks of 50 tiles, 512
+    # resident workgroups at d = 200 (two per CU), the last chunk 1,600 rows
+    rc, p = plan(lib, 200000, 20000, 200, 10, 64_000_000)
+    assert rc == 0 and p[0] == 3200 and p[1] == 64 and p[4] == 512 and p[2] == 0 and p[5] == 0
+    assert p[6] >= p[3] > 1
+
+
+K_LIST = (2, 4, 8, 11, 16, 32)
+
+
+def test_knn_plan_invariants_and_workspace(lib):
+    rng = __import__("numpy").random.default_rng(0)
+    for _ in range(300):
+        n = int(rng.integers(1, 700_000))
+        m = int(rng.integers(1, 600_000))
+        d = int(rng.integers(1, 257))
+        k = int(rng.integers(1, min(32, m) + 1))
+        dots = int(rng.choice([0, 0, int(rng.integers(1, 10 ** 10))]))
+        rc, p = plan(lib, n, m, d, k, dots)
+        assert rc == 0
+        rows, qt, body, splits, slots, lbody, lsplits = p
+        K = next(x for x in K_LIST if x >= k)
+        tiles = -(-m // (16 if d > 128 else 32))
+        assert qt in (64, 128) and slots in (512, 768) and rows >= 1
+        assert rows == n or rows % qt == 0
+        last = n % rows or rows
+        for r, b, s in ((rows, body, splits), (last, lbody, lsplits)):
+            q = -(-r // qt)
+            assert b % slots == 0 and 0 <= b < q or b == 0
+            assert 1 <= s <= max(1, min(64, tiles // 4))
+            if b:
+                assert s > 1  # whole tiles only pay off when the rest is split
+            # the split scratch fits the workspace (8-byte entries)
+            if s > 1:
+                assert lib.ekh_knn_workspace_bytes(n, m, d, k, dots) >= 8 * K * s * (r - b * qt)
+    assert plan(lib, 0, 10, 4, 1)[0] == -1
+    assert plan(lib, 10, 10, 4, 11)[0] == -1
+    assert plan(lib, 10, 10, 257, 1)[0] == -1
+    assert lib.ekh_knn_plan(10, 10, 4, 1, 0, None) == -1
 
 
 BOGUS = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first

@@ -111,6 +111,36 @@ def test_knn_chunk_and_split_invariance():
         np.testing.assert_array_equal(host(dd), ref_d)
 
 
+@pytest.mark.parametrize("n,m,d,k,dots,layout", [
+    # 813 query tiles of 64 rows (d = 102), 768 resident: one whole round, 45 split tiles
+    (52001, 3001, 102, 10, 0, (768, 0)),
+    # 774 tiles of 128 rows (d = 61, K = 11): one whole round, 6 split tiles (ragged last tile)
+    (99001, 1500, 61, 11, 0, (768, 0)),
+    # two chunks: 99,968 rows (781 tiles: one whole round + 13 split tiles), then 20,032 rows (all split)
+    (120000, 1000, 16, 8, 100_000_000, (768, 0)),
+])
+def test_knn_whole_round_and_split_tail(n, m, d, k, dots, layout):
+    """The launch layout with whole tiles for the full rounds of resident
+    workgroups and database splits for the rest: parity with the oracle on every
+    row, and bitwise the same result as the layout with every tile split alike
+    (chunks of fewer tiles than one round)."""
+    p = ekh.knn_plan(n, m, d, k, dots)
+    assert (p["body_tiles"], p["last_body_tiles"] if dots else 0) == layout and p["splits"] > 1, p
+    X = datagen.gaussian_mixture(n, d, 20, seed=n % 97)
+    Y = datagen.gaussian_mixture(m, d, 20, seed=m % 89)
+    Xg, Yg = dev(X), dev(Y)
+    say("knn n=%d m=%d d=%d k=%d dots=%d plan %s" % (n, m, d, k, dots, p))
+    i, dd = ekh.knn(Xg, Yg, k, max_chunk_dots=dots)
+    i, dd = host(i), host(dd)
+    check_knn(X, Y, k, i, dd, rescored=True)
+    small = 256 * p["tile_rows"] * m  # 256 tiles per chunk: fewer than one round
+    q = ekh.knn_plan(n, m, d, k, small)
+    assert q["body_tiles"] == 0 and q["last_body_tiles"] == 0, q
+    i2, d2 = ekh.knn(Xg, Yg, k, max_chunk_dots=small)
+    np.testing.assert_array_equal(host(i2), i)
+    np.testing.assert_array_equal(host(d2), dd)
+
+
 def test_knn_repeatable():
     X = datagen.spike_clips(3000, 8, seed=4)
     Xg = dev(X)
