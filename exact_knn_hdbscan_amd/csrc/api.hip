@@ -114,7 +114,6 @@ struct ChunkPlan {
 };
 
 constexpr int64_t kMaxLd = int64_t(1) << 25;
-constexpr int64_t kTargetGroups = 1024; // scan launches: workgroups to aim for (256 CUs)
 constexpr int64_t kMinTilesPerSplit = 4;
 constexpr int64_t kCUs = 256;             // MI355X compute units (fixed, so that a workspace
                                           // query and the run always plan alike)
@@ -175,6 +174,27 @@ ChunkPlan plan_chunk(const KnnPlan &p, int64_t rows) {
 int64_t chunk_part_entries(const KnnPlan &p, int64_t rows) {
     const ChunkPlan c = plan_chunk(p, rows);
     return c.splits > 1 ? (rows - c.body_q * p.QT) * c.splits * p.K : 0;
+}
+
+// Boruvka scan workgroups resident per CU (the LDS tile, and a three-slot ring
+// of norms, component labels and core distances)
+int64_t scan_groups_per_cu(int QM) {
+    const int64_t tr = tile_rows(QM), rs = 4 * QM + 4;
+    const int64_t lds = 2 * tr * rs * 4 + 3 * 3 * tr * 4;
+    const int64_t by_lds = kLdsPerCu / lds;
+    const int64_t want = scan_waves_per_simd(QM);
+    return by_lds < want ? (by_lds < 1 ? 1 : by_lds) : want;
+}
+
+// Database splits of one scan launch over q query tiles: as many as fill one
+// round of resident workgroups (the scan has no list warm-up, and a second,
+// partly filled round would cost a whole round), at least kMinTilesPerSplit
+// tiles each; one split when the query tiles alone fill a round.
+int scan_splits(int QM, int64_t q, int64_t tiles) {
+    const int64_t slots = kCUs * scan_groups_per_cu(QM);
+    int64_t sp = q < slots ? slots / q : 1;
+    sp = std::min<int64_t>(sp, std::max<int64_t>(1, tiles / kMinTilesPerSplit));
+    return (int)std::max<int64_t>(1, std::min<int64_t>(sp, 65535));
 }
 
 KnnPlan plan_knn(int64_t n, int64_t m, int d, int k, int64_t max_chunk_dots) {
@@ -539,10 +559,7 @@ int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const flo
             sa.d = d;
             sa.chunks = feature_chunks(d);
             sa.tiles = tiles;
-            const int64_t ctiles = (nact + QT - 1) / QT;
-            int64_t sp = (kTargetGroups + ctiles - 1) / ctiles;
-            sp = std::min<int64_t>(sp, std::max<int64_t>(1, tiles / kMinTilesPerSplit));
-            sa.splits = (int)std::max<int64_t>(1, std::min<int64_t>(sp, 65535));
+            sa.splits = scan_splits(QM, (nact + QT - 1) / QT, tiles);
             TimedLaunch tl(1, 2.0 * d * (double)nact * (double)n, s);
             EKH_HIP(launch_scan_tile(QM, sa, s));
             tl.done();
