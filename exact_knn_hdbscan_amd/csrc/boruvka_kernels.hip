@@ -14,6 +14,12 @@ namespace ekh {
 
 static inline dim3 grid_for(int64_t n, int bs) { return dim3((unsigned)((n + bs - 1) / bs)); }
 constexpr int kBs = 256;
+// Per-point passes whose atomics go to few addresses late in the run (a
+// component's minimum, a global counter) combine them per workgroup in LDS
+// first: 1,024 points per workgroup, one global atomic per workgroup and label.
+constexpr int kBigBs = 1024;
+constexpr int kHashBits = 11;
+constexpr int kHashSlots = 1 << kHashBits; // > kBigBs: the table of one workgroup never fills
 
 __global__ void bv_init_kernel(BvState st) {
     const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -54,30 +60,60 @@ __device__ __forceinline__ void wave_count(bool pred, uint32_t *ctr) {
         atomicAdd(ctr, (uint32_t)__popcll(m));
 }
 
-// atomicMin(&base[c], v) for every lane with `active`.  Late in the run most
-// points of a wave belong to one component, so the lanes that share the
-// wave's first component combine with a wave minimum and issue one atomic; the
-// others issue their own.  The same minima land either way.
-template <class T>
-__device__ __forceinline__ void atomic_min_grouped(T *base, int32_t c, T v, bool active) {
-    const uint64_t act = __ballot(active);
-    if (!act) return;
-    const int lane = threadIdx.x & 63;
-    const int leader = __ffsll((long long)act) - 1;
-    const int32_t c0 = __shfl(c, leader);
-    const bool same = active && c == c0;
-    const uint64_t sm = __ballot(same);
-    if (__popcll(sm) > 1) {
+// Per-workgroup minima by label in LDS: open addressing with linear probing
+// (label -1 = free slot).  A workgroup inserts at most kBigBs labels into
+// kHashSlots > kBigBs slots, so a free slot always exists; the bounded probe
+// loop falls back to the global atomic all the same.
+template <class T> struct LdsMinTable {
+    int32_t key[kHashSlots];
+    T val[kHashSlots];
+
+    __device__ __forceinline__ void clear() {
+        for (int i = threadIdx.x; i < kHashSlots; i += blockDim.x) {
+            key[i] = -1;
+            val[i] = ~T(0);
+        }
+    }
+    __device__ __forceinline__ void insert(int32_t c, T v, T *gbase) {
+        uint32_t h = ((uint32_t)c * 2654435761u) >> (32 - kHashBits);
+        for (int p = 0; p < kHashSlots; ++p) {
+            const int32_t k = atomicCAS(&key[h], -1, c);
+            if (k == -1 || k == c) {
+                atomicMin(&val[h], v);
+                return;
+            }
+            h = (h + 1) & (kHashSlots - 1);
+        }
+        atomicMin(&gbase[c], v);
+    }
+    // the lanes that share the wave's first label combine with a wave minimum
+    // and insert once; the others insert their own
+    __device__ __forceinline__ void insert_grouped(int32_t c, T v, bool active, T *gbase) {
+        const uint64_t act = __ballot(active);
+        if (!act) return;
+        const int lane = threadIdx.x & 63;
+        const int leader = __ffsll((long long)act) - 1;
+        const int32_t c0 = __shfl(c, leader);
+        const bool same = active && c == c0;
         T m = same ? v : ~T(0);
         for (int o = 32; o > 0; o >>= 1) {
             const T y = __shfl_xor(m, o);
             m = y < m ? y : m;
         }
-        if (lane == leader) atomicMin(&base[c0], m);
-        if (active && !same) atomicMin(&base[c], v);
-    } else if (active) {
-        atomicMin(&base[c], v);
+        if (lane == leader) insert(c0, m, gbase);
+        if (active && !same) insert(c, v, gbase);
     }
+    // after a barrier: one global atomic per label the workgroup saw
+    __device__ __forceinline__ void flush(T *gbase) {
+        for (int i = threadIdx.x; i < kHashSlots; i += blockDim.x)
+            if (key[i] >= 0) atomicMin(&gbase[key[i]], val[i]);
+    }
+};
+
+// Adds the wave's set predicates to the workgroup's LDS counter (zeroed before a barrier).
+__device__ __forceinline__ void lds_count(bool pred, uint32_t *cnt) {
+    const uint64_t m = __ballot(pred);
+    if ((threadIdx.x & 63) == 0 && m) atomicAdd(cnt, (uint32_t)__popcll(m));
 }
 
 // Neighbour-edge candidates ("Exact shortcuts", first item).  For point a with
@@ -88,7 +124,12 @@ __device__ __forceinline__ void atomic_min_grouped(T *base, int32_t c, T v, bool
 //    cheapest edge provided the list holds every point within core_a, i.e. the
 //    last entry lies strictly farther than core_a (then the lowest qualifying
 //    index is in the list too).  Such a point is resolved without a scan.
-__global__ void bv_candidates_kernel(BvState st, int use_nb, int use_bound) {
+__global__ __launch_bounds__(kBigBs) void bv_candidates_kernel(BvState st, int use_nb, int use_bound) {
+    __shared__ LdsMinTable<uint32_t> tab;
+    __shared__ uint32_t n_res;
+    tab.clear();
+    if (threadIdx.x == 0) n_res = 0;
+    __syncthreads();
     const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     bool res = false, bnd = false;
     uint32_t wb = 0;
@@ -119,12 +160,15 @@ __global__ void bv_candidates_kernel(BvState st, int use_nb, int use_bound) {
         wb = (uint32_t)(nb >> 32);
         cb = ca;
     }
-    atomic_min_grouped<uint32_t>(st.compW, cb, wb, bnd);
-    wave_count(res, &st.ctr->n_resolved);
+    tab.insert_grouped(cb, wb, bnd, st.compW);
+    lds_count(res, &n_res);
+    __syncthreads();
+    tab.flush(st.compW);
+    if (threadIdx.x == 0 && n_res) atomicAdd(&st.ctr->n_resolved, n_res);
 }
 
 hipError_t bv_candidates(const BvState &st, int use_nb, int use_bound, hipStream_t s) {
-    hipLaunchKernelGGL(bv_candidates_kernel, grid_for(st.n, kBs), dim3(kBs), 0, s, st, use_nb, use_bound);
+    hipLaunchKernelGGL(bv_candidates_kernel, grid_for(st.n, kBigBs), dim3(kBigBs), 0, s, st, use_nb, use_bound);
     return hipGetLastError();
 }
 
@@ -133,7 +177,10 @@ hipError_t bv_candidates(const BvState &st, int use_nb, int use_bound, hipStream
 // known edge out of its component cannot supply a lighter one; on equality it
 // still could, through a lower index, so it stays active).  Compacted into
 // st.act with one atomic per wave.
-__global__ void bv_select_active_kernel(BvState st, int use_bound) {
+__global__ __launch_bounds__(kBigBs) void bv_select_active_kernel(BvState st, int use_bound) {
+    __shared__ uint32_t n_skip;
+    if (threadIdx.x == 0) n_skip = 0;
+    __syncthreads();
     const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     bool act = false, skip = false;
     if (a < st.n && !st.resolved[a]) {
@@ -150,18 +197,23 @@ __global__ void bv_select_active_kernel(BvState st, int use_bound) {
         const uint32_t below = (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
         st.act[base + below] = (int32_t)a;
     }
-    wave_count(skip, &st.ctr->n_skipped);
+    lds_count(skip, &n_skip);
+    __syncthreads();
+    if (threadIdx.x == 0 && n_skip) atomicAdd(&st.ctr->n_skipped, n_skip);
 }
 
 hipError_t bv_select_active(const BvState &st, int use_bound, hipStream_t s) {
-    hipLaunchKernelGGL(bv_select_active_kernel, grid_for(st.n, kBs), dim3(kBs), 0, s, st, use_bound);
+    hipLaunchKernelGGL(bv_select_active_kernel, grid_for(st.n, kBigBs), dim3(kBigBs), 0, s, st, use_bound);
     return hipGetLastError();
 }
 
 // Component minimum of (W, lo, hi) over the members' best edges: the 70-bit key
 // is reduced in two integer passes, (W bits << 32 | lo) first, then hi among
 // the edges that reach that minimum.
-__global__ void bv_cmin1_kernel(BvState st) {
+__global__ __launch_bounds__(kBigBs) void bv_cmin1_kernel(BvState st) {
+    __shared__ LdsMinTable<unsigned long long> tab;
+    tab.clear();
+    __syncthreads();
     const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     bool has = false;
     unsigned long long key = 0;
@@ -176,7 +228,9 @@ __global__ void bv_cmin1_kernel(BvState st) {
             has = true;
         }
     }
-    atomic_min_grouped<unsigned long long>((unsigned long long *)st.cmin1, c, key, has);
+    tab.insert_grouped(c, key, has, (unsigned long long *)st.cmin1);
+    __syncthreads();
+    tab.flush((unsigned long long *)st.cmin1);
 }
 
 __global__ void bv_cmin2_kernel(BvState st) {
@@ -191,7 +245,7 @@ __global__ void bv_cmin2_kernel(BvState st) {
 }
 
 hipError_t bv_component_min(const BvState &st, hipStream_t s) {
-    hipLaunchKernelGGL(bv_cmin1_kernel, grid_for(st.n, kBs), dim3(kBs), 0, s, st);
+    hipLaunchKernelGGL(bv_cmin1_kernel, grid_for(st.n, kBigBs), dim3(kBigBs), 0, s, st);
     hipLaunchKernelGGL(bv_cmin2_kernel, grid_for(st.n, kBs), dim3(kBs), 0, s, st);
     return hipGetLastError();
 }
