@@ -41,7 +41,8 @@ template <> hipError_t launch_knn_rescore_k<EKH_KNN_K>(const KnnArgs &a, hipStre
 
 template <> hipError_t launch_knn_merge_k<EKH_KNN_K>(const KnnArgs &a, hipStream_t s) {
     const int bs = 256;
-    hipLaunchKernelGGL(knn_merge_kernel<EKH_KNN_K>, dim3((unsigned)((a.nq + bs - 1) / bs)), dim3(bs), 0, s, a);
+    const int64_t threads = a.nq * kMergeLanes;
+    hipLaunchKernelGGL(knn_merge_kernel<EKH_KNN_K>, dim3((unsigned)((threads + bs - 1) / bs)), dim3(bs), 0, s, a);
     return hipGetLastError();
 }
 

@@ -550,22 +550,32 @@ void knn_tile_kernel(KnnArgs a) {
     }
 }
 
-// One thread per row of the split tiles (a.q0, a.nq name them): merges the split
-// lists in split order.
-template <int K> __global__ void knn_merge_kernel(KnnArgs a) {
-    const int64_t ql = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (ql >= a.nq) return;
+// Split lists of the split tiles' rows (a.q0, a.nq name them), merged by
+// kMergeLanes lanes per row: lane r takes splits r, r + kMergeLanes, ..., then
+// the lanes' lists are combined by xor merges (full (D2, index) comparisons on
+// disjoint sets, so any order gives the same list).
+constexpr int kMergeLanes = 16;
+static_assert(64 % kMergeLanes == 0, "a row's lanes lie in one wave");
+template <int K> __global__ __launch_bounds__(256) void knn_merge_kernel(KnnArgs a) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t ql = gid / kMergeLanes;
+    const int r = (int)(gid % kMergeLanes);
     TopK<K> L;
     L.clear();
-    for (int s = 0; s < a.splits; ++s) {
-        const Entry *src = a.part + ((int64_t)s * a.nq + ql) * K;
+    if (ql < a.nq) {
+        for (int s = r; s < a.splits; s += kMergeLanes) {
+            const Entry *src = a.part + ((int64_t)s * a.nq + ql) * K;
 #pragma unroll
-        for (int t = 0; t < K; ++t) {
-            const Entry e = src[t];
-            L.push_any(e.d2, e.idx);
+            for (int t = 0; t < K; ++t) {
+                const Entry e = src[t];
+                L.push_any(e.d2, e.idx);
+            }
         }
     }
-    write_list<K>(a, L, a.q0 + ql, nullptr);
+    // every lane of the wave takes part in the shuffles (rows past the end hold empty lists)
+#pragma unroll
+    for (int mask = 1; mask < kMergeLanes; mask <<= 1) L.merge_xor(mask);
+    if (ql < a.nq && r == 0) write_list<K>(a, L, a.q0 + ql, 0);
 }
 
 // Reported kNN distances: the selected neighbours' D2 recomputed by direct
