@@ -19,6 +19,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <limits>
 #include <numeric>
@@ -46,11 +47,37 @@ struct Entry {
     int64_t size;
 };
 
+// Stable LSD radix sort of (key, value) pairs by key, 11-bit digits over the
+// key bits in use.
+void radix_sort(std::vector<uint64_t> &key, std::vector<uint32_t> &val) {
+    const size_t m = key.size();
+    uint64_t any = 0;
+    for (const uint64_t k : key) any |= k;
+    int bits = 0;
+    while (bits < 64 && (any >> bits)) ++bits;
+    std::vector<uint64_t> k2(m);
+    std::vector<uint32_t> v2(m);
+    std::vector<size_t> cnt(2049);
+    for (int sh = 0; sh < bits; sh += 11) {
+        std::fill(cnt.begin(), cnt.end(), 0);
+        for (size_t i = 0; i < m; ++i) ++cnt[((key[i] >> sh) & 2047) + 1];
+        for (int b = 0; b < 2048; ++b) cnt[b + 1] += cnt[b];
+        for (size_t i = 0; i < m; ++i) {
+            const size_t d = cnt[(key[i] >> sh) & 2047]++;
+            k2[d] = key[i];
+            v2[d] = val[i];
+        }
+        key.swap(k2);
+        val.swap(v2);
+    }
+}
+
 struct Tail {
     int64_t n;
     int64_t mcs;
     // hierarchy: internal node n + k (k = 0 .. n - 2) merges left[k] and right[k] at dist[k]
-    std::vector<int64_t> left, right, size, minpt;
+    // (32-bit: node ids stay below 2n <= 2^31)
+    std::vector<int32_t> left, right, size, minpt;
     std::vector<float> dist;
     // provisional clusters (creation order), then final ids n + c
     std::vector<double> birth;
@@ -78,10 +105,10 @@ struct Tail {
         for (int64_t e = 0; e + 1 < m && sorted; ++e) sorted = !less(e + 1, e);
         if (!sorted) std::stable_sort(order.begin(), order.end(), less);
 
-        std::vector<int64_t> uf(n), ufsize(n, 1), top(n);
-        std::iota(uf.begin(), uf.end(), int64_t(0));
-        std::iota(top.begin(), top.end(), int64_t(0));
-        auto find = [&](int64_t x) {
+        std::vector<int32_t> uf(n), ufsize(n, 1), top(n);
+        std::iota(uf.begin(), uf.end(), int32_t(0));
+        std::iota(top.begin(), top.end(), int32_t(0));
+        auto find = [&](int32_t x) {
             while (uf[x] != x) {
                 uf[x] = uf[uf[x]];
                 x = uf[x];
@@ -93,12 +120,12 @@ struct Tail {
         dist.resize(m);
         size.assign(2 * n - 1, 1);
         minpt.resize(2 * n - 1);
-        std::iota(minpt.begin(), minpt.begin() + n, int64_t(0));
+        std::iota(minpt.begin(), minpt.begin() + n, int32_t(0));
         for (int64_t k = 0; k < m; ++k) {
             const int64_t e = order[k];
-            int64_t ra = find(lo[e]), rb = find(hi[e]);
+            int32_t ra = find(lo[e]), rb = find(hi[e]);
             if (ra == rb) return fail(EKH_EINVAL, "edges do not form a spanning tree (cycle at edge %lld)", (long long)e);
-            const int64_t node = n + k, a = top[ra], b = top[rb];
+            const int32_t node = (int32_t)(n + k), a = top[ra], b = top[rb];
             left[k] = a;
             right[k] = b;
             dist[k] = w[e];
@@ -218,16 +245,27 @@ extern "C" int ekh_hdbscan_tail(const int32_t *lo, const int32_t *hi, const floa
         by_id[next++] = k1;
     }
 
-    // entries in ascending (parent, child) order
+    // entries in ascending (parent, child) order: a radix sort of the packed
+    // key (parent - n) << cb | child, cb = the bits of the largest child id
+    // (children are below n + clusters < 2^31; the pairs are distinct)
     const int64_t ne = (int64_t)T.raw.size();
-    std::vector<Entry> ent(ne);
+    int cb = 0;
+    while ((int64_t(1) << cb) < n + ncl) ++cb;
+    const uint64_t cmask = (uint64_t(1) << cb) - 1;
+    std::vector<uint64_t> key(ne);
+    std::vector<uint32_t> at(ne);
     for (int64_t i = 0; i < ne; ++i) {
         const Entry &r = T.raw[i];
-        ent[i] = Entry{fid[r.parent], T.child_is_cluster[i] ? fid[r.child] : r.child, r.lambda, r.size};
+        const uint64_t child = (uint64_t)(T.child_is_cluster[i] ? fid[r.child] : r.child);
+        key[i] = (uint64_t)(fid[r.parent] - n) << cb | child;
+        at[i] = (uint32_t)i;
     }
-    std::sort(ent.begin(), ent.end(), [](const Entry &a, const Entry &b) {
-        return a.parent != b.parent ? a.parent < b.parent : a.child < b.child;
-    });
+    radix_sort(key, at);
+    std::vector<Entry> ent(ne);
+    for (int64_t j = 0; j < ne; ++j) {
+        const Entry &r = T.raw[at[j]];
+        ent[j] = Entry{n + (int64_t)(key[j] >> cb), (int64_t)(key[j] & cmask), r.lambda, r.size};
+    }
 
     // stabilities (final id order), summed over each cluster's entries in list order
     std::vector<double> birth(ncl), st(ncl, 0.0);
