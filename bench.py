@@ -318,6 +318,7 @@ def main():
                 "kernel_ms_per_step": tk["ms"] / args.steps},
         "mst": {"ms": mst_step_ms, "rounds": stats["rounds"], "scanned": stats["scanned"],
                 "resolved": stats["resolved"], "skipped": stats["skipped"],
+                "scanned_giant": stats["scanned_giant"],
                 "components": stats["n_components"],
                 "scan_kernel_ms_per_step": ts["ms"] / args.steps,
                 "scan_tflops": ts["flop"] / (ts["ms"] / 1e3) / 1e12 if ts["ms"] else None},

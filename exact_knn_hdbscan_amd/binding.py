@@ -47,6 +47,7 @@ class MstStats(ctypes.Structure):
         ("scanned", ctypes.c_int64 * MAX_ROUNDS),
         ("edges_added", ctypes.c_int64 * MAX_ROUNDS),
         ("round_ms", ctypes.c_double * MAX_ROUNDS),
+        ("scanned_giant", ctypes.c_int64 * MAX_ROUNDS),
     ]
 
     def as_dict(self) -> dict:
@@ -59,6 +60,7 @@ class MstStats(ctypes.Structure):
             "scanned": list(self.scanned[:r]),
             "edges_added": list(self.edges_added[:r]),
             "round_ms": list(self.round_ms[:r]),
+            "scanned_giant": list(self.scanned_giant[:r]),
         }
 
 

@@ -319,6 +319,7 @@ struct MstWs {
     float *nbr_d2;
     float *knn_nx;
     Entry *knn_part;
+    float *xs; // points outside the largest component, feature-major [d, <= n / 2]
 };
 
 size_t carve_mst(Carver &c, int64_t n, int d, int ms, bool with_nb, MstWs &w) {
@@ -344,6 +345,11 @@ size_t carve_mst(Carver &c, int64_t n, int d, int ms, bool with_nb, MstWs &w) {
     w.sort_tmp_bytes = edge_sort_temp_bytes(n - 1);
     w.sort_tmp = c.take<char>(w.sort_tmp_bytes);
     w.ctr = c.take<BvCounters>(1);
+    // the largest component's complement (used when it holds >= n / 2 points):
+    // its points' features here; orig, labels, sizes and the second active list
+    // in the edge sort's u32 scratch (sb, sc, sd, sa), norms and core distances
+    // in s64a -- all idle until the final sort
+    w.xs = c.take<float>((size_t)d * (size_t)(n / 2 + 1));
     w.nbr_idx = nullptr;
     w.nbr_d2 = nullptr;
     w.knn_nx = nullptr;
@@ -474,7 +480,8 @@ int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const flo
         return fail(EKH_EINVAL, "min_samples = %d out of range [1, min(n - 1, %d)]", min_samples, EKH_MAX_K - 1);
     if ((nbr_idx == nullptr) != (nbr_d2 == nullptr))
         return fail(EKH_EINVAL, "nbr_idx and nbr_d2 must both be NULL or both be set");
-    if (flags & ~(EKH_MST_NO_NEIGHBOUR_EDGES | EKH_MST_NO_COMPONENT_BOUND)) return fail(EKH_EINVAL, "unknown flags");
+    if (flags & ~(EKH_MST_NO_NEIGHBOUR_EDGES | EKH_MST_NO_COMPONENT_BOUND | EKH_MST_FULL_SCANS))
+        return fail(EKH_EINVAL, "unknown flags");
     if (n >= 2 && (!out_lo || !out_hi || !out_w)) return fail(EKH_EINVAL, "edge outputs are NULL");
     if (!ws) return fail(EKH_EINVAL, "workspace is NULL");
     const bool with_nb = nbr_idx != nullptr;
@@ -516,6 +523,8 @@ int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const flo
     st.cmin1 = w.cmin1;
     st.cmin2 = w.cmin2;
     st.compW = w.compW;
+    st.csize = w.sd;
+    st.act_g = reinterpret_cast<int32_t *>(w.sa);
     st.e_lo = w.e_lo;
     st.e_hi = w.e_hi;
     st.e_w = w.e_w;
@@ -539,28 +548,72 @@ int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const flo
                         (long long)ncomp);
         const auto t0 = std::chrono::steady_clock::now();
         EKH_HIP(bv_reset_counters(st, s));
+        // after the first round (all singletons), find the largest component:
+        // when it holds >= n / 2 points its active points are scanned only
+        // against the points outside it (a cheapest edge leaves the component)
+        const int split_giant = round > 0 && !(flags & EKH_MST_FULL_SCANS) ? 1 : 0;
+        if (split_giant) EKH_HIP(bv_giant(st, s));
         EKH_HIP(bv_candidates(st, use_nb, use_bound, s));
-        EKH_HIP(bv_select_active(st, use_bound, s));
+        EKH_HIP(bv_select_active(st, use_bound, split_giant, s));
         EKH_HIP(hipMemcpyAsync(&h, w.ctr, sizeof h, hipMemcpyDeviceToHost, s));
         EKH_HIP(hipStreamSynchronize(s));
-        const int64_t nact = h.n_active;
+        const int64_t nact = h.n_active, nact_g = h.n_active_g;
+        ScanArgs sa{};
+        sa.X = X;
+        sa.ldx = ldx;
+        sa.n = n;
+        sa.nrm = w.nrm;
+        sa.core = core;
+        sa.comp = w.comp;
+        sa.compW = w.compW;
+        sa.best = w.best;
+        sa.d = d;
+        sa.chunks = feature_chunks(d);
         if (nact > 0) {
-            ScanArgs sa{};
-            sa.X = X;
-            sa.ldx = ldx;
-            sa.n = n;
-            sa.nrm = w.nrm;
-            sa.core = core;
-            sa.comp = w.comp;
-            sa.compW = w.compW;
+            sa.Xb = X;
+            sa.ldb = ldx;
+            sa.nb = n;
+            sa.nrm_b = w.nrm;
+            sa.core_b = core;
+            sa.comp_b = w.comp;
+            sa.orig = nullptr;
             sa.act = w.act;
             sa.nact = nact;
-            sa.best = w.best;
-            sa.d = d;
-            sa.chunks = feature_chunks(d);
             sa.tiles = tiles;
             sa.splits = scan_splits(QM, (nact + QT - 1) / QT, tiles);
             TimedLaunch tl(1, 2.0 * d * (double)nact * (double)n, s);
+            EKH_HIP(launch_scan_tile(QM, sa, s));
+            tl.done();
+        }
+        if (nact_g > 0) {
+            const int64_t sg = (int64_t)(h.giant >> 32), ns = n - sg;
+            const int32_t g = (int32_t)(uint32_t)h.giant;
+            if (sg * 2 < n || ns < 1)
+                return fail(EKH_EINTERNAL, "round %d: largest component %lld of %lld", round, (long long)sg,
+                            (long long)n);
+            int32_t *orig = reinterpret_cast<int32_t *>(w.sb);
+            int32_t *comp_s = reinterpret_cast<int32_t *>(w.sc);
+            float *nrm_s = reinterpret_cast<float *>(w.s64a), *core_s = nrm_s + (n / 2 + 1);
+            EKH_HIP(bv_complement(st, g, orig, s));
+            EKH_HIP(hipMemcpyAsync(&h, w.ctr, sizeof h, hipMemcpyDeviceToHost, s));
+            EKH_HIP(hipStreamSynchronize(s));
+            if ((int64_t)h.n_comp_g != ns)
+                return fail(EKH_EINTERNAL, "round %d: %u points outside the largest component, expected %lld", round,
+                            h.n_comp_g, (long long)ns);
+            EKH_HIP(bv_gather_points(X, ldx, d, orig, ns, w.nrm, core, w.comp, w.xs, nrm_s, core_s, comp_s, s));
+            const int64_t tiles_g = (ns + TR - 1) / TR;
+            sa.Xb = w.xs;
+            sa.ldb = ns;
+            sa.nb = ns;
+            sa.nrm_b = nrm_s;
+            sa.core_b = core_s;
+            sa.comp_b = comp_s;
+            sa.orig = orig;
+            sa.act = st.act_g;
+            sa.nact = nact_g;
+            sa.tiles = tiles_g;
+            sa.splits = scan_splits(QM, (nact_g + QT - 1) / QT, tiles_g);
+            TimedLaunch tl(1, 2.0 * d * (double)nact_g * (double)ns, s);
             EKH_HIP(launch_scan_tile(QM, sa, s));
             tl.done();
         }
@@ -580,7 +633,8 @@ int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const flo
             stats->n_components[round] = (int32_t)ncomp;
             stats->resolved[round] = h.n_resolved;
             stats->skipped[round] = h.n_skipped;
-            stats->scanned[round] = nact;
+            stats->scanned[round] = nact + nact_g;
+            stats->scanned_giant[round] = nact_g;
             stats->edges_added[round] = before - ncomp;
             stats->round_ms[round] =
                 std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();

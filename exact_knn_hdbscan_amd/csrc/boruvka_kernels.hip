@@ -30,6 +30,7 @@ __global__ void bv_init_kernel(BvState st) {
     st.cmin1[a] = kNoEdge;
     st.cmin2[a] = 0xffffffffu;
     st.compW[a] = kInfBits;
+    st.csize[a] = 0;
     if (a == 0) *st.ctr = BvCounters{};
 }
 
@@ -45,6 +46,9 @@ __global__ void bv_reset_counters_kernel(BvCounters *c) {
         c->n_skipped = 0;
         c->n_roots = 0;
         c->n_missing = 0;
+        c->n_active_g = 0;
+        c->n_comp_g = 0;
+        c->giant = 0;
     }
 }
 
@@ -60,18 +64,24 @@ __device__ __forceinline__ void wave_count(bool pred, uint32_t *ctr) {
         atomicAdd(ctr, (uint32_t)__popcll(m));
 }
 
-// Per-workgroup minima by label in LDS: open addressing with linear probing
-// (label -1 = free slot).  A workgroup inserts at most kBigBs labels into
-// kHashSlots > kBigBs slots, so a free slot always exists; the bounded probe
-// loop falls back to the global atomic all the same.
-template <class T> struct LdsMinTable {
+// Per-workgroup minima (or sums, ADD) by label in LDS: open addressing with
+// linear probing (label -1 = free slot).  A workgroup inserts at most kBigBs
+// labels into kHashSlots > kBigBs slots, so a free slot always exists; the
+// bounded probe loop falls back to the global atomic all the same.
+template <class T, bool ADD = false> struct LdsMinTable {
+    __device__ __forceinline__ static void op(T *p, T v) {
+        if (ADD)
+            atomicAdd(p, v);
+        else
+            atomicMin(p, v);
+    }
     int32_t key[kHashSlots];
     T val[kHashSlots];
 
     __device__ __forceinline__ void clear() {
         for (int i = threadIdx.x; i < kHashSlots; i += blockDim.x) {
             key[i] = -1;
-            val[i] = ~T(0);
+            val[i] = ADD ? T(0) : ~T(0);
         }
     }
     __device__ __forceinline__ void insert(int32_t c, T v, T *gbase) {
@@ -79,14 +89,14 @@ template <class T> struct LdsMinTable {
         for (int p = 0; p < kHashSlots; ++p) {
             const int32_t k = atomicCAS(&key[h], -1, c);
             if (k == -1 || k == c) {
-                atomicMin(&val[h], v);
+                op(&val[h], v);
                 return;
             }
             h = (h + 1) & (kHashSlots - 1);
         }
-        atomicMin(&gbase[c], v);
+        op(&gbase[c], v);
     }
-    // the lanes that share the wave's first label combine with a wave minimum
+    // the lanes that share the wave's first label combine (wave minimum or sum)
     // and insert once; the others insert their own
     __device__ __forceinline__ void insert_grouped(int32_t c, T v, bool active, T *gbase) {
         const uint64_t act = __ballot(active);
@@ -95,10 +105,10 @@ template <class T> struct LdsMinTable {
         const int leader = __ffsll((long long)act) - 1;
         const int32_t c0 = __shfl(c, leader);
         const bool same = active && c == c0;
-        T m = same ? v : ~T(0);
+        T m = same ? v : (ADD ? T(0) : ~T(0));
         for (int o = 32; o > 0; o >>= 1) {
             const T y = __shfl_xor(m, o);
-            m = y < m ? y : m;
+            m = ADD ? m + y : (y < m ? y : m);
         }
         if (lane == leader) insert(c0, m, gbase);
         if (active && !same) insert(c, v, gbase);
@@ -106,7 +116,7 @@ template <class T> struct LdsMinTable {
     // after a barrier: one global atomic per label the workgroup saw
     __device__ __forceinline__ void flush(T *gbase) {
         for (int i = threadIdx.x; i < kHashSlots; i += blockDim.x)
-            if (key[i] >= 0) atomicMin(&gbase[key[i]], val[i]);
+            if (key[i] >= 0) op(&gbase[key[i]], val[i]);
     }
 };
 
@@ -177,33 +187,133 @@ hipError_t bv_candidates(const BvState &st, int use_nb, int use_bound, hipStream
 // known edge out of its component cannot supply a lighter one; on equality it
 // still could, through a lower index, so it stays active).  Compacted into
 // st.act with one atomic per wave.
-__global__ __launch_bounds__(kBigBs) void bv_select_active_kernel(BvState st, int use_bound) {
+// Appends the lanes with `take` to list[] at positions claimed with one
+// atomic per wave on *count.
+__device__ __forceinline__ void wave_append(bool take, int32_t value, uint32_t *count, int32_t *list) {
+    const uint64_t m = __ballot(take);
+    const int lane = threadIdx.x & 63;
+    uint32_t base = 0;
+    if (lane == 0 && m) base = atomicAdd(count, (uint32_t)__popcll(m));
+    base = __shfl(base, 0);
+    if (take) list[base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull))] = value;
+}
+
+// With split_giant, the active points of the largest component (when it holds
+// at least half of the points) go to act_g instead: they need to be scanned
+// only against the points outside it.
+__global__ __launch_bounds__(kBigBs) void bv_select_active_kernel(BvState st, int use_bound, int split_giant) {
     __shared__ uint32_t n_skip;
     if (threadIdx.x == 0) n_skip = 0;
     __syncthreads();
+    const uint64_t gk = split_giant ? st.ctr->giant : 0;
+    const bool use_g = split_giant && (gk >> 32) * 2 >= (uint64_t)st.n;
+    const int32_t g = (int32_t)(uint32_t)gk;
     const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    bool act = false, skip = false;
+    bool act = false, skip = false, in_g = false;
     if (a < st.n && !st.resolved[a]) {
-        skip = use_bound && st.core[a] > __uint_as_float(st.compW[st.comp[a]]);
+        const int32_t c = st.comp[a];
+        skip = use_bound && st.core[a] > __uint_as_float(st.compW[c]);
         act = !skip;
+        in_g = use_g && c == g;
     }
-    const uint64_t m = __ballot(act);
-    const int lane = threadIdx.x & 63;
-    const int leader = __ffsll((long long)__ballot(1)) - 1;
-    uint32_t base = 0;
-    if (lane == leader && m) base = atomicAdd(&st.ctr->n_active, (uint32_t)__popcll(m));
-    base = __shfl(base, leader);
-    if (act) {
-        const uint32_t below = (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-        st.act[base + below] = (int32_t)a;
-    }
+    wave_append(act && !in_g, (int32_t)a, &st.ctr->n_active, st.act);
+    wave_append(act && in_g, (int32_t)a, &st.ctr->n_active_g, st.act_g);
     lds_count(skip, &n_skip);
     __syncthreads();
     if (threadIdx.x == 0 && n_skip) atomicAdd(&st.ctr->n_skipped, n_skip);
 }
 
-hipError_t bv_select_active(const BvState &st, int use_bound, hipStream_t s) {
-    hipLaunchKernelGGL(bv_select_active_kernel, grid_for(st.n, kBigBs), dim3(kBigBs), 0, s, st, use_bound);
+hipError_t bv_select_active(const BvState &st, int use_bound, int split_giant, hipStream_t s) {
+    hipLaunchKernelGGL(bv_select_active_kernel, grid_for(st.n, kBigBs), dim3(kBigBs), 0, s, st, use_bound,
+                       split_giant);
+    return hipGetLastError();
+}
+
+// Size of every component (LDS-combined counts per label), then the largest
+// as size << 32 | label (ties to the larger label) in ctr->giant.
+__global__ __launch_bounds__(kBigBs) void bv_comp_sizes_kernel(BvState st) {
+    __shared__ LdsMinTable<uint32_t, true> tab;
+    tab.clear();
+    __syncthreads();
+    const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool in = a < st.n;
+    tab.insert_grouped(in ? st.comp[a] : 0, 1u, in, st.csize);
+    __syncthreads();
+    tab.flush(st.csize);
+}
+
+__global__ __launch_bounds__(kBigBs) void bv_giant_kernel(BvState st) {
+    __shared__ unsigned long long bmax;
+    if (threadIdx.x == 0) bmax = 0;
+    __syncthreads();
+    const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    unsigned long long k = 0;
+    if (a < st.n && st.comp[a] == (int32_t)a) k = ((unsigned long long)st.csize[a] << 32) | (uint32_t)a;
+    for (int o = 32; o > 0; o >>= 1) {
+        const unsigned long long y = __shfl_xor(k, o);
+        k = y > k ? y : k;
+    }
+    if ((threadIdx.x & 63) == 0 && k) atomicMax(&bmax, k);
+    __syncthreads();
+    if (threadIdx.x == 0 && bmax) atomicMax((unsigned long long *)&st.ctr->giant, bmax);
+}
+
+hipError_t bv_giant(const BvState &st, hipStream_t s) {
+    hipLaunchKernelGGL(bv_comp_sizes_kernel, grid_for(st.n, kBigBs), dim3(kBigBs), 0, s, st);
+    hipLaunchKernelGGL(bv_giant_kernel, grid_for(st.n, kBigBs), dim3(kBigBs), 0, s, st);
+    return hipGetLastError();
+}
+
+// The points outside component `giant`, listed in orig (ctr->n_comp_g of
+// them); one atomic per workgroup, waves placed by an LDS prefix.
+__global__ __launch_bounds__(kBigBs) void bv_complement_kernel(BvState st, int32_t giant, int32_t *orig) {
+    __shared__ uint32_t wcount[kBigBs / 64];
+    __shared__ uint32_t base;
+    const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool out = a < st.n && st.comp[a] != giant;
+    const uint64_t m = __ballot(out);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) wcount[wave] = (uint32_t)__popcll(m);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+        for (int w = 0; w < kBigBs / 64; ++w) {
+            const uint32_t c = wcount[w];
+            wcount[w] = t;
+            t += c;
+        }
+        base = t ? atomicAdd(&st.ctr->n_comp_g, t) : 0;
+    }
+    __syncthreads();
+    if (out) orig[base + wcount[wave] + (uint32_t)__popcll(m & ((1ull << lane) - 1ull))] = (int32_t)a;
+}
+
+hipError_t bv_complement(const BvState &st, int32_t giant, int32_t *orig, hipStream_t s) {
+    hipLaunchKernelGGL(bv_complement_kernel, grid_for(st.n, kBigBs), dim3(kBigBs), 0, s, st, giant, orig);
+    return hipGetLastError();
+}
+
+// Feature-major copy [d, ns] of the listed points with their norms, core
+// distances and labels (writes coalesced along the list).
+__global__ __launch_bounds__(kBs) void bv_gather_points_kernel(const float *X, int64_t ldx, int d,
+                                                                const int32_t *orig, int64_t ns, const float *nrm,
+                                                                const float *core, const int32_t *comp, float *xs,
+                                                                float *nrm_s, float *core_s, int32_t *comp_s) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= ns) return;
+    const int32_t p = orig[i];
+    for (int f = 0; f < d; ++f) xs[(int64_t)f * ns + i] = X[(int64_t)f * ldx + p];
+    nrm_s[i] = nrm[p];
+    core_s[i] = core[p];
+    comp_s[i] = comp[p];
+}
+
+hipError_t bv_gather_points(const float *X, int64_t ldx, int d, const int32_t *orig, int64_t ns, const float *nrm,
+                            const float *core, const int32_t *comp, float *xs, float *nrm_s, float *core_s,
+                            int32_t *comp_s, hipStream_t s) {
+    if (ns <= 0) return hipSuccess;
+    hipLaunchKernelGGL(bv_gather_points_kernel, grid_for(ns, kBs), dim3(kBs), 0, s, X, ldx, d, orig, ns, nrm, core,
+                       comp, xs, nrm_s, core_s, comp_s);
     return hipGetLastError();
 }
 
@@ -313,6 +423,7 @@ __global__ void bv_relabel_kernel(BvState st) {
         st.cmin1[a] = kNoEdge;
         st.cmin2[a] = 0xffffffffu;
         st.compW[a] = kInfBits;
+        st.csize[a] = 0;
     }
     wave_count(root, &st.ctr->n_roots);
 }

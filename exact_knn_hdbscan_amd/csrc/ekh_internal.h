@@ -117,16 +117,27 @@ struct BvCounters {
     uint32_t n_edges;
     uint32_t n_roots;
     uint32_t n_missing;
-    uint32_t pad[2];
+    uint32_t n_active_g; // active points of the largest component, listed apart
+    uint32_t n_comp_g;   // points outside it, gathered for their scan
+    uint64_t giant;      // size << 32 | label of the largest component
 };
 
 struct ScanArgs {
+    // query side (the active points index these)
     const float *X;
     int64_t ldx;
     int64_t n;
     const float *nrm;     // |x|^2 [n]
     const float *core;    // [n]
     const int32_t *comp;  // component label of every point
+    // database side: all points, or a gathered subset whose row j is point orig[j]
+    const float *Xb;
+    int64_t ldb;
+    int64_t nb;
+    const float *nrm_b;
+    const float *core_b;
+    const int32_t *comp_b;
+    const int32_t *orig;  // NULL: row j is point j
     const uint32_t *compW; // bound W bits per component (kInfBits = none)
     const int32_t *act;   // active points
     int64_t nact;
@@ -134,7 +145,7 @@ struct ScanArgs {
     int d;
     int chunks;
     int splits;
-    int64_t tiles;
+    int64_t tiles;        // database tiles
 };
 
 hipError_t launch_scan_tile(int QM, const ScanArgs &a, hipStream_t s);
@@ -154,6 +165,8 @@ struct BvState {
     uint64_t *cmin1;   // per component (W bits << 32 | lo)
     uint32_t *cmin2;   // per component hi
     uint32_t *compW;   // per component bound W bits
+    uint32_t *csize;   // per component size (zero between rounds)
+    int32_t *act_g;    // active points of the largest component
     int32_t *e_lo;
     int32_t *e_hi;
     float *e_w;
@@ -163,7 +176,12 @@ struct BvState {
 hipError_t bv_init(const BvState &st, hipStream_t s);
 hipError_t bv_reset_counters(const BvState &st, hipStream_t s);
 hipError_t bv_candidates(const BvState &st, int use_neighbour_edges, int use_bound, hipStream_t s);
-hipError_t bv_select_active(const BvState &st, int use_bound, hipStream_t s);
+hipError_t bv_select_active(const BvState &st, int use_bound, int split_giant, hipStream_t s);
+hipError_t bv_giant(const BvState &st, hipStream_t s);
+hipError_t bv_complement(const BvState &st, int32_t giant, int32_t *orig, hipStream_t s);
+hipError_t bv_gather_points(const float *X, int64_t ldx, int d, const int32_t *orig, int64_t ns, const float *nrm,
+                            const float *core, const int32_t *comp, float *xs, float *nrm_s, float *core_s,
+                            int32_t *comp_s, hipStream_t s);
 hipError_t bv_component_min(const BvState &st, hipStream_t s);
 hipError_t bv_select_edges(const BvState &st, hipStream_t s);
 hipError_t bv_jump(const BvState &st, hipStream_t s);

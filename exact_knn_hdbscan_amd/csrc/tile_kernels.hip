@@ -128,12 +128,15 @@ template <int CB, int RB> struct EpiScan {
     float corea[CB];
     int32_t ca[CB];
     int g;
+    const int32_t *orig; // database row -> point (NULL: the same)
 
     __device__ __forceinline__ void candidate(int cb, float d2, int32_t j, int32_t cj, float corej) {
-        if (cj == ca[cb]) return;
+        // same component, or a padding row past the database (label -1)
+        if (cj == ca[cb] || cj < 0) return;
         const float D = sqrt_rn(d2 > 0.f ? d2 : 0.f);
         const float W = fmaxf(fmaxf(corea[cb], corej), D);
-        const uint64_t key = ((uint64_t)__float_as_uint(W) << 32) | (uint32_t)j;
+        const uint32_t b = orig ? (uint32_t)orig[j] : (uint32_t)j;
+        const uint64_t key = ((uint64_t)__float_as_uint(W) << 32) | b;
         if (key < best[cb]) {
             best[cb] = key;
             thr[cb] = scan_threshold(W);
@@ -179,6 +182,7 @@ void scan_tile_kernel(ScanArgs a) {
 
     EpiScan<CB, T::RB> epi;
     epi.g = g;
+    epi.orig = a.orig;
     float bq[CB][QM];
     int32_t pt[CB];
     bool valid[CB];
@@ -201,7 +205,7 @@ void scan_tile_kernel(ScanArgs a) {
         epi.thr[cb] = (!valid[cb] || epi.corea[cb] > w0) ? -INFINITY : scan_threshold(w0);
     }
     const int64_t tb = a.tiles * split / a.splits, te = a.tiles * (split + 1) / a.splits;
-    run_tiles<QM, CB, true, FULL>(a.X, a.ldx, a.n, a.nrm, a.comp, a.core, a.d, a.chunks, tb, te, bq, epi);
+    run_tiles<QM, CB, true, FULL>(a.Xb, a.ldb, a.nb, a.nrm_b, a.comp_b, a.core_b, a.d, a.chunks, tb, te, bq, epi);
 
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {

@@ -137,15 +137,20 @@ int ekh_core_distances(const float *X, int64_t ldx, int64_t n, int32_t d, int32_
 /* flags for ekh_mst_boruvka: switch the exact shortcuts off (results do not change) */
 #define EKH_MST_NO_NEIGHBOUR_EDGES 1u
 #define EKH_MST_NO_COMPONENT_BOUND 2u
+/* scan the largest component's active points against all points, not only
+   against the points outside it (used when it holds at least n / 2 points) */
+#define EKH_MST_FULL_SCANS 4u
 
 typedef struct {
     int32_t rounds;                          /* Boruvka rounds run */
     int32_t n_components[EKH_MAX_ROUNDS];    /* components after each round */
     int64_t resolved[EKH_MAX_ROUNDS];        /* points whose cheapest edge came from their list */
     int64_t skipped[EKH_MAX_ROUNDS];         /* points skipped by the component bound */
-    int64_t scanned[EKH_MAX_ROUNDS];         /* points scanned against all n */
+    int64_t scanned[EKH_MAX_ROUNDS];         /* points scanned */
     int64_t edges_added[EKH_MAX_ROUNDS];
     double round_ms[EKH_MAX_ROUNDS];         /* host wall time of each round */
+    int64_t scanned_giant[EKH_MAX_ROUNDS];   /* of the scanned, points of a component holding >= n / 2
+                                                points, scanned only against the points outside it */
 } ekh_mst_stats;
 
 size_t ekh_mst_workspace_bytes(int64_t n, int32_t d, int32_t min_samples, int with_neighbours);

@@ -126,7 +126,7 @@ def test_core_and_mst_reject_bad_arguments(lib):
     assert lib.ekh_core_distances(BOGUS, 10, 10, 3, 10, BOGUS, None, None, BOGUS, 1 << 30, None) == -1  # ms >= n
     assert lib.ekh_core_distances(BOGUS, 10, 10, 3, 3, None, None, None, BOGUS, 1 << 30, None) == -1
     assert lib.ekh_core_distances(BOGUS, 10, 10, 3, 3, BOGUS, BOGUS, None, BOGUS, 1 << 30, None) == -1
-    assert lib.ekh_mst_boruvka(BOGUS, 10, 10, 3, BOGUS, 3, None, None, 4, BOGUS, BOGUS, BOGUS, None, BOGUS,
+    assert lib.ekh_mst_boruvka(BOGUS, 10, 10, 3, BOGUS, 3, None, None, 8, BOGUS, BOGUS, BOGUS, None, BOGUS,
                                1 << 30, None) == -1  # unknown flag
     assert lib.ekh_mst_boruvka(BOGUS, 10, 10, 3, None, 3, None, None, 0, BOGUS, BOGUS, BOGUS, None, BOGUS,
                                1 << 30, None) == -1

@@ -105,8 +105,11 @@ def test_core_and_mst_clips_full_size(name):
     lo, hi, w, st = ekh.mst_boruvka(Xg, core, ms, ni, nd2, return_stats=True)
     core, ni, nd2 = host(core).astype(np.float64), host(ni), host(nd2)
     lo, hi, w = host(lo).astype(np.int64), host(hi).astype(np.int64), host(w).astype(np.float64)
-    say("rounds %d scanned %s" % (st["rounds"], st["scanned"]))
+    say("rounds %d scanned %s, of them against the largest component's complement %s"
+        % (st["rounds"], st["scanned"], st["scanned_giant"]))
     assert st["rounds"] <= int(np.ceil(np.log2(n)))
+    # the last round's largest component (most of the points) takes the complement scan
+    assert sum(st["scanned_giant"]) > 0
 
     # sampled rows: lists and core distances against the oracle
     rows = sample_rows(n, 200, 3)

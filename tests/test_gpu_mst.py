@@ -79,15 +79,23 @@ def test_mst_clips(ms):
 def test_pruning_is_exact():
     """The tree with every exact shortcut equals the tree without any, bit for
     bit, on clip-like data with duplicates ("Exact shortcuts": the test
-    pruning_is_exact builds it both ways)."""
+    pruning_is_exact builds it both ways); so does the tree whose largest
+    component is scanned against all points (flag 4) instead of only the points
+    outside it."""
     base = datagen.spike_clips(3000, 10, seed=3)
     X = np.ascontiguousarray(np.concatenate([base, base[:, :200], base[:, 1000:1100]], axis=1))
     say("pruning is exact, n=%d" % X.shape[1])
-    ref = gpu_mst(X, 10, flags=3)
-    for flags in (0, 1, 2):
-        got = gpu_mst(X, 10, flags=flags)
-        for a, b in zip(got, ref):
+    ref = gpu_mst(X, 10, flags=7)
+    giant = 0
+    for flags in (0, 1, 2, 3, 4):
+        got = gpu_mst(X, 10, flags=flags, stats=True)
+        for a, b in zip(got[:3], ref):
             np.testing.assert_array_equal(a, b)
+        giant += sum(got[3]["scanned_giant"]) if not flags & 4 else 0
+        if flags & 4:
+            assert sum(got[3]["scanned_giant"]) == 0
+    say("points scanned against the largest component's complement: %d" % giant)
+    assert giant > 0
     got = gpu_mst(X, 10, with_lists=False)
     for a, b in zip(got, ref):
         np.testing.assert_array_equal(a, b)
