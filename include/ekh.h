@@ -167,7 +167,11 @@ size_t ekh_mst_workspace_bytes(int64_t n, int32_t d, int32_t min_samples, int wi
  *      in the workspace query).  The shortcuts are exact for any core array:
  *      a list settles a point only when its last entry is strictly farther
  *      than the point's core distance.
- *  flags: EKH_MST_NO_* switches.
+ *  flags: EKH_MST_NO_* and EKH_MST_FULL_SCANS switches (none changes the tree).
+ *      From the second round on, when one component holds at least n / 2
+ *      points, its active points are scanned only against a gathered copy of
+ *      the points outside it (the workspace holds d * (n / 2 + 1) floats for
+ *      that copy).
  *  out_lo, out_hi [n - 1] int32, out_w [n - 1] float32: the edges, lo < hi,
  *      sorted by (w, lo, hi).  n = 1 gives no edges.
  *  stats: optional host struct filled per round.
