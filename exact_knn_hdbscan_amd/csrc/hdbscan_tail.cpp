@@ -261,11 +261,8 @@ extern "C" int ekh_hdbscan_tail(const int32_t *lo, const int32_t *hi, const floa
         at[i] = (uint32_t)i;
     }
     radix_sort(key, at);
-    std::vector<Entry> ent(ne);
-    for (int64_t j = 0; j < ne; ++j) {
-        const Entry &r = T.raw[at[j]];
-        ent[j] = Entry{n + (int64_t)(key[j] >> cb), (int64_t)(key[j] & cmask), r.lambda, r.size};
-    }
+    // entry j of the sorted list: parent n + (key[j] >> cb), child key[j] & cmask,
+    // lambda and size from T.raw[at[j]]
 
     // stabilities (final id order), summed over each cluster's entries in list order
     std::vector<double> birth(ncl), st(ncl, 0.0);
@@ -276,9 +273,10 @@ extern "C" int ekh_hdbscan_tail(const int32_t *lo, const int32_t *hi, const floa
         par[i] = T.parent[c] < 0 ? -1 : fid[T.parent[c]] - n;
     }
     for (int64_t i = 1; i < ncl; ++i) (k0[par[i]] < 0 ? k0[par[i]] : k1[par[i]]) = i; // ascending: k0 < k1
-    for (const Entry &e : ent) {
-        const int64_t i = e.parent - n;
-        if (e.lambda != birth[i]) st[i] += (double)e.size * (e.lambda - birth[i]);
+    for (int64_t j = 0; j < ne; ++j) {
+        const Entry &r = T.raw[at[j]];
+        const int64_t i = (int64_t)(key[j] >> cb);
+        if (r.lambda != birth[i]) st[i] += (double)r.size * (r.lambda - birth[i]);
     }
 
     // excess of mass, children first; the root is never selected
@@ -309,15 +307,18 @@ extern "C" int ekh_hdbscan_tail(const int32_t *lo, const int32_t *hi, const floa
         else
             clab[i] = p >= 0 ? clab[p] : -1;
     }
-    for (const Entry &e : ent)
-        if (e.child < n) out_labels[e.child] = clab[e.parent - n];
+    for (int64_t j = 0; j < ne; ++j) {
+        const int64_t child = (int64_t)(key[j] & cmask);
+        if (child < n) out_labels[child] = clab[key[j] >> cb];
+    }
 
     if (want_tree)
-        for (int64_t i = 0; i < ne; ++i) {
-            ct_parent[i] = ent[i].parent;
-            ct_child[i] = ent[i].child;
-            ct_lambda[i] = ent[i].lambda;
-            ct_size[i] = ent[i].size;
+        for (int64_t j = 0; j < ne; ++j) {
+            const Entry &r = T.raw[at[j]];
+            ct_parent[j] = n + (int64_t)(key[j] >> cb);
+            ct_child[j] = (int64_t)(key[j] & cmask);
+            ct_lambda[j] = r.lambda;
+            ct_size[j] = r.size;
         }
     if (out_stability) std::copy(st.begin(), st.end(), out_stability);
     if (info) *info = ekh_hdbscan_info{ne, (int32_t)ncl, nsel};
