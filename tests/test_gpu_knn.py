@@ -118,6 +118,8 @@ def test_knn_chunk_and_split_invariance():
     (99001, 1500, 61, 11, 0, (768, 0)),
     # two chunks: 99,968 rows (781 tiles: one whole round + 13 split tiles), then 20,032 rows (all split)
     (120000, 1000, 16, 8, 100_000_000, (768, 0)),
+    # K = 32 lists: two workgroups per CU (512 resident), 648 tiles of 64 rows: 512 whole + 136 split
+    (41435, 2552, 128, 21, 0, (512, 0)),
 ])
 def test_knn_whole_round_and_split_tail(n, m, d, k, dots, layout):
     """The launch layout with whole tiles for the full rounds of resident
