@@ -143,6 +143,19 @@ def test_knn_whole_round_and_split_tail(n, m, d, k, dots, layout):
     np.testing.assert_array_equal(host(d2), dd)
 
 
+def test_knn_query_tiles_fill_whole_rounds():
+    """98,304 queries = 768 tiles of 128 rows, exactly one round of resident
+    workgroups: no split tail, every tile reads the whole database."""
+    n, m, d, k = 98304, 1000, 61, 11
+    p = ekh.knn_plan(n, m, d, k)
+    assert p["body_tiles"] == 0 and p["splits"] == 1, p
+    X = datagen.gaussian_mixture(n, d, 15, seed=21)
+    Y = datagen.gaussian_mixture(m, d, 15, seed=22)
+    say("knn n=%d m=%d: %s" % (n, m, p))
+    i, dd = ekh.knn(dev(X), dev(Y), k)
+    check_knn(X, Y, k, host(i), host(dd), rescored=True)
+
+
 def test_knn_repeatable():
     X = datagen.spike_clips(3000, 8, seed=4)
     Xg = dev(X)
