@@ -24,8 +24,9 @@ constexpr int kThreads = kWaves * 64; // 256 threads
 template <int QM> struct TileGeo;
 template <> struct TileGeo<16> { static constexpr int TR = 32; };
 template <> struct TileGeo<32> { static constexpr int TR = 32; };
-// d > 128: 16-row tiles keep the prefetch registers and the LDS tile small
-// enough for two workgroups per CU
+template <> struct TileGeo<56> { static constexpr int TR = 32; };
+// d > 224: 16-row tiles keep the prefetch registers and the LDS tile small
+// enough for two workgroups per CU without spills
 template <> struct TileGeo<64> { static constexpr int TR = 16; };
 
 // instantiated list lengths; a request for k uses the smallest K >= k
@@ -36,7 +37,8 @@ inline int pick_k(int k) {
         if (k <= kKList[i]) return kKList[i];
     return -1;
 }
-inline int pick_qm(int d) { return d <= 64 ? 16 : (d <= 128 ? 32 : 64); }
+// (with 32-row tiles the loader needs 4 * QM to be a multiple of 32)
+inline int pick_qm(int d) { return d <= 64 ? 16 : (d <= 128 ? 32 : (d <= 224 ? 56 : 64)); }
 inline int tile_rows(int qm) { return qm == 64 ? 16 : 32; }
 // kNN tile kernel occupancy: three waves per SIMD where the registers fit
 // without spills (d <= 64 and K <= 16: 156 VGPRs at K = 11; d <= 128 and

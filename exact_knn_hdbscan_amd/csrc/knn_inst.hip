@@ -28,6 +28,7 @@ template <> hipError_t launch_knn_tile_k<EKH_KNN_K>(int QM, const KnnArgs &a, hi
     switch (QM) {
     case 16: return knn_tile_full<EKH_KNN_K, 16>(a, s);
     case 32: return knn_tile_full<EKH_KNN_K, 32>(a, s);
+    case 56: return knn_tile_full<EKH_KNN_K, 56>(a, s);
     case 64: return knn_tile_full<EKH_KNN_K, 64>(a, s);
     default: return hipErrorInvalidValue;
     }

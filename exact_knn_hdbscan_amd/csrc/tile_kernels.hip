@@ -237,6 +237,7 @@ hipError_t launch_scan_tile(int QM, const ScanArgs &a, hipStream_t s) {
     switch (QM) {
     case 16: return scan_full<16>(a, s);
     case 32: return scan_full<32>(a, s);
+    case 56: return scan_full<56>(a, s);
     case 64: return scan_full<64>(a, s);
     default: return hipErrorInvalidValue;
     }

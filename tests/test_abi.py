@@ -86,7 +86,7 @@ def test_knn_plan_invariants_and_workspace(lib):
         assert rc == 0
         rows, qt, body, splits, slots, lbody, lsplits = p
         K = next(x for x in K_LIST if x >= k)
-        tiles = -(-m // (16 if d > 128 else 32))
+        tiles = -(-m // (16 if d > 224 else 32))
         assert qt in (64, 128) and slots in (512, 768) and rows >= 1
         assert rows == n or rows % qt == 0
         last = n % rows or rows

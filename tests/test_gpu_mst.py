@@ -33,7 +33,7 @@ def test_mst_tiny():
     say("report", rep)
 
 
-@pytest.mark.parametrize("n,d,ms", [(700, 5, 4), (1001, 61, 10), (513, 3, 1), (400, 2, 2)])
+@pytest.mark.parametrize("n,d,ms", [(700, 5, 4), (1001, 61, 10), (513, 3, 1), (400, 2, 2), (600, 150, 3)])
 def test_mst_integer_grid_identical(n, d, ms):
     """Integer coordinates keep every D2 exact and every weight comparison
     identical in float32 and float64, so the trees must be equal edge for edge."""
@@ -100,6 +100,17 @@ def test_pruning_is_exact():
     for a, b in zip(got, ref):
         np.testing.assert_array_equal(a, b)
     check_mst(X, 10, *ref)
+
+
+@pytest.mark.parametrize("d", [100, 129, 200, 256])
+def test_mst_dimensions(d):
+    """The scan kernel at every feature width it is built for (d <= 128: 32
+    features per k-step group; 128 < d <= 224 and d > 224: the wider forms)."""
+    X = datagen.gaussian_mixture(1500, d, 6, seed=d)
+    say("mst d=%d" % d)
+    lo, hi, w, st = gpu_mst(X, 5, stats=True)
+    say("scanned", st["scanned"])
+    check_mst(X, 5, lo, hi, w)
 
 
 def test_mst_small_sizes():
