@@ -47,6 +47,24 @@ def test_mst_integer_grid_identical(n, d, ms):
     np.testing.assert_array_equal(w, ow.astype(np.float32))
 
 
+def test_mst_integer_grid_large_with_ties():
+    """20,000 integer points in 3-D (coordinates -6..6): heavy exact ties in
+    every round, and a last round whose largest component is scanned against
+    the points outside it only.  Edge for edge equal to the oracle's Prim, and
+    to the tree with full scans (flag 4)."""
+    X = datagen.integer_grid(20000, 3, seed=20003, half_range=6)
+    lo, hi, w, st = gpu_mst(X, 4, stats=True)
+    say("scanned %s, largest component apart %s" % (st["scanned"], st["scanned_giant"]))
+    assert sum(st["scanned_giant"]) > 0
+    core = oracle.core_distances(X, 4)
+    olo, ohi, ow = oracle.mst_prim(X, core)
+    np.testing.assert_array_equal(lo, olo)
+    np.testing.assert_array_equal(hi, ohi)
+    np.testing.assert_array_equal(w, ow.astype(np.float32))
+    for a, b in zip((lo, hi, w), gpu_mst(X, 4, flags=4)):
+        np.testing.assert_array_equal(a, b)
+
+
 def test_mst_closed_forms():
     n = 150
     say("mst collinear ms=2 / ms=3, duplicates star")
