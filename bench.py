@@ -178,7 +178,8 @@ def time_seeding(ekh, datagen, oracle_too, reps=10):
 def time_sections(ekh, datagen, oracle_too=False, reps=5):
     """ekh_knn on the two section workloads (50,000 x 5,000 at d = 102, k = 10; and
     200,000 x 20,000 at d = 200, k = 10, in chunks of max_chunk_dots = 64e6): median
-    time per call with inputs resident, the tile kernel's rate, and the pair rate."""
+    time per call with inputs resident, the tile kernel's rate per launch, the
+    rate over the whole call, and the pair rate."""
     import numpy as np
     import torch
 
@@ -205,9 +206,15 @@ def time_sections(ekh, datagen, oracle_too=False, reps=5):
         timer.stop()
         ms_call = float(np.median(ts))
         pairs = float(X.shape[1]) * float(Y.shape[1])
+        plan = ekh.knn_plan(X.shape[1], Y.shape[1], X.shape[0], k, dots)
+        # with two chunks in flight the tile launches overlap: tile_ms sums their
+        # durations (each launch's own rate is tile_tflops); call_tflops is the
+        # algorithmic flop of the whole call over its wall time
         out[name] = {"ms": ms_call, "pairs_per_s": pairs / (ms_call / 1e3), "k": k, "max_chunk_dots": dots,
+                     "chunks_in_flight": plan["chunks_in_flight"],
                      "tile_launches": tk["launches"] // reps, "tile_ms": tk["ms"] / reps,
-                     "tile_tflops": tk["flop"] / (tk["ms"] / 1e3) / 1e12 if tk["ms"] else None}
+                     "tile_tflops": tk["flop"] / (tk["ms"] / 1e3) / 1e12 if tk["ms"] else None,
+                     "call_tflops": 2.0 * X.shape[0] * pairs / (ms_call / 1e3) / 1e12}
         if name == "ks4_section_50000x102":
             idx, _ = ekh.knn(X, Y, k, workspace=ws)
             out["bipartite_assignment"] = time_bipartite(ekh, datagen, idx, Y.shape[1], oracle_too)

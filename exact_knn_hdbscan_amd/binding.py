@@ -150,9 +150,10 @@ def knn_workspace_bytes(n: int, m: int, d: int, k: int, max_chunk_dots: int = 0)
 
 def knn_plan(n: int, m: int, d: int, k: int, max_chunk_dots: int = 0) -> dict:
     """Launch layout of the kNN tile kernel for these sizes (host only)."""
-    out = (_i64 * 7)()
+    out = (_i64 * 8)()
     _check(library().ekh_knn_plan(n, m, d, k, max_chunk_dots, out))
-    keys = ("chunk_rows", "tile_rows", "body_tiles", "splits", "slots", "last_body_tiles", "last_splits")
+    keys = ("chunk_rows", "tile_rows", "body_tiles", "splits", "slots", "last_body_tiles", "last_splits",
+            "chunks_in_flight")
     return dict(zip(keys, (int(v) for v in out)))
 
 

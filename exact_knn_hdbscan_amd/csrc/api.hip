@@ -101,9 +101,10 @@ struct KnnPlan {
     int K, QM, TR, QT, chunks;
     int64_t rows;   // rows per chunk
     int64_t tiles;  // database tiles
-    int64_t slots;  // workgroups resident at once
+    int64_t slots;  // workgroups resident at once, per chunk in flight
     int64_t warm;   // warm-up of fresh lists, in tiles
     int64_t part_entries; // split scratch (entries) of the largest chunk
+    int conc;       // chunks in flight at once (each on its own stream and scratch)
 };
 
 // How one chunk of query tiles is laid out on the grid of one launch: the
@@ -119,6 +120,7 @@ constexpr int64_t kCUs = 256;             // MI355X compute units (fixed, so tha
                                           // query and the run always plan alike)
 constexpr int64_t kLdsPerCu = 160 * 1024;
 constexpr int64_t kWarmupWork = 12000;    // warm-up of fresh lists, in 32-row tiles x k-steps (measured)
+constexpr int kChunkStreams = 2;          // chunks of one kNN call in flight at once (measured: 2 best)
 
 // kNN workgroups resident per CU: one per wave per SIMD that the registers
 // allow (four-wave workgroups), fewer if the double-buffered LDS tile and the
@@ -210,7 +212,12 @@ KnnPlan plan_knn(int64_t n, int64_t m, int d, int k, int64_t max_chunk_dots) {
         p.rows = std::min<int64_t>(n, std::max<int64_t>(r, p.QT));
     }
     p.tiles = (m + p.TR - 1) / p.TR;
-    p.slots = kCUs * knn_groups_per_cu(p.K, p.QM);
+    // Row chunks run kChunkStreams at a time, so each needs to fill only its
+    // share of the resident workgroups: fewer database splits, hence fewer
+    // list warm-ups per query, than one chunk filling the chip alone.
+    const int64_t nchunks = (n + p.rows - 1) / p.rows;
+    p.conc = (int)std::min<int64_t>(kChunkStreams, nchunks);
+    p.slots = std::max<int64_t>(1, kCUs * knn_groups_per_cu(p.K, p.QM) / p.conc);
     p.warm = kWarmupWork * 32 / (4 * p.chunks * p.TR); // measured at 32-row tiles
     p.part_entries = chunk_part_entries(p, p.rows);
     if (n % p.rows) p.part_entries = std::max(p.part_entries, chunk_part_entries(p, n % p.rows));
@@ -224,7 +231,8 @@ size_t knn_ws(const KnnPlan &p, int64_t n, int64_t m, bool self, Carver &c, floa
               int32_t **idx_scratch = nullptr, int k = 0, float **bt = nullptr, int d = 0) {
     *nx = c.take<float>(n);
     *ny = self ? *nx : c.take<float>(m);
-    *part = p.part_entries ? c.take<Entry>((size_t)p.part_entries) : nullptr;
+    // one split-list scratch per chunk in flight
+    *part = p.part_entries ? c.take<Entry>((size_t)p.part_entries * p.conc) : nullptr;
     if (idx_scratch) *idx_scratch = c.take<int32_t>((size_t)n * k);
     if (bt) *bt = c.take<float>((size_t)m * padded_dim(d));
     return c.used;
@@ -240,14 +248,72 @@ int check_points(const float *X, int64_t ld, int64_t n, int d, const char *name)
     return EKH_OK;
 }
 
+// Streams for the chunks of one call beyond the caller's own: created on first
+// use on each device (non-blocking, default priority) and kept until the
+// process ends.  Calls share them; each call orders its work on them through
+// its own events, so concurrent calls only queue behind each other.
+int chunk_streams(hipStream_t s, hipStream_t (&out)[kChunkStreams - 1]) {
+    static std::mutex mu;
+    static std::vector<std::vector<hipStream_t>> per_dev;
+    int dev = 0, cur = 0;
+    EKH_HIP(hipStreamGetDevice(s, &dev));
+    EKH_HIP(hipGetDevice(&cur));
+    std::lock_guard<std::mutex> lk(mu);
+    if ((int)per_dev.size() <= dev) per_dev.resize(dev + 1);
+    auto &v = per_dev[dev];
+    if (v.empty()) {
+        if (cur != dev) EKH_HIP(hipSetDevice(dev));
+        std::vector<hipStream_t> made(kChunkStreams - 1, nullptr);
+        hipError_t e = hipSuccess;
+        for (auto &x : made)
+            if (e == hipSuccess) e = hipStreamCreateWithFlags(&x, hipStreamNonBlocking);
+        if (cur != dev) hipSetDevice(cur);
+        if (e != hipSuccess) {
+            for (auto &x : made)
+                if (x) hipStreamDestroy(x);
+            return fail(EKH_EHIP, "hipStreamCreateWithFlags failed: %s", hipGetErrorString(e));
+        }
+        v = made;
+    }
+    for (int i = 0; i < kChunkStreams - 1; ++i) out[i] = v[i];
+    return EKH_OK;
+}
+
+// Makes `waiter` wait for the work queued so far on `from` (a one-use event).
+int stream_wait(hipStream_t waiter, hipStream_t from) {
+    hipEvent_t e;
+    EKH_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    hipError_t r = hipEventRecord(e, from);
+    if (r == hipSuccess) r = hipStreamWaitEvent(waiter, e, 0);
+    hipEventDestroy(e); // released once the recorded work completes
+    if (r != hipSuccess) return fail(EKH_EHIP, "stream ordering failed: %s", hipGetErrorString(r));
+    return EKH_OK;
+}
+
 // Runs the dense kNN over all chunks.  out_mode: kOutKnn or kOutCore.
+// Chunk c runs on stream c mod p.conc (0 = the caller's) with its own split
+// scratch; the other streams start after the norms and the caller's stream
+// waits for all of them before anything that reads the outputs.
 int run_knn(const KnnPlan &p, const float *X, int64_t ldx, int64_t n, const float *Y, int64_t ldy, int64_t m, int d,
             bool self, int out_mode, int k_out, int min_samples, int32_t *out_idx, float *out_dist, float *out_core,
             float *nx, float *ny, Entry *part, float *bt, hipStream_t s) {
     EKH_HIP(launch_norms(X, ldx, n, d, nx, s));
     if (!self) EKH_HIP(launch_norms(Y, ldy, m, d, ny, s));
     if (out_mode == kOutKnn) EKH_HIP(launch_point_major(Y, ldy, m, d, padded_dim(d), bt, s));
-    for (int64_t q0 = 0; q0 < n; q0 += p.rows) {
+    hipStream_t cs[kChunkStreams] = {s};
+    if (p.conc > 1) {
+        hipStream_t extra[kChunkStreams - 1];
+        int rc;
+        if ((rc = chunk_streams(s, extra)) != EKH_OK) return rc;
+        for (int i = 1; i < p.conc; ++i) {
+            cs[i] = extra[i - 1];
+            if ((rc = stream_wait(cs[i], s)) != EKH_OK) return rc;
+        }
+    }
+    int64_t chunk = 0;
+    for (int64_t q0 = 0; q0 < n; q0 += p.rows, ++chunk) {
+        const int lane = (int)(chunk % p.conc);
+        const hipStream_t cstream = cs[lane];
         KnnArgs a{};
         a.Q = X;
         a.ldq = ldx;
@@ -267,20 +333,24 @@ int run_knn(const KnnPlan &p, const float *X, int64_t ldx, int64_t n, const floa
         a.tiles = p.tiles;
         a.k_out = k_out;
         a.min_samples = min_samples;
-        a.part = part;
+        a.part = part ? part + (size_t)lane * p.part_entries : nullptr;
         a.out_idx = out_idx;
         a.out_dist = out_dist;
         a.out_core = out_core;
         a.out_mode = out_mode;
-        TimedLaunch tl(0, 2.0 * d * (double)a.nq * (double)m, s);
-        EKH_HIP(launch_knn_tile(p.K, p.QM, a, s));
+        TimedLaunch tl(0, 2.0 * d * (double)a.nq * (double)m, cstream);
+        EKH_HIP(launch_knn_tile(p.K, p.QM, a, cstream));
         tl.done();
         if (cp.splits > 1) {
             // the split tiles' rows only
             a.q0 += cp.body_q * p.QT;
             a.nq -= cp.body_q * p.QT;
-            EKH_HIP(launch_knn_merge(p.K, a, s));
+            EKH_HIP(launch_knn_merge(p.K, a, cstream));
         }
+    }
+    for (int i = 1; i < p.conc; ++i) {
+        int rc;
+        if ((rc = stream_wait(s, cs[i])) != EKH_OK) return rc;
     }
     if (out_mode == kOutKnn) {
         // reported distances, over all rows at once (no rows x m scratch involved)
@@ -390,7 +460,7 @@ size_t ekh_knn_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t k, int64
     return knn_ws(p, n, m, false, c, &nx, &ny, &part, &idx, k, &bt, d);
 }
 
-int ekh_knn_plan(int64_t n, int64_t m, int32_t d, int32_t k, int64_t max_chunk_dots, int64_t out[7]) {
+int ekh_knn_plan(int64_t n, int64_t m, int32_t d, int32_t k, int64_t max_chunk_dots, int64_t out[8]) {
     if (!out) return fail(EKH_EINVAL, "out is NULL");
     if (n < 1 || n > INT32_MAX || m < 1 || m > INT32_MAX || d < 1 || d > EKH_MAX_DIM || k < 1 || k > EKH_MAX_K ||
         k > m)
@@ -405,6 +475,7 @@ int ekh_knn_plan(int64_t n, int64_t m, int32_t d, int32_t k, int64_t max_chunk_d
     out[4] = p.slots;
     out[5] = last.body_q;
     out[6] = last.splits;
+    out[7] = p.conc;
     return EKH_OK;
 }
 

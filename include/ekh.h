@@ -26,7 +26,11 @@
  *    included; the bound keeps the tile loads' byte offsets within 32 bits).
  *    X, Y, outputs and the workspace are DEVICE pointers owned by the caller;
  *    the library never allocates or frees caller memory and keeps no state
- *    between calls (except the optional kernel timer below).
+ *    between calls, except the optional kernel timer below and one extra
+ *    stream per device (non-blocking, default priority, created on the first
+ *    chunked ekh_knn call and kept to the end of the process) on which a
+ *    second row chunk runs beside the caller's stream, joined back to it with
+ *    events before the call's later work.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
  *    ekh_knn and ekh_core_distances do not synchronise the host.
  *    ekh_mst_boruvka blocks: it reads a few counters back after each round.
@@ -104,14 +108,18 @@ int ekh_knn(const float *X, int64_t ldx, int64_t n, const float *Y, int64_t ldy,
  * in chunks; each chunk is one launch whose query tiles (64 or 128 rows) either
  * all read the database in the same number of splits, or (when a last round of
  * resident workgroups would be ragged) the first body tiles read the whole
- * database and only the rest are split.  Split lists are merged by one more
- * launch; results never depend on the layout.
+ * database and only the rest are split.  Up to 2 chunks are in flight at once,
+ * each on its own stream (the caller's and streams the library creates once per
+ * device, joined back to the caller's stream with events) and scratch, and each
+ * sized to its share of the resident workgroups.  Split lists are merged by one
+ * more launch; results never depend on the layout.
  *  out[0] rows per chunk, out[1] query rows per tile, out[2] body tiles of the
  *  first chunk, out[3] database splits of its other tiles, out[4] resident
- *  workgroups assumed, out[5] body tiles of the last chunk, out[6] its splits.
+ *  workgroups per chunk in flight, out[5] body tiles of the last chunk,
+ *  out[6] its splits, out[7] chunks in flight.
  * Returns EKH_OK, or EKH_EINVAL for sizes ekh_knn rejects or a NULL out.
  */
-int ekh_knn_plan(int64_t n, int64_t m, int32_t d, int32_t k, int64_t max_chunk_dots, int64_t out[7]);
+int ekh_knn_plan(int64_t n, int64_t m, int32_t d, int32_t k, int64_t max_chunk_dots, int64_t out[8]);
 
 /* ------------------------------------------------------------------ core distances */
 

@@ -46,7 +46,7 @@ def test_workspace_queries(lib):
 
 
 def plan(lib, n, m, d, k, dots=0):
-    out = (ctypes.c_int64 * 7)()
+    out = (ctypes.c_int64 * 8)()
     rc = lib.ekh_knn_plan(n, m, d, k, dots, out)
     return rc, list(out)
 
@@ -55,20 +55,22 @@ def test_knn_plan_of_the_clip_and_section_workloads(lib):
     # clips 500,000 x 61, lists of K = 11: 3,907 query tiles of 128 rows, 768
     # workgroups resident (256 CUs x 3): five whole rounds unsplit, the 67 tiles
     # left over in 11 database splits (737 workgroups: one more round)
-    assert plan(lib, 500000, 500000, 61, 11) == (0, [500000, 128, 3840, 11, 768, 3840, 11])
+    assert plan(lib, 500000, 500000, 61, 11) == (0, [500000, 128, 3840, 11, 768, 3840, 11, 1])
     # clips 100,000 x 61: 782 tiles, one whole round + 14 tiles in 54 splits
-    assert plan(lib, 100000, 100000, 61, 11) == (0, [100000, 128, 768, 54, 768, 768, 54])
+    assert plan(lib, 100000, 100000, 61, 11) == (0, [100000, 128, 768, 54, 768, 768, 54, 1])
     # Kilosort4 section, 50,000 queries x 5,000 (d = 102, 64-row tiles): 782 tiles
     rc, p = plan(lib, 50000, 5000, 102, 10)
     assert rc == 0 and p[1] == 64 and p[2] == 768 and p[3] > 1
     # fewer tiles than one round: every tile in the same number of splits
     rc, p = plan(lib, 5000, 50000, 102, 10)
     assert rc == 0 and p[2] == 0 and p[3] > 1
-    # wide section in chunks of 64e6 dots: 3,200-row chunks of 50 tiles, 512
-    # resident workgroups at d = 200 (two per CU), the last chunk 1,600 rows
+    # wide section in chunks of 64e6 dots: 3,200-row chunks of 50 tiles, two in
+    # flight, each with half of the 512 resident workgroups (two per CU at
+    # d = 200): 5 database splits instead of the 10 one chunk alone would take;
+    # the last chunk 1,600 rows
     rc, p = plan(lib, 200000, 20000, 200, 10, 64_000_000)
-    assert rc == 0 and p[0] == 3200 and p[1] == 64 and p[4] == 512 and p[2] == 0 and p[5] == 0
-    assert p[6] >= p[3] > 1
+    assert rc == 0 and p[0] == 3200 and p[1] == 64 and p[7] == 2 and p[4] == 256 and p[2] == 0 and p[5] == 0
+    assert p[3] == 5 and p[6] >= p[3]
 
 
 K_LIST = (2, 4, 8, 11, 16, 32)
@@ -84,11 +86,12 @@ def test_knn_plan_invariants_and_workspace(lib):
         dots = int(rng.choice([0, 0, int(rng.integers(1, 10 ** 10))]))
         rc, p = plan(lib, n, m, d, k, dots)
         assert rc == 0
-        rows, qt, body, splits, slots, lbody, lsplits = p
+        rows, qt, body, splits, slots, lbody, lsplits, conc = p
         K = next(x for x in K_LIST if x >= k)
         tiles = -(-m // (16 if d > 224 else 32))
-        assert qt in (64, 128) and slots in (512, 768) and rows >= 1
-        assert rows == n or rows % qt == 0
+        nchunks = -(-n // rows)
+        assert conc == min(2, nchunks) and slots * conc in range(511, 769) and rows >= 1
+        assert qt in (64, 128) and rows == n or rows % qt == 0
         last = n % rows or rows
         for r, b, s in ((rows, body, splits), (last, lbody, lsplits)):
             q = -(-r // qt)
@@ -98,7 +101,7 @@ def test_knn_plan_invariants_and_workspace(lib):
                 assert s > 1  # whole tiles only pay off when the rest is split
             # the split scratch fits the workspace (8-byte entries)
             if s > 1:
-                assert lib.ekh_knn_workspace_bytes(n, m, d, k, dots) >= 8 * K * s * (r - b * qt)
+                assert lib.ekh_knn_workspace_bytes(n, m, d, k, dots) >= 8 * K * s * (r - b * qt) * conc
     assert plan(lib, 0, 10, 4, 1)[0] == -1
     assert plan(lib, 10, 10, 4, 11)[0] == -1
     assert plan(lib, 10, 10, 257, 1)[0] == -1

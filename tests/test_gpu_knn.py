@@ -135,7 +135,7 @@ def test_knn_whole_round_and_split_tail(n, m, d, k, dots, layout):
     i, dd = ekh.knn(Xg, Yg, k, max_chunk_dots=dots)
     i, dd = host(i), host(dd)
     check_knn(X, Y, k, i, dd, rescored=True)
-    small = 256 * p["tile_rows"] * m  # 256 tiles per chunk: fewer than one round
+    small = 64 * p["tile_rows"] * m  # 64 tiles per chunk: fewer than one round of a chunk's share
     q = ekh.knn_plan(n, m, d, k, small)
     assert q["body_tiles"] == 0 and q["last_body_tiles"] == 0, q
     i2, d2 = ekh.knn(Xg, Yg, k, max_chunk_dots=small)
