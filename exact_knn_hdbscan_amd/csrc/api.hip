@@ -116,6 +116,7 @@ struct ChunkPlan {
 
 constexpr int64_t kMaxLd = int64_t(1) << 25;
 constexpr int64_t kMinTilesPerSplit = 4;
+constexpr int64_t kMaxSplits = 1024;     // a few query tiles against a long database fill the chip
 constexpr int64_t kCUs = 256;             // MI355X compute units (fixed, so that a workspace
                                           // query and the run always plan alike)
 constexpr int64_t kLdsPerCu = 160 * 1024;
@@ -142,7 +143,7 @@ int64_t split_cost(const KnnPlan &p, int64_t q, int64_t s) {
 }
 
 int best_splits(const KnnPlan &p, int64_t q, int64_t *cost) {
-    const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(64, p.tiles / kMinTilesPerSplit));
+    const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(kMaxSplits, p.tiles / kMinTilesPerSplit));
     int64_t best_s = 1, best = -1;
     for (int64_t s = 1; s <= smax; ++s) {
         const int64_t c = split_cost(p, q, s);

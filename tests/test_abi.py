@@ -96,7 +96,7 @@ def test_knn_plan_invariants_and_workspace(lib):
         for r, b, s in ((rows, body, splits), (last, lbody, lsplits)):
             q = -(-r // qt)
             assert b % slots == 0 and 0 <= b < q or b == 0
-            assert 1 <= s <= max(1, min(64, tiles // 4))
+            assert 1 <= s <= max(1, min(1024, tiles // 4))
             if b:
                 assert s > 1  # whole tiles only pay off when the rest is split
             # the split scratch fits the workspace (8-byte entries)

@@ -156,6 +156,19 @@ def test_knn_query_tiles_fill_whole_rounds():
     check_knn(X, Y, k, host(i), host(dd), rescored=True)
 
 
+def test_knn_few_queries_long_database():
+    """200 queries against 2,000,000 points: two query tiles, so the database
+    is split 384 ways (768 workgroups) and the merge combines 384 lists a row."""
+    n, m, d, k = 200, 2_000_000, 16, 10
+    p = ekh.knn_plan(n, m, d, k)
+    assert p["splits"] > 64, p
+    X = datagen.gaussian_mixture(n, d, 5, seed=31)
+    Y = datagen.gaussian_mixture(m, d, 50, seed=32)
+    say("knn n=%d m=%d: %s" % (n, m, p))
+    i, dd = ekh.knn(dev(X), dev(Y), k)
+    check_knn(X, Y, k, host(i), host(dd), rescored=True)
+
+
 def test_knn_repeatable():
     X = datagen.spike_clips(3000, 8, seed=4)
     Xg = dev(X)
