@@ -231,7 +231,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sections", action="store_true", help="skip the ekh_knn section workloads")
     ap.add_argument("--pmc-probe", action="store_true",
-                    help="for counter runs: one plain copy of COPY_BYTES (calibration) and one pass of the path")
+                    help="for counter runs: one plain copy of COPY_BYTES (calibration), one pass of the path, and "
+                         "(unless --no-sections) one ekh_knn call on each section workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -270,7 +271,17 @@ def main():
         del src, dst
         step()
         torch.cuda.synchronize()
-        print("pmc probe done: copy of %d bytes, one pass of %s" % (COPY_BYTES, args.workload), flush=True)
+        print("pmc probe: copy of %d bytes, one pass of %s" % (COPY_BYTES, args.workload), flush=True)
+        if not args.no_sections:
+            # one ekh_knn call on each section workload (their kernels in the same counter run)
+            for name in ("ks4_section_50000x102", "wide_section_200000x200"):
+                swl = datagen.make(name)
+                Xs, Ys = torch.from_numpy(swl["X"]).to(dev), torch.from_numpy(swl["Y"]).to(dev)
+                ekh.knn(Xs, Ys, swl["k"], max_chunk_dots=swl.get("max_chunk_bytes", 0) // 4)
+                torch.cuda.synchronize()
+                print("pmc probe: one ekh_knn call on %s" % name, flush=True)
+                del Xs, Ys
+        print("pmc probe done", flush=True)
         return
 
     for _ in range(args.warmup):

@@ -88,13 +88,23 @@ struct TimedLaunch {
         if (hipEventCreate(&rec.e0) != hipSuccess || hipEventCreate(&rec.e1) != hipSuccess) return;
         on = hipEventRecord(rec.e0, s) == hipSuccess;
     }
-    void done() {
-        if (!on) return;
+    // returns the record's position (for timer_set_flop), or -1 when the timer is off
+    int64_t done() {
+        if (!on) return -1;
         hipEventRecord(rec.e1, s);
         std::lock_guard<std::mutex> lk(g_tmu);
         g_trecs.push_back(rec);
+        return (int64_t)g_trecs.size() - 1;
     }
 };
+
+// Sets the algorithmic flop of a recorded launch whose work the host learns only
+// later (the Boruvka scan: the active points are counted on the device).
+void timer_set_flop(int64_t pos, double flop) {
+    if (pos < 0) return;
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (pos < (int64_t)g_trecs.size()) g_trecs[(size_t)pos].flop = flop;
+}
 
 // ---- kNN planning -----------------------------------------------------------
 struct KnnPlan {
@@ -189,18 +199,8 @@ int64_t scan_groups_per_cu(int QM) {
     return by_lds < want ? (by_lds < 1 ? 1 : by_lds) : want;
 }
 
-// Database splits of one scan launch over q query tiles: as many as fill one
-// round of resident workgroups (the scan has no list warm-up, and a second,
-// partly filled round would cost a whole round), at least kMinTilesPerSplit
-// tiles each; one split when the query tiles alone fill a round.
-int scan_splits(int QM, int64_t q, int64_t tiles) {
-    const int64_t slots = kCUs * scan_groups_per_cu(QM);
-    int64_t sp = q < slots ? slots / q : 1;
-    sp = std::min<int64_t>(sp, std::max<int64_t>(1, tiles / kMinTilesPerSplit));
-    return (int)std::max<int64_t>(1, std::min<int64_t>(sp, 65535));
-}
-
-KnnPlan plan_knn(int64_t n, int64_t m, int d, int k, int64_t max_chunk_dots) {
+// max_conc: chunks in flight at most (1: everything on the caller's stream)
+KnnPlan plan_knn(int64_t n, int64_t m, int d, int k, int64_t max_chunk_dots, int max_conc = kChunkStreams) {
     KnnPlan p{};
     p.K = pick_k(k);
     p.QM = pick_qm(d);
@@ -217,7 +217,7 @@ KnnPlan plan_knn(int64_t n, int64_t m, int d, int k, int64_t max_chunk_dots) {
     // share of the resident workgroups: fewer database splits, hence fewer
     // list warm-ups per query, than one chunk filling the chip alone.
     const int64_t nchunks = (n + p.rows - 1) / p.rows;
-    p.conc = (int)std::min<int64_t>(kChunkStreams, nchunks);
+    p.conc = (int)std::max<int64_t>(1, std::min<int64_t>(std::min(kChunkStreams, max_conc), nchunks));
     p.slots = std::max<int64_t>(1, kCUs * knn_groups_per_cu(p.K, p.QM) / p.conc);
     p.warm = kWarmupWork * 32 / (4 * p.chunks * p.TR); // measured at 32-row tiles
     p.part_entries = chunk_part_entries(p, p.rows);
@@ -295,22 +295,41 @@ int stream_wait(hipStream_t waiter, hipStream_t from) {
 // Chunk c runs on stream c mod p.conc (0 = the caller's) with its own split
 // scratch; the other streams start after the norms and the caller's stream
 // waits for all of them before anything that reads the outputs.
+// core_direct (core mode): the core distances are recomputed by direct
+// differences from the final lists (knn_core_kernel), which needs bt.
 int run_knn(const KnnPlan &p, const float *X, int64_t ldx, int64_t n, const float *Y, int64_t ldy, int64_t m, int d,
             bool self, int out_mode, int k_out, int min_samples, int32_t *out_idx, float *out_dist, float *out_core,
-            float *nx, float *ny, Entry *part, float *bt, hipStream_t s) {
+            float *nx, float *ny, Entry *part, float *bt, hipStream_t s, bool core_direct = false) {
     EKH_HIP(launch_norms(X, ldx, n, d, nx, s));
     if (!self) EKH_HIP(launch_norms(Y, ldy, m, d, ny, s));
-    if (out_mode == kOutKnn) EKH_HIP(launch_point_major(Y, ldy, m, d, padded_dim(d), bt, s));
+    if (out_mode == kOutKnn || core_direct) EKH_HIP(launch_point_major(Y, ldy, m, d, padded_dim(d), bt, s));
     hipStream_t cs[kChunkStreams] = {s};
+    int forked = 1; // streams in use: the caller's, then those made to wait for it
+    // After the fork every exit, an error included, first makes the caller's
+    // stream wait for the other streams: the caller may free the workspace and
+    // the outputs as soon as its own stream has passed the call's work.
+    auto join = [&](int rc) {
+        for (int i = 1; i < forked; ++i) {
+            const int r = stream_wait(s, cs[i]);
+            if (rc == EKH_OK) rc = r;
+        }
+        return rc;
+    };
     if (p.conc > 1) {
         hipStream_t extra[kChunkStreams - 1];
         int rc;
         if ((rc = chunk_streams(s, extra)) != EKH_OK) return rc;
         for (int i = 1; i < p.conc; ++i) {
             cs[i] = extra[i - 1];
-            if ((rc = stream_wait(cs[i], s)) != EKH_OK) return rc;
+            if ((rc = stream_wait(cs[i], s)) != EKH_OK) return join(rc);
+            forked = i + 1;
         }
     }
+#define EKH_HIP_JOIN(call)                                                                                             \
+    do {                                                                                                               \
+        hipError_t e_ = (call);                                                                                        \
+        if (e_ != hipSuccess) return join(fail(EKH_EHIP, "%s failed: %s", #call, hipGetErrorString(e_)));            \
+    } while (0)
     int64_t chunk = 0;
     for (int64_t q0 = 0; q0 < n; q0 += p.rows, ++chunk) {
         const int lane = (int)(chunk % p.conc);
@@ -340,18 +359,19 @@ int run_knn(const KnnPlan &p, const float *X, int64_t ldx, int64_t n, const floa
         a.out_core = out_core;
         a.out_mode = out_mode;
         TimedLaunch tl(0, 2.0 * d * (double)a.nq * (double)m, cstream);
-        EKH_HIP(launch_knn_tile(p.K, p.QM, a, cstream));
+        EKH_HIP_JOIN(launch_knn_tile(p.K, p.QM, a, cstream));
         tl.done();
         if (cp.splits > 1) {
             // the split tiles' rows only
             a.q0 += cp.body_q * p.QT;
             a.nq -= cp.body_q * p.QT;
-            EKH_HIP(launch_knn_merge(p.K, a, cstream));
+            EKH_HIP_JOIN(launch_knn_merge(p.K, a, cstream));
         }
     }
-    for (int i = 1; i < p.conc; ++i) {
-        int rc;
-        if ((rc = stream_wait(s, cs[i])) != EKH_OK) return rc;
+#undef EKH_HIP_JOIN
+    {
+        const int rc = join(EKH_OK);
+        if (rc != EKH_OK) return rc;
     }
     if (out_mode == kOutKnn) {
         // reported distances, over all rows at once (no rows x m scratch involved)
@@ -368,6 +388,21 @@ int run_knn(const KnnPlan &p, const float *X, int64_t ldx, int64_t n, const floa
         a.Bt = bt;
         a.dp = padded_dim(d);
         EKH_HIP(launch_knn_rescore(p.K, a, s));
+    } else if (core_direct) {
+        KnnArgs a{};
+        a.Q = X;
+        a.ldq = ldx;
+        a.q0 = 0;
+        a.nq = n;
+        a.m = m;
+        a.d = d;
+        a.k_out = k_out;
+        a.min_samples = min_samples;
+        a.out_idx = out_idx;
+        a.out_core = out_core;
+        a.Bt = bt;
+        a.dp = padded_dim(d);
+        EKH_HIP(launch_knn_core(p.K, a, s));
     }
     return EKH_OK;
 }
@@ -377,6 +412,7 @@ struct MstWs {
     float *nrm;
     int32_t *comp, *parent, *act;
     uint8_t *resolved;
+    float *lbound;
     uint64_t *best, *cmin1, *cc;
     uint32_t *cmin2, *compW;
     int32_t *e_lo, *e_hi;
@@ -391,6 +427,7 @@ struct MstWs {
     float *knn_nx;
     Entry *knn_part;
     float *xs; // points outside the largest component, feature-major [d, <= n / 2]
+    float *pm; // point-major copy [n, padded_dim(d)] for the reported edge weights
 };
 
 size_t carve_mst(Carver &c, int64_t n, int d, int ms, bool with_nb, MstWs &w) {
@@ -400,6 +437,7 @@ size_t carve_mst(Carver &c, int64_t n, int d, int ms, bool with_nb, MstWs &w) {
     w.parent = c.take<int32_t>(n);
     w.act = c.take<int32_t>(n);
     w.resolved = c.take<uint8_t>(n);
+    w.lbound = c.take<float>(n);
     w.best = c.take<uint64_t>(n);
     w.cmin1 = c.take<uint64_t>(n);
     w.cmin2 = c.take<uint32_t>(n);
@@ -421,6 +459,7 @@ size_t carve_mst(Carver &c, int64_t n, int d, int ms, bool with_nb, MstWs &w) {
     // in the edge sort's u32 scratch (sb, sc, sd, sa), norms and core distances
     // in s64a -- all idle until the final sort
     w.xs = c.take<float>((size_t)d * (size_t)(n / 2 + 1));
+    w.pm = c.take<float>((size_t)n * (size_t)padded_dim(d));
     w.nbr_idx = nullptr;
     w.nbr_d2 = nullptr;
     w.knn_nx = nullptr;
@@ -508,9 +547,10 @@ size_t ekh_core_workspace_bytes(int64_t n, int32_t d, int32_t min_samples) {
     if (n < 1 || d < 1 || d > EKH_MAX_DIM || min_samples < 1 || min_samples + 1 > EKH_MAX_K) return 0;
     const KnnPlan p = plan_knn(n, n, d, min_samples + 1, 0);
     Carver c(nullptr);
-    float *nx, *ny;
+    float *nx, *ny, *bt;
     Entry *part;
-    return knn_ws(p, n, n, true, c, &nx, &ny, &part);
+    int32_t *idx;
+    return knn_ws(p, n, n, true, c, &nx, &ny, &part, &idx, min_samples + 1, &bt, d);
 }
 
 int ekh_core_distances(const float *X, int64_t ldx, int64_t n, int32_t d, int32_t min_samples, float *out_core,
@@ -528,11 +568,12 @@ int ekh_core_distances(const float *X, int64_t ldx, int64_t n, int32_t d, int32_
     const int K = min_samples + 1;
     const KnnPlan p = plan_knn(n, n, d, K, 0);
     Carver c(ws);
-    float *nx, *ny;
+    float *nx, *ny, *bt;
     Entry *part;
-    knn_ws(p, n, n, true, c, &nx, &ny, &part);
-    return run_knn(p, X, ldx, n, X, ldx, n, d, true, kOutCore, K, min_samples, out_nbr_idx, out_nbr_d2, out_core, nx,
-                   nx, part, nullptr, (hipStream_t)stream);
+    int32_t *idx_scratch;
+    knn_ws(p, n, n, true, c, &nx, &ny, &part, &idx_scratch, K, &bt, d);
+    return run_knn(p, X, ldx, n, X, ldx, n, d, true, kOutCore, K, min_samples, out_nbr_idx ? out_nbr_idx : idx_scratch,
+                   out_nbr_d2, out_core, nx, nx, part, bt, (hipStream_t)stream, true);
 }
 
 size_t ekh_mst_workspace_bytes(int64_t n, int32_t d, int32_t min_samples, int with_neighbours) {
@@ -591,6 +632,7 @@ int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const flo
     st.parent = w.parent;
     st.act = w.act;
     st.resolved = w.resolved;
+    st.lbound = w.lbound;
     st.best = w.best;
     st.cmin1 = w.cmin1;
     st.cmin2 = w.cmin2;
@@ -604,12 +646,28 @@ int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const flo
 
     const int use_nb = (flags & EKH_MST_NO_NEIGHBOUR_EDGES) ? 0 : 1;
     const int use_bound = (flags & EKH_MST_NO_COMPONENT_BOUND) ? 0 : 1;
+    const bool giant_scans = !(flags & EKH_MST_FULL_SCANS);
     const int QM = pick_qm(d);
     const int TR = tile_rows(QM);
-    const int QT = scan_query_tile(QM);
     const int64_t tiles = (n + TR - 1) / TR;
+    const int64_t scan_grid = kCUs * scan_groups_per_cu(QM); // one round of resident workgroups
     const int cap = std::max(1, ceil_log2(n));
 
+    ScanArgs sa{};
+    sa.X = X;
+    sa.ldx = ldx;
+    sa.n = n;
+    sa.nrm = w.nrm;
+    sa.core = core;
+    sa.comp = w.comp;
+    sa.compW = w.compW;
+    sa.best = w.best;
+    sa.d = d;
+    sa.chunks = feature_chunks(d);
+
+    // One host read-back per round, after the merge: the scans size their work
+    // from the device-side active counts, and the largest component of the next
+    // round (size << 32 | label) is counted before the read-back.
     EKH_HIP(bv_init(st, s));
     int64_t ncomp = n;
     int round = 0;
@@ -619,61 +677,37 @@ int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const flo
             return fail(EKH_EINTERNAL, "Boruvka did not finish in %d rounds (%lld components left)", cap,
                         (long long)ncomp);
         const auto t0 = std::chrono::steady_clock::now();
+        // the largest component, when it holds >= n / 2 points: its active points
+        // are scanned only against the points outside it (a cheapest edge leaves
+        // the component)
+        const int64_t sg = (int64_t)(h.giant >> 32), ns = n - sg;
+        const int32_t g = (int32_t)(uint32_t)h.giant;
+        const int split_giant = round > 0 && giant_scans && sg * 2 >= n && ns >= 1 ? 1 : 0;
         EKH_HIP(bv_reset_counters(st, s));
-        // after the first round (all singletons), find the largest component:
-        // when it holds >= n / 2 points its active points are scanned only
-        // against the points outside it (a cheapest edge leaves the component)
-        const int split_giant = round > 0 && !(flags & EKH_MST_FULL_SCANS) ? 1 : 0;
-        if (split_giant) EKH_HIP(bv_giant(st, s));
         EKH_HIP(bv_candidates(st, use_nb, use_bound, s));
         EKH_HIP(bv_select_active(st, use_bound, split_giant, s));
-        EKH_HIP(hipMemcpyAsync(&h, w.ctr, sizeof h, hipMemcpyDeviceToHost, s));
-        EKH_HIP(hipStreamSynchronize(s));
-        const int64_t nact = h.n_active, nact_g = h.n_active_g;
-        ScanArgs sa{};
-        sa.X = X;
-        sa.ldx = ldx;
-        sa.n = n;
-        sa.nrm = w.nrm;
-        sa.core = core;
-        sa.comp = w.comp;
-        sa.compW = w.compW;
-        sa.best = w.best;
-        sa.d = d;
-        sa.chunks = feature_chunks(d);
-        if (nact > 0) {
-            sa.Xb = X;
-            sa.ldb = ldx;
-            sa.nb = n;
-            sa.nrm_b = w.nrm;
-            sa.core_b = core;
-            sa.comp_b = w.comp;
-            sa.orig = nullptr;
-            sa.act = w.act;
-            sa.nact = nact;
-            sa.tiles = tiles;
-            sa.splits = scan_splits(QM, (nact + QT - 1) / QT, tiles);
-            TimedLaunch tl(1, 2.0 * d * (double)nact * (double)n, s);
-            EKH_HIP(launch_scan_tile(QM, sa, s));
-            tl.done();
-        }
-        if (nact_g > 0) {
-            const int64_t sg = (int64_t)(h.giant >> 32), ns = n - sg;
-            const int32_t g = (int32_t)(uint32_t)h.giant;
-            if (sg * 2 < n || ns < 1)
-                return fail(EKH_EINTERNAL, "round %d: largest component %lld of %lld", round, (long long)sg,
-                            (long long)n);
+        sa.Xb = X;
+        sa.ldb = ldx;
+        sa.nb = n;
+        sa.nrm_b = w.nrm;
+        sa.core_b = core;
+        sa.comp_b = w.comp;
+        sa.orig = nullptr;
+        sa.act = w.act;
+        sa.nact = &w.ctr->n_active;
+        sa.tiles = tiles;
+        TimedLaunch tl(1, 0.0, s);
+        EKH_HIP(launch_scan_tile(QM, sa, scan_grid, s));
+        const int64_t t_main = tl.done();
+        int64_t t_giant = -1;
+        if (split_giant) {
             int32_t *orig = reinterpret_cast<int32_t *>(w.sb);
             int32_t *comp_s = reinterpret_cast<int32_t *>(w.sc);
             float *nrm_s = reinterpret_cast<float *>(w.s64a), *core_s = nrm_s + (n / 2 + 1);
+            // both do nothing when no active point of the component was listed
             EKH_HIP(bv_complement(st, g, orig, s));
-            EKH_HIP(hipMemcpyAsync(&h, w.ctr, sizeof h, hipMemcpyDeviceToHost, s));
-            EKH_HIP(hipStreamSynchronize(s));
-            if ((int64_t)h.n_comp_g != ns)
-                return fail(EKH_EINTERNAL, "round %d: %u points outside the largest component, expected %lld", round,
-                            h.n_comp_g, (long long)ns);
-            EKH_HIP(bv_gather_points(X, ldx, d, orig, ns, w.nrm, core, w.comp, w.xs, nrm_s, core_s, comp_s, s));
-            const int64_t tiles_g = (ns + TR - 1) / TR;
+            EKH_HIP(bv_gather_points(X, ldx, d, orig, ns, w.nrm, core, w.comp, w.xs, nrm_s, core_s, comp_s,
+                                     &w.ctr->n_comp_g, &w.ctr->n_active_g, s));
             sa.Xb = w.xs;
             sa.ldb = ns;
             sa.nb = ns;
@@ -682,21 +716,27 @@ int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const flo
             sa.comp_b = comp_s;
             sa.orig = orig;
             sa.act = st.act_g;
-            sa.nact = nact_g;
-            sa.tiles = tiles_g;
-            sa.splits = scan_splits(QM, (nact_g + QT - 1) / QT, tiles_g);
-            TimedLaunch tl(1, 2.0 * d * (double)nact_g * (double)ns, s);
-            EKH_HIP(launch_scan_tile(QM, sa, s));
-            tl.done();
+            sa.nact = &w.ctr->n_active_g;
+            sa.tiles = (ns + TR - 1) / TR;
+            TimedLaunch tg(1, 0.0, s);
+            EKH_HIP(launch_scan_tile(QM, sa, scan_grid, s));
+            t_giant = tg.done();
         }
         EKH_HIP(bv_component_min(st, s));
         EKH_HIP(bv_select_edges(st, s));
         const int jumps = ceil_log2(ncomp) + 1;
         for (int j = 0; j < jumps; ++j) EKH_HIP(bv_jump(st, s));
         EKH_HIP(bv_relabel(st, s));
+        if (giant_scans) EKH_HIP(bv_giant(st, s)); // for the next round
         EKH_HIP(hipMemcpyAsync(&h, w.ctr, sizeof h, hipMemcpyDeviceToHost, s));
         EKH_HIP(hipStreamSynchronize(s));
+        const int64_t nact = h.n_active, nact_g = split_giant ? h.n_active_g : 0;
+        timer_set_flop(t_main, 2.0 * d * (double)nact * (double)n);
+        timer_set_flop(t_giant, 2.0 * d * (double)nact_g * (double)ns);
         if (h.n_missing) return fail(EKH_EINTERNAL, "round %d: %u components found no outgoing edge", round, h.n_missing);
+        if (split_giant && nact_g > 0 && (int64_t)h.n_comp_g != ns)
+            return fail(EKH_EINTERNAL, "round %d: %u points outside the largest component, expected %lld", round,
+                        h.n_comp_g, (long long)ns);
         const int64_t before = ncomp;
         ncomp = h.n_roots;
         if (ncomp >= before || ncomp < 1)
@@ -716,6 +756,9 @@ int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const flo
     if (stats) stats->rounds = round;
     if ((int64_t)h.n_edges != n - 1)
         return fail(EKH_EINTERNAL, "tree has %u edges, expected %lld", h.n_edges, (long long)(n - 1));
+    // each edge's reported weight by direct differences, then the (w, lo, hi) order
+    EKH_HIP(launch_point_major(X, ldx, n, d, padded_dim(d), w.pm, s));
+    EKH_HIP(bv_edge_weights(w.pm, padded_dim(d), core, w.e_lo, w.e_hi, n - 1, n, w.e_w, s));
     EKH_HIP(edge_sort(w.e_lo, w.e_hi, w.e_w, n - 1, w.sort_tmp, w.sort_tmp_bytes, w.sa, w.sb, w.sc, w.sd, w.s64a,
                       w.s64b, out_lo, out_hi, out_w, s));
     return EKH_OK;

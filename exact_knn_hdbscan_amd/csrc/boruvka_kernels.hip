@@ -39,6 +39,8 @@ hipError_t bv_init(const BvState &st, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The per-round counters; ctr->giant (set at the end of the previous round by
+// bv_giant) is kept.
 __global__ void bv_reset_counters_kernel(BvCounters *c) {
     if (threadIdx.x == 0) {
         c->n_active = 0;
@@ -48,7 +50,6 @@ __global__ void bv_reset_counters_kernel(BvCounters *c) {
         c->n_missing = 0;
         c->n_active_g = 0;
         c->n_comp_g = 0;
-        c->giant = 0;
     }
 }
 
@@ -127,13 +128,22 @@ __device__ __forceinline__ void lds_count(bool pred, uint32_t *cnt) {
 }
 
 // Neighbour-edge candidates ("Exact shortcuts", first item).  For point a with
-// list entries b (self included, ascending (D2, index)):
+// list entries b (self included, ascending (D2, index)), last entry at distance
+// D_last:
 //  - every entry in another component is a real edge W = max(core_a, core_b, D);
 //    the smallest (W, b) is a's best list edge and feeds the component bound;
-//  - W >= core_a for every edge of a, so a list edge with W == core_a is a's
-//    cheapest edge provided the list holds every point within core_a, i.e. the
-//    last entry lies strictly farther than core_a (then the lowest qualifying
-//    index is in the list too).  Such a point is resolved without a scan.
+//  - the list holds every point closer than D_last (it is the K nearest under
+//    (D2, index), with the same D2 the scan computes), so every edge of a to a
+//    point outside the list weighs at least max(core_a, D_last).  A best list
+//    edge lighter than D_last is therefore a's cheapest edge, and a is resolved
+//    without a scan.  This contains the page's case (W == core_a with the last
+//    entry, the extra (min_samples + 1)-th neighbour, strictly farther than
+//    core_a) and extends it to any best list edge below D_last;
+//  - a point that is not resolved has no edge lighter than
+//    lb = max(core_a, D_last) (its list edges are >= the best one >= D_last):
+//    lb goes to the activity pass, which compares it with the component bound.
+// With use_nb = 0 neither list argument is used (lb = core_a, which bounds
+// every edge of a by the definition of W).
 __global__ __launch_bounds__(kBigBs) void bv_candidates_kernel(BvState st, int use_nb, int use_bound) {
     __shared__ LdsMinTable<uint32_t> tab;
     __shared__ uint32_t n_res;
@@ -162,10 +172,11 @@ __global__ __launch_bounds__(kBigBs) void bv_candidates_kernel(BvState st, int u
                 nb = key < nb ? key : nb;
             }
         }
-        const bool complete = sqrt_rn(last_d2 > 0.f ? last_d2 : 0.f) > corea;
-        res = use_nb && complete && nb != kNoEdge && (uint32_t)(nb >> 32) == __float_as_uint(corea);
+        const float dlast = sqrt_rn(last_d2 > 0.f ? last_d2 : 0.f);
+        res = use_nb && nb != kNoEdge && __uint_as_float((uint32_t)(nb >> 32)) < dlast;
         st.best[a] = nb;
         st.resolved[a] = res ? 1 : 0;
+        st.lbound[a] = use_nb ? fmaxf(corea, dlast) : corea;
         bnd = use_bound && nb != kNoEdge;
         wb = (uint32_t)(nb >> 32);
         cb = ca;
@@ -183,10 +194,11 @@ hipError_t bv_candidates(const BvState &st, int use_nb, int use_bound, hipStream
 }
 
 // Active points ("Exact shortcuts", second item): not resolved, and not skipped
-// by the component bound (a point whose core distance exceeds the lightest
-// known edge out of its component cannot supply a lighter one; on equality it
-// still could, through a lower index, so it stays active).  Compacted into
-// st.act with one atomic per wave.
+// by the component bound (a point whose lower bound lb (core_a, or
+// max(core_a, D_last) from its list, see bv_candidates_kernel) exceeds the
+// lightest known edge out of its component cannot supply a lighter one; on
+// equality it still could, through a lower index, so it stays active).
+// Compacted into st.act with one atomic per wave.
 // Appends the lanes with `take` to list[] at positions claimed with one
 // atomic per wave on *count.
 __device__ __forceinline__ void wave_append(bool take, int32_t value, uint32_t *count, int32_t *list) {
@@ -212,7 +224,7 @@ __global__ __launch_bounds__(kBigBs) void bv_select_active_kernel(BvState st, in
     bool act = false, skip = false, in_g = false;
     if (a < st.n && !st.resolved[a]) {
         const int32_t c = st.comp[a];
-        skip = use_bound && st.core[a] > __uint_as_float(st.compW[c]);
+        skip = use_bound && st.lbound[a] > __uint_as_float(st.compW[c]);
         act = !skip;
         in_g = use_g && c == g;
     }
@@ -230,9 +242,11 @@ hipError_t bv_select_active(const BvState &st, int use_bound, int split_giant, h
 }
 
 // Size of every component (LDS-combined counts per label), then the largest
-// as size << 32 | label (ties to the larger label) in ctr->giant.
+// as size << 32 | label (ties to the larger label) in ctr->giant.  Run after a
+// round's relabel (csize is zero then), for the next round.
 __global__ __launch_bounds__(kBigBs) void bv_comp_sizes_kernel(BvState st) {
     __shared__ LdsMinTable<uint32_t, true> tab;
+    if (blockIdx.x == 0 && threadIdx.x == 0) st.ctr->giant = 0; // bv_giant_kernel, launched next, accumulates it
     tab.clear();
     __syncthreads();
     const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -266,9 +280,11 @@ hipError_t bv_giant(const BvState &st, hipStream_t s) {
 
 // The points outside component `giant`, listed in orig (ctr->n_comp_g of
 // them); one atomic per workgroup, waves placed by an LDS prefix.
+// Nothing to do when the round lists no active point of that component.
 __global__ __launch_bounds__(kBigBs) void bv_complement_kernel(BvState st, int32_t giant, int32_t *orig) {
     __shared__ uint32_t wcount[kBigBs / 64];
     __shared__ uint32_t base;
+    if (__hip_atomic_load(&st.ctr->n_active_g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) return;
     const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const bool out = a < st.n && st.comp[a] != giant;
     const uint64_t m = __ballot(out);
@@ -294,13 +310,26 @@ hipError_t bv_complement(const BvState &st, int32_t giant, int32_t *orig, hipStr
 }
 
 // Feature-major copy [d, ns] of the listed points with their norms, core
-// distances and labels (writes coalesced along the list).
+// distances and labels (writes coalesced along the list).  Only the first
+// *count (<= ns) list entries are read; with *gate == 0 nothing is done.
 __global__ __launch_bounds__(kBs) void bv_gather_points_kernel(const float *X, int64_t ldx, int d,
                                                                 const int32_t *orig, int64_t ns, const float *nrm,
                                                                 const float *core, const int32_t *comp, float *xs,
-                                                                float *nrm_s, float *core_s, int32_t *comp_s) {
+                                                                float *nrm_s, float *core_s, int32_t *comp_s,
+                                                                const uint32_t *count, const uint32_t *gate) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gate && __hip_atomic_load(gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) return;
+    const int64_t listed = count ? (int64_t)__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : ns;
     if (i >= ns) return;
+    if (i >= listed) {
+        // fewer points listed than the host sized the copy for (it reports the
+        // mismatch after the round): such rows carry the padding label and
+        // never form an edge
+        nrm_s[i] = INFINITY;
+        core_s[i] = INFINITY;
+        comp_s[i] = -1;
+        return;
+    }
     const int32_t p = orig[i];
     for (int f = 0; f < d; ++f) xs[(int64_t)f * ns + i] = X[(int64_t)f * ldx + p];
     nrm_s[i] = nrm[p];
@@ -310,10 +339,10 @@ __global__ __launch_bounds__(kBs) void bv_gather_points_kernel(const float *X, i
 
 hipError_t bv_gather_points(const float *X, int64_t ldx, int d, const int32_t *orig, int64_t ns, const float *nrm,
                             const float *core, const int32_t *comp, float *xs, float *nrm_s, float *core_s,
-                            int32_t *comp_s, hipStream_t s) {
+                            int32_t *comp_s, const uint32_t *count, const uint32_t *gate, hipStream_t s) {
     if (ns <= 0) return hipSuccess;
     hipLaunchKernelGGL(bv_gather_points_kernel, grid_for(ns, kBs), dim3(kBs), 0, s, X, ldx, d, orig, ns, nrm, core,
-                       comp, xs, nrm_s, core_s, comp_s);
+                       comp, xs, nrm_s, core_s, comp_s, count, gate);
     return hipGetLastError();
 }
 
@@ -430,6 +459,44 @@ __global__ void bv_relabel_kernel(BvState st) {
 
 hipError_t bv_relabel(const BvState &st, hipStream_t s) {
     hipLaunchKernelGGL(bv_relabel_kernel, grid_for(st.n, kBs), dim3(kBs), 0, s, st);
+    return hipGetLastError();
+}
+
+// Reported weight of every tree edge: max(core_lo, core_hi, D) with D by direct
+// differences, sqrt_rn(sum_f (x_lo,f - x_hi,f)^2) with fmaf in feature order,
+// from a point-major copy P [n, dp] (zero padding features add exact zeros).
+// The tree was chosen with the GEMM-form D (the value the candidate pass and
+// the scan share bit for bit); the two differ by its rounding only, which the
+// direct form does not carry.  Symmetric in (lo, hi) bit for bit.
+__global__ void bv_edge_weights_kernel(const float *__restrict__ P, int dp, const float *__restrict__ core,
+                                       const int32_t *__restrict__ lo, const int32_t *__restrict__ hi, int64_t ne,
+                                       int64_t n, float *__restrict__ w) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= ne) return;
+    const int32_t a = lo[i], b = hi[i];
+    if (a < 0 || a >= n || b < 0 || b >= n) { // cannot come from a finished tree
+        w[i] = INFINITY;
+        return;
+    }
+    const f4 *pa = reinterpret_cast<const f4 *>(P + (int64_t)a * dp);
+    const f4 *pb = reinterpret_cast<const f4 *>(P + (int64_t)b * dp);
+    float s = 0.f;
+    for (int f = 0; f < dp / 4; ++f) {
+        const f4 x = pa[f], y = pb[f];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float v = x[e] - y[e];
+            s = fmaf(v, v, s);
+        }
+    }
+    w[i] = fmaxf(fmaxf(core[a], core[b]), sqrt_rn(s));
+}
+
+hipError_t bv_edge_weights(const float *P, int dp, const float *core, const int32_t *lo, const int32_t *hi, int64_t ne,
+                           int64_t n, float *w, hipStream_t s) {
+    if (ne <= 0) return hipSuccess;
+    hipLaunchKernelGGL(bv_edge_weights_kernel, grid_for(ne, kBs), dim3(kBs), 0, s, P, dp, core, lo, hi, ne, n, w);
     return hipGetLastError();
 }
 

@@ -71,7 +71,8 @@ struct __align__(8) Entry {
 // ---- kNN -----------------------------------------------------------------
 enum KnnOut : int {
     kOutKnn = 1,     // final: out_idx / out_dist, first k entries
-    kOutCore = 2,    // final: core = sqrt(d2[ms-1]); optional nbr lists (K = ms + 1)
+    kOutCore = 2,    // final: nbr lists (K = ms + 1) and core = sqrt(d2[ms-1]) (GEMM form; replaced by the
+                     // direct-difference value of knn_core_kernel where the caller asks for core distances)
 };
 
 struct KnnArgs {
@@ -106,6 +107,7 @@ hipError_t launch_norms(const float *X, int64_t ldx, int64_t n, int d, float *ou
 hipError_t launch_knn_tile(int K, int QM, const KnnArgs &a, hipStream_t s);
 hipError_t launch_knn_merge(int K, const KnnArgs &a, hipStream_t s);
 hipError_t launch_knn_rescore(int K, const KnnArgs &a, hipStream_t s);
+hipError_t launch_knn_core(int K, const KnnArgs &a, hipStream_t s);
 hipError_t launch_point_major(const float *B, int64_t ldb, int64_t m, int d, int dp, float *Bt, hipStream_t s);
 
 // ---- Boruvka ---------------------------------------------------------------
@@ -142,15 +144,19 @@ struct ScanArgs {
     const int32_t *orig;  // NULL: row j is point j
     const uint32_t *compW; // bound W bits per component (kInfBits = none)
     const int32_t *act;   // active points
-    int64_t nact;
+    const uint32_t *nact; // their number, read on the device (set by the activity pass)
     uint64_t *best;       // per-point best key (W bits << 32 | partner), atomicMin
     int d;
     int chunks;
-    int splits;
     int64_t tiles;        // database tiles
 };
+// Database tiles per split of the scan, at least (the split count is chosen on
+// the device, where the number of active points is known).
+constexpr int64_t kScanMinTilesPerSplit = 4;
 
-hipError_t launch_scan_tile(int QM, const ScanArgs &a, hipStream_t s);
+// grid: workgroups launched (normally one round of resident ones); they walk
+// the (query tile, database split) items the device-side count implies
+hipError_t launch_scan_tile(int QM, const ScanArgs &a, int64_t grid, hipStream_t s);
 
 struct BvState {
     int64_t n;
@@ -163,6 +169,7 @@ struct BvState {
     int32_t *parent;
     int32_t *act;
     uint8_t *resolved;
+    float *lbound;     // per point: no edge of it is lighter (from its core and list)
     uint64_t *best;
     uint64_t *cmin1;   // per component (W bits << 32 | lo)
     uint32_t *cmin2;   // per component hi
@@ -183,11 +190,15 @@ hipError_t bv_giant(const BvState &st, hipStream_t s);
 hipError_t bv_complement(const BvState &st, int32_t giant, int32_t *orig, hipStream_t s);
 hipError_t bv_gather_points(const float *X, int64_t ldx, int d, const int32_t *orig, int64_t ns, const float *nrm,
                             const float *core, const int32_t *comp, float *xs, float *nrm_s, float *core_s,
-                            int32_t *comp_s, hipStream_t s);
+                            int32_t *comp_s, const uint32_t *count, const uint32_t *gate, hipStream_t s);
 hipError_t bv_component_min(const BvState &st, hipStream_t s);
 hipError_t bv_select_edges(const BvState &st, hipStream_t s);
 hipError_t bv_jump(const BvState &st, hipStream_t s);
 hipError_t bv_relabel(const BvState &st, hipStream_t s);
+
+// reported edge weights by direct differences (P: point-major copy [n, dp])
+hipError_t bv_edge_weights(const float *P, int dp, const float *core, const int32_t *lo, const int32_t *hi, int64_t ne,
+                           int64_t n, float *w, hipStream_t s);
 
 // final edge order (W, lo, hi)
 size_t edge_sort_temp_bytes(int64_t ne);

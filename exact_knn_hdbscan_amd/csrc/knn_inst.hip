@@ -40,6 +40,12 @@ template <> hipError_t launch_knn_rescore_k<EKH_KNN_K>(const KnnArgs &a, hipStre
     return hipGetLastError();
 }
 
+template <> hipError_t launch_knn_core_k<EKH_KNN_K>(const KnnArgs &a, hipStream_t s) {
+    const int bs = 128;
+    hipLaunchKernelGGL(knn_core_kernel<EKH_KNN_K>, dim3((unsigned)((a.nq + bs - 1) / bs)), dim3(bs), 0, s, a);
+    return hipGetLastError();
+}
+
 template <> hipError_t launch_knn_merge_k<EKH_KNN_K>(const KnnArgs &a, hipStream_t s) {
     const int bs = 256;
     const int64_t threads = a.nq * kMergeLanes;

@@ -630,8 +630,66 @@ template <int K> __global__ void knn_rescore_kernel(KnnArgs a) {
     }
 }
 
+// Core distances by direct differences: for each row, the squared distance to
+// every entry of its final list as sum_f (q_f - y_f)^2 (fmaf in feature order,
+// no cancellation error), and core = sqrt_rn of the min_samples-th smallest of
+// them (ties by list position).  The list itself was selected with the
+// GEMM-form D2; its first min_samples + 1 entries hold every point within the
+// true rank-min_samples distance unless the GEMM form's rounding exceeds the
+// gap between ranks min_samples and min_samples + 2, so this is the float32
+// value of the exact core distance ("HDBSCAN" page, "The algorithm on the
+// device": the distance to the min_samples-th neighbour, the point itself
+// counted).  Same access pattern as knn_rescore_kernel: one thread per row,
+// the neighbours' features from the point-major copy Bt.
+template <int K> __global__ void knn_core_kernel(KnnArgs a) {
+    const int64_t ql = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (ql >= a.nq) return;
+    const int64_t q = a.q0 + ql;
+    int32_t jr[K];
+    bool ok[K];
+    float s[K];
+#pragma unroll
+    for (int t = 0; t < K; ++t) {
+        const int32_t j = t < a.k_out ? a.out_idx[q * a.k_out + t] : -1;
+        ok[t] = t < a.k_out && j >= 0 && j < a.m;
+        jr[t] = ok[t] ? j : 0; // never used as an address out of range
+        s[t] = 0.f;
+    }
+    for (int f = 0; f < a.dp; f += 4) {
+        float qv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qv[e] = f + e < a.d ? a.Q[(int64_t)(f + e) * a.ldq + q] : 0.f;
+#pragma unroll
+        for (int t = 0; t < K; ++t) {
+            if (t < a.k_out) {
+                const f4 y = *reinterpret_cast<const f4 *>(a.Bt + (int64_t)jr[t] * a.dp + f);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float v = qv[e] - y[e];
+                    s[t] = fmaf(v, v, s[t]);
+                }
+            }
+        }
+    }
+    // the min_samples-th smallest (rank min_samples - 1 from 0) of the k_out values
+    float c2 = 0.f;
+#pragma unroll
+    for (int t = 0; t < K; ++t) {
+        if (!ok[t]) s[t] = INFINITY;
+    }
+#pragma unroll
+    for (int t = 0; t < K; ++t) {
+        int r = 0;
+#pragma unroll
+        for (int u = 0; u < K; ++u) r += (u < a.k_out && (s[u] < s[t] || (s[u] == s[t] && u < t))) ? 1 : 0;
+        if (t < a.k_out && r == a.min_samples - 1) c2 = s[t];
+    }
+    a.out_core[q] = sqrt_rn(c2);
+}
+
 template <int K> hipError_t launch_knn_tile_k(int QM, const KnnArgs &a, hipStream_t s);
 template <int K> hipError_t launch_knn_rescore_k(const KnnArgs &a, hipStream_t s);
+template <int K> hipError_t launch_knn_core_k(const KnnArgs &a, hipStream_t s);
 template <int K> hipError_t launch_knn_merge_k(const KnnArgs &a, hipStream_t s);
 
 } // namespace ekh

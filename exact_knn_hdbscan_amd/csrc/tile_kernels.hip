@@ -92,6 +92,19 @@ hipError_t launch_knn_rescore(int K, const KnnArgs &a, hipStream_t s) {
     }
 }
 
+hipError_t launch_knn_core(int K, const KnnArgs &a, hipStream_t s) {
+    if (a.nq <= 0) return hipSuccess;
+    switch (K) {
+    case 2: return launch_knn_core_k<2>(a, s);
+    case 4: return launch_knn_core_k<4>(a, s);
+    case 8: return launch_knn_core_k<8>(a, s);
+    case 11: return launch_knn_core_k<11>(a, s);
+    case 16: return launch_knn_core_k<16>(a, s);
+    case 32: return launch_knn_core_k<32>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_knn_merge(int K, const KnnArgs &a, hipStream_t s) {
     if (a.nq <= 0) return hipSuccess;
     switch (K) {
@@ -177,68 +190,84 @@ void scan_tile_kernel(ScanArgs a) {
     using T = Tile<QM>;
     constexpr int QT = kWaves * 16 * CB;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, li = lane & 15;
-    const int split = blockIdx.y;
-    const int64_t cbase = (int64_t)blockIdx.x * QT;
+    // The number of active points is known only here (the host does not wait
+    // for it): q query tiles, each in sp database splits, as many as fill the
+    // launched workgroups once (the scan has no list warm-up), at least
+    // kScanMinTilesPerSplit tiles each.  Workgroup w takes items w, w + grid,
+    // ... (item = split * q + query tile), a loop every workgroup leaves after
+    // at most ceil(items / grid) trips.
+    const int64_t nact = (int64_t)__hip_atomic_load(a.nact, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int64_t q = (nact + QT - 1) / QT;
+    if (q == 0) return;
+    const int64_t G = gridDim.x;
+    int64_t sp = q < G ? G / q : 1;
+    const int64_t smax = a.tiles / kScanMinTilesPerSplit;
+    sp = sp < smax ? sp : (smax > 1 ? smax : 1);
+    const int64_t items = q * sp;
+    for (int64_t it = blockIdx.x; it < items; it += G) {
+        const int64_t qt = it % q;
+        const int64_t split = it / q;
+        const int64_t cbase = qt * QT;
 
-    EpiScan<CB, T::RB> epi;
-    epi.g = g;
-    epi.orig = a.orig;
-    float bq[CB][QM];
-    int32_t pt[CB];
-    bool valid[CB];
+        EpiScan<CB, T::RB> epi;
+        epi.g = g;
+        epi.orig = a.orig;
+        float bq[CB][QM];
+        int32_t pt[CB];
+        bool valid[CB];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-        const int64_t c = cbase + wave * 16 * CB + cb * 16 + li;
-        valid[cb] = c < a.nact;
-        const int32_t p = valid[cb] ? a.act[c] : 0;
-        pt[cb] = p;
-        load_query<QM>(a.X, a.ldx, p, valid[cb], a.d, a.chunks, g, bq[cb]);
-        epi.na[cb] = a.nrm[p];
-        epi.corea[cb] = a.core[p];
-        epi.ca[cb] = a.comp[p];
-        // start from the best edge already known for this point's component
-        float w0 = __uint_as_float(a.compW[epi.ca[cb]]);
-        const uint64_t own = a.best[p];
-        if (own != kNoEdge) w0 = fminf(w0, __uint_as_float((uint32_t)(own >> 32)));
-        epi.init[cb] = ((uint64_t)__float_as_uint(w0) << 32) | 0xffffffffull;
-        epi.best[cb] = epi.init[cb];
-        epi.thr[cb] = (!valid[cb] || epi.corea[cb] > w0) ? -INFINITY : scan_threshold(w0);
-    }
-    const int64_t tb = a.tiles * split / a.splits, te = a.tiles * (split + 1) / a.splits;
-    run_tiles<QM, CB, true, FULL>(a.Xb, a.ldb, a.nb, a.nrm_b, a.comp_b, a.core_b, a.d, a.chunks, tb, te, bq, epi);
-
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-        uint64_t b = epi.best[cb];
-#pragma unroll
-        for (int mask = 16; mask <= 32; mask <<= 1) {
-            const uint32_t lo = __shfl_xor((uint32_t)b, mask), hi = __shfl_xor((uint32_t)(b >> 32), mask);
-            const uint64_t o = ((uint64_t)hi << 32) | lo;
-            b = o < b ? o : b;
+        for (int cb = 0; cb < CB; ++cb) {
+            const int64_t c = cbase + wave * 16 * CB + cb * 16 + li;
+            valid[cb] = c < nact;
+            const int32_t p = valid[cb] ? a.act[c] : 0;
+            pt[cb] = p;
+            load_query<QM>(a.X, a.ldx, p, valid[cb], a.d, a.chunks, g, bq[cb]);
+            epi.na[cb] = a.nrm[p];
+            epi.corea[cb] = a.core[p];
+            epi.ca[cb] = a.comp[p];
+            // start from the best edge already known for this point's component
+            float w0 = __uint_as_float(a.compW[epi.ca[cb]]);
+            const uint64_t own = a.best[p];
+            if (own != kNoEdge) w0 = fminf(w0, __uint_as_float((uint32_t)(own >> 32)));
+            epi.init[cb] = ((uint64_t)__float_as_uint(w0) << 32) | 0xffffffffull;
+            epi.best[cb] = epi.init[cb];
+            epi.thr[cb] = (!valid[cb] || epi.corea[cb] > w0) ? -INFINITY : scan_threshold(w0);
         }
-        if (g == 0 && valid[cb] && b < epi.init[cb])
-            atomicMin((unsigned long long *)&a.best[pt[cb]], (unsigned long long)b);
+        const int64_t tb = a.tiles * split / sp, te = a.tiles * (split + 1) / sp;
+        run_tiles<QM, CB, true, FULL>(a.Xb, a.ldb, a.nb, a.nrm_b, a.comp_b, a.core_b, a.d, a.chunks, tb, te, bq,
+                                      epi);
+
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            uint64_t b = epi.best[cb];
+#pragma unroll
+            for (int mask = 16; mask <= 32; mask <<= 1) {
+                const uint32_t lo = __shfl_xor((uint32_t)b, mask), hi = __shfl_xor((uint32_t)(b >> 32), mask);
+                const uint64_t o = ((uint64_t)hi << 32) | lo;
+                b = o < b ? o : b;
+            }
+            if (g == 0 && valid[cb] && b < epi.init[cb])
+                atomicMin((unsigned long long *)&a.best[pt[cb]], (unsigned long long)b);
+        }
     }
 }
 
-template <int QM, bool FULL> static hipError_t scan_launch(const ScanArgs &a, hipStream_t s) {
-    constexpr int QT = kWaves * 16 * scan_col_blocks(QM);
-    const dim3 grid((unsigned)((a.nact + QT - 1) / QT), (unsigned)a.splits);
-    hipLaunchKernelGGL((scan_tile_kernel<QM, FULL>), grid, dim3(kThreads), 0, s, a);
+template <int QM, bool FULL> static hipError_t scan_launch(const ScanArgs &a, int64_t grid, hipStream_t s) {
+    hipLaunchKernelGGL((scan_tile_kernel<QM, FULL>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
-template <int QM> static hipError_t scan_full(const ScanArgs &a, hipStream_t s) {
-    return a.chunks == QM / 4 ? scan_launch<QM, true>(a, s) : scan_launch<QM, false>(a, s);
+template <int QM> static hipError_t scan_full(const ScanArgs &a, int64_t grid, hipStream_t s) {
+    return a.chunks == QM / 4 ? scan_launch<QM, true>(a, grid, s) : scan_launch<QM, false>(a, grid, s);
 }
 
-hipError_t launch_scan_tile(int QM, const ScanArgs &a, hipStream_t s) {
-    if (a.nact <= 0) return hipSuccess;
+hipError_t launch_scan_tile(int QM, const ScanArgs &a, int64_t grid, hipStream_t s) {
+    if (grid <= 0 || grid > 0x7fffffff || a.tiles <= 0) return hipErrorInvalidValue;
     switch (QM) {
-    case 16: return scan_full<16>(a, s);
-    case 32: return scan_full<32>(a, s);
-    case 56: return scan_full<56>(a, s);
-    case 64: return scan_full<64>(a, s);
+    case 16: return scan_full<16>(a, grid, s);
+    case 32: return scan_full<32>(a, grid, s);
+    case 56: return scan_full<56>(a, grid, s);
+    case 64: return scan_full<64>(a, grid, s);
     default: return hipErrorInvalidValue;
     }
 }

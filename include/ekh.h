@@ -132,10 +132,19 @@ size_t ekh_core_workspace_bytes(int64_t n, int32_t d, int32_t min_samples);
  * entry serves the neighbour-edge shortcut of ekh_mst_boruvka).
  *
  *  min_samples: 1 <= min_samples <= n - 1 and min_samples + 1 <= EKH_MAX_K.
- *  out_core [n] float32 (required): sqrt_rn(D2 of entry min_samples - 1).
+ *  out_core [n] float32 (required): the min_samples-th smallest (from 1) of
+ *      the row's K = min_samples + 1 list entries' distances recomputed by direct
+ *      differences, sqrt_rn(sum_f (x_f - y_f)^2) with fmaf in feature order.
+ *      The GEMM form's cancellation error (about 1e-5 relative for points whose
+ *      norm is large against their neighbour distance) does not reach it; the
+ *      list's extra entry keeps the rank-min_samples point in the list even
+ *      when that error reorders ranks min_samples and min_samples + 1.
  *  out_nbr_idx [n, min_samples + 1] int32, out_nbr_d2 [n, min_samples + 1]
  *      float32 (both NULL or both set): the self-kNN rows, ascending under
- *      (D2, index), self included with D2 = 0.
+ *      (D2, index), self included with D2 = 0; D2 here is the GEMM form, the
+ *      value ekh_mst_boruvka's scan computes for the same pair bit for bit.
+ *  ws: at least ekh_core_workspace_bytes() (norms, split lists, a point-major
+ *      copy of X for the direct differences and the list indices).
  */
 int ekh_core_distances(const float *X, int64_t ldx, int64_t n, int32_t d, int32_t min_samples, float *out_core,
                        int32_t *out_nbr_idx, float *out_nbr_d2, void *ws, size_t ws_bytes, void *stream);
@@ -169,20 +178,35 @@ size_t ekh_mst_workspace_bytes(int64_t n, int32_t d, int32_t min_samples, int wi
  * index, higher index), by Boruvka rounds with the exact shortcuts of
  * "Exact shortcuts" ("HDBSCAN" page).
  *
+ *  D2 is the GEMM form, the value ekh_core_distances' lists hold for the same
+ *  pair bit for bit, so the list shortcuts and the scan weigh every edge alike.
+ *
  *  core [n] float32: core distances as given (normally ekh_core_distances).
  *  nbr_idx, nbr_d2 [n, min_samples + 1]: the self-kNN rows ekh_core_distances
  *      returns; if both NULL they are recomputed inside (with_neighbours = 0
  *      in the workspace query).  The shortcuts are exact for any core array:
- *      a list settles a point only when its last entry is strictly farther
- *      than the point's core distance.
- *  flags: EKH_MST_NO_* and EKH_MST_FULL_SCANS switches (none changes the tree).
+ *      a list holds every point closer than its last entry, so a point whose
+ *      lightest edge into its list is lighter than that entry's distance needs
+ *      no scan, and a point whose core distance or last-entry distance exceeds
+ *      its component's lightest known edge cannot supply a lighter one.
+ *  flags: EKH_MST_NO_* and EKH_MST_FULL_SCANS switches (none changes the tree;
+ *      EKH_MST_NO_NEIGHBOUR_EDGES stops every use of the lists' completeness).
  *      From the second round on, when one component holds at least n / 2
  *      points, its active points are scanned only against a gathered copy of
  *      the points outside it (the workspace holds d * (n / 2 + 1) floats for
  *      that copy).
  *  out_lo, out_hi [n - 1] int32, out_w [n - 1] float32: the edges, lo < hi,
- *      sorted by (w, lo, hi).  n = 1 gives no edges.
+ *      sorted by (w, lo, hi).  The tree is the minimum one under the W above;
+ *      each reported w is max(core_lo, core_hi, D) with D recomputed by direct
+ *      differences (sqrt_rn of sum_f (x_lo,f - x_hi,f)^2, fmaf in feature
+ *      order), free of the GEMM form's cancellation error.  n = 1 gives no
+ *      edges.
  *  stats: optional host struct filled per round.
+ *  Blocks the host once per round (one read-back of the round's counters);
+ *  the scans find the number of points to scan on the device.
+ *  ws: at least ekh_mst_workspace_bytes() (round state, the complement copy,
+ *      a point-major copy of X for the reported weights, sort buffers, and the
+ *      lists when they are recomputed).
  *  Requires 1 <= min_samples < n for n >= 2.  At most ceil(log2 n) rounds;
  *  more returns EKH_EINTERNAL.
  */

@@ -199,9 +199,16 @@ def test_core_tiny_and_lists():
     say("core tiny ms=10")
     core, ni, nd2 = ekh.core_distances(dev(X), 10, return_neighbours=True)
     core, ni, nd2 = host(core), host(ni), host(nd2)
-    check_core(X, 10, core)
-    check_knn(X, X, 11, ni, np.sqrt(nd2))
-    np.testing.assert_array_equal(core, np.sqrt(nd2[:, 9]))
+    rep = {}
+    check_core(X, 10, core, report=rep)
+    check_knn(X, X, 11, ni, np.sqrt(nd2), report=rep, gemm_lists=True)
+    say("report", rep)
+    # the core distance is the direct-difference distance of the 10th-nearest list
+    # entry; the list's own D2 is the GEMM form, equal to it within float32 rounding
+    from parity import true_sqdist
+    t2 = np.sort(true_sqdist(X, np.arange(X.shape[1]), X, ni), axis=1)
+    np.testing.assert_allclose(core.astype(np.float64), np.sqrt(t2[:, 9]), rtol=2e-6)
+    np.testing.assert_allclose(core, np.sqrt(nd2[:, 9]), rtol=1e-5)
 
 
 def test_core_closed_forms():
