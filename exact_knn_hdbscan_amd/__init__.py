@@ -5,7 +5,7 @@ The compute lives in the HIP library ``libekh.so`` (C ABI declared in
 to it.  The binding is loaded on first use of one of the entry points below so
 that ``exact_knn_hdbscan_amd.datagen`` can be imported without a GPU.
 """
-_ENTRY_POINTS = ("knn", "core_distances", "mst_boruvka", "knn_workspace_bytes", "knn_plan", "core_workspace_bytes",
+_ENTRY_POINTS = ("knn", "knn_noalloc", "core_distances", "mst_boruvka", "knn_workspace_bytes", "knn_plan", "core_workspace_bytes",
                  "mst_workspace_bytes", "hdbscan_tail", "bipartite_assign", "bipartite_workspace_bytes",
                  "cluster_edge_counts", "merge_tree", "kmeanspp", "kmeanspp_workspace_bytes", "library", "MstStats", "EkhError", "kernel_timer")
 

@@ -92,6 +92,9 @@ def library() -> ctypes.CDLL:
             lib.ekh_knn_workspace_bytes.restype = _sz
             lib.ekh_knn.argtypes = [_p, _i64, _i64, _p, _i64, _i64, _i32, _i32, _p, _p, _i64, _p, _sz, _p]
             lib.ekh_knn_plan.argtypes = [_i64, _i64, _i32, _i32, _i64, ctypes.POINTER(_i64)]
+            lib.ekh_knn_noalloc_bytes.argtypes = [_i64, _i64, _i32, _i32, _i64]
+            lib.ekh_knn_noalloc_bytes.restype = _sz
+            lib.ekh_knn_noalloc.argtypes = [_p, _i64, _i64, _p, _i64, _i64, _i32, _i32, _p, _p, _i64, _p]
             lib.ekh_core_workspace_bytes.argtypes = [_i64, _i32, _i32]
             lib.ekh_core_workspace_bytes.restype = _sz
             lib.ekh_core_distances.argtypes = [_p, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _sz, _p]
@@ -186,6 +189,25 @@ def knn(X: torch.Tensor, Y: torch.Tensor, k: int, max_chunk_dots: int = 0, works
     _check(lib.ekh_knn(px, ldx, n, py, ldy, m, d, k, idx.data_ptr(), dist.data_ptr(), max_chunk_dots,
                        ws.data_ptr(), ws.numel(), _stream(X.device)))
     return idx, dist
+
+
+def knn_noalloc(X: torch.Tensor, Y: torch.Tensor, k: int, max_chunk_dots: int = 0, out_idx: torch.Tensor = None,
+                out_dist: torch.Tensor = None):
+    """ekh_knn_noalloc: knn() with the library's static scratch instead of a
+    workspace (no allocation inside the call).  Outputs may be passed in
+    (int32 / float32 [n, k] on X's device); otherwise they are allocated here."""
+    lib = library()
+    px, ldx, n, d = _points(X, "X")
+    py, ldy, m, dy = _points(Y, "Y")
+    if dy != d:
+        raise ValueError("X and Y must have the same dimension")
+    if out_idx is None:
+        out_idx = torch.empty((n, k), dtype=torch.int32, device=X.device)
+    if out_dist is None:
+        out_dist = torch.empty((n, k), dtype=torch.float32, device=X.device)
+    _check(lib.ekh_knn_noalloc(px, ldx, n, py, ldy, m, d, k, _ptr(out_idx), _ptr(out_dist), max_chunk_dots,
+                               _stream(X.device)))
+    return out_idx, out_dist
 
 
 def core_distances(X: torch.Tensor, min_samples: int, return_neighbours: bool = False, workspace=None):

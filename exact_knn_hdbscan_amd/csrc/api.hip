@@ -483,6 +483,42 @@ int ceil_log2(int64_t x) {
 
 } // namespace
 
+// ---- scratch of ekh_knn_noalloc -----------------------------------------------
+// One array per GPU (each device holds its own copy, at its own address), kept
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// never the device memory: host code uses only the address that
+// hipGetSymbolAddress returns for the device, taken once per device with that
+// device current, and passes that to the kernels.
+static __device__ __align__(256) unsigned char scratch[EKH_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::vector<void *> g_scratch_dev; // device address of `scratch`, per device
+
+// Device address of `scratch` on the device of stream s.
+int noalloc_scratch(hipStream_t s, void **out) {
+    int cur = 0, dev = 0;
+    EKH_HIP(hipGetDevice(&cur));
+    if (s) EKH_HIP(hipStreamGetDevice(s, &dev));
+    else dev = cur;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if ((int)g_scratch_dev.size() <= dev) g_scratch_dev.resize((size_t)dev + 1, nullptr);
+    if (!g_scratch_dev[(size_t)dev]) {
+        if (cur != dev) EKH_HIP(hipSetDevice(dev));
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) hipSetDevice(cur);
+        if (e != hipSuccess || !p)
+            return fail(EKH_EHIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_dev[(size_t)dev] = p;
+    }
+    *out = g_scratch_dev[(size_t)dev];
+    return EKH_OK;
+}
+
+} // namespace
+
 extern "C" {
 
 int ekh_version(void) { return 100; }
@@ -762,6 +798,43 @@ int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const flo
     EKH_HIP(edge_sort(w.e_lo, w.e_hi, w.e_w, n - 1, w.sort_tmp, w.sort_tmp_bytes, w.sa, w.sb, w.sc, w.sd, w.s64a,
                       w.s64b, out_lo, out_hi, out_w, s));
     return EKH_OK;
+}
+
+size_t ekh_knn_noalloc_bytes(int64_t n, int64_t m, int32_t d, int32_t k, int64_t max_chunk_dots) {
+    if (n < 1 || m < 1 || d < 1 || d > EKH_MAX_DIM || k < 1 || k > EKH_MAX_K) return 0;
+    const KnnPlan p = plan_knn(n, m, d, k, max_chunk_dots, 1);
+    Carver c(nullptr);
+    float *nx, *ny, *bt;
+    Entry *part;
+    int32_t *idx;
+    return knn_ws(p, n, m, false, c, &nx, &ny, &part, &idx, k, &bt, d);
+}
+
+int ekh_knn_noalloc(const float *X, int64_t ldx, int64_t n, const float *Y, int64_t ldy, int64_t m, int32_t d,
+                    int32_t k, int32_t *out_idx, float *out_dist, int64_t max_chunk_dots, void *stream) {
+    int rc;
+    if ((rc = check_points(X, ldx, n, d, "X")) != EKH_OK) return rc;
+    if ((rc = check_points(Y, ldy, m, d, "Y")) != EKH_OK) return rc;
+    if (k < 1 || k > EKH_MAX_K || k > m) return fail(EKH_EINVAL, "k = %d out of range [1, min(m, %d)]", k, EKH_MAX_K);
+    if (max_chunk_dots < 0) return fail(EKH_EINVAL, "max_chunk_dots < 0");
+    if (!out_idx && !out_dist) return fail(EKH_EINVAL, "no output requested");
+    const size_t need = ekh_knn_noalloc_bytes(n, m, d, k, max_chunk_dots);
+    if (need > (size_t)EKH_NOALLOC_SCRATCH_BYTES)
+        return fail(EKH_EWORKSPACE, "ekh_knn_noalloc needs %zu bytes of scratch for these sizes; its static scratch holds %zu",
+                    need, (size_t)EKH_NOALLOC_SCRATCH_BYTES);
+    hipStream_t s = (hipStream_t)stream;
+    void *ws = nullptr;
+    if ((rc = noalloc_scratch(s, &ws)) != EKH_OK) return rc;
+    const bool self = (X == Y) && (ldx == ldy) && (n == m);
+    const KnnPlan p = plan_knn(n, m, d, k, max_chunk_dots, 1); // every chunk on the caller's stream
+    Carver c(ws);
+    float *nx, *ny, *bt;
+    Entry *part;
+    int32_t *idx_scratch;
+    knn_ws(p, n, m, false, c, &nx, &ny, &part, &idx_scratch, k, &bt, d);
+    if (self) ny = nx;
+    return run_knn(p, X, ldx, n, Y, ldy, m, d, self, kOutKnn, k, 0, out_idx ? out_idx : idx_scratch, out_dist,
+                   nullptr, nx, ny, part, bt, s);
 }
 
 int ekh_timer_enable(int on) {

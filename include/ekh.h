@@ -121,6 +121,24 @@ int ekh_knn(const float *X, int64_t ldx, int64_t n, const float *Y, int64_t ldy,
  */
 int ekh_knn_plan(int64_t n, int64_t m, int32_t d, int32_t k, int64_t max_chunk_dots, int64_t out[8]);
 
+/*
+ * ekh_knn without a workspace or any allocation, for callers that cannot call
+ * hipMalloc (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments and results as ekh_knn, bit for bit,
+ * except ws and ws_bytes: its scratch is a static device array of
+ * EKH_NOALLOC_SCRATCH_BYTES held by every GPU the library runs on until the
+ * process ends, and every chunk runs on `stream` (no second stream, no event).
+ * Sizes whose scratch (ekh_knn_noalloc_bytes) exceeds the array return
+ * EKH_EWORKSPACE with a message.  All calls on one GPU share that GPU's array
+ * (it keeps the last call's contents; nothing in it needs clearing): calls
+ * that overlap on one GPU race and must be ordered by the caller, e.g. on one
+ * stream.  Other errors as ekh_knn.
+ */
+#define EKH_NOALLOC_SCRATCH_BYTES (64u << 20)
+size_t ekh_knn_noalloc_bytes(int64_t n, int64_t m, int32_t d, int32_t k, int64_t max_chunk_dots);
+int ekh_knn_noalloc(const float *X, int64_t ldx, int64_t n, const float *Y, int64_t ldy, int64_t m, int32_t d,
+                    int32_t k, int32_t *out_idx, float *out_dist, int64_t max_chunk_dots, void *stream);
+
 /* ------------------------------------------------------------------ core distances */
 
 size_t ekh_core_workspace_bytes(int64_t n, int32_t d, int32_t min_samples);

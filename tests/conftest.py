@@ -18,6 +18,11 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    """Run GPU tests in file order but put the full-size ones last, so a quick
-    failure surfaces before the long cases."""
-    items.sort(key=lambda it: (1 if it.get_closest_marker("fullsize") else 0))
+    """Run GPU tests in file order but put the full-size ones after the others,
+    so a quick failure surfaces before the long cases, and the test of the
+    allocation-free entry point last of all."""
+    def rank(it):
+        if it.module is not None and it.module.__name__.endswith("test_zz_no_alloc"):
+            return 2
+        return 1 if it.get_closest_marker("fullsize") else 0
+    items.sort(key=rank)
