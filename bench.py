@@ -32,13 +32,15 @@ TAIL_MIN_CLUSTER_SIZE = 20  # the HDBSCAN page's results use min_cluster_size = 
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "knn_tile_traffic_clips_500000x61.md")
+# the kernel and the planner that decides its launch layout
 KNN_SOURCES = ["exact_knn_hdbscan_amd/csrc/tile_common.h", "exact_knn_hdbscan_amd/csrc/knn_inst.hip",
-               "exact_knn_hdbscan_amd/csrc/ekh_internal.h"]
+               "exact_knn_hdbscan_amd/csrc/ekh_internal.h", "exact_knn_hdbscan_amd/csrc/api.hip"]
 
 
 def stored_traffic():
-    """HBM bytes per kNN-tile launch from the committed counter summary, or None
-    if the kernel sources have changed since the counters were taken."""
+    """L2-miss (fabric) bytes per kNN-tile launch from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size), or None if
+    the kernel or planner sources have changed since the counters were taken."""
     import hashlib
     import re
     try:
@@ -173,6 +175,75 @@ def time_seeding(ekh, datagen, oracle_too, reps=10):
         res["oracle_ms"] = 1000.0 * (time.perf_counter() - t0)
         res["matches_oracle"] = got == (want[0], want[1])
     return res
+
+
+def time_clips(ekh, datagen, oracle_too, reps=5):
+    """The path (core distances + Boruvka MST) on the two other clip-like
+    workloads: the tiny set (2,000 x 60) and clips 100,000 x 61, median of reps
+    steps, with the kNN kernel's rate and the MST time.  With the CPU baseline,
+    the oracle's core distances and Prim on the tiny set are timed beside the
+    GPU (all host threads), and the stored oracle times of the two clip sets
+    (tests/golden, written by make_golden.py) are quoted as context."""
+    import numpy as np
+    import torch
+
+    out = {}
+    for name in ("tiny_2000x60", "clips_100000x61"):
+        wl = datagen.make(name)
+        Xh = wl["X"]
+        d, n = Xh.shape
+        ms = wl.get("min_samples", 10)
+        X = torch.from_numpy(Xh).cuda()
+        wc = torch.empty(ekh.core_workspace_bytes(n, d, ms), dtype=torch.uint8, device=X.device)
+        wm = torch.empty(ekh.mst_workspace_bytes(n, d, ms, True), dtype=torch.uint8, device=X.device)
+
+        def step():
+            core, ni, nd2 = ekh.core_distances(X, ms, return_neighbours=True, workspace=wc)
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            r = ekh.mst_boruvka(X, core, ms, ni, nd2, return_stats=True, workspace=wm)
+            return r, e
+
+        step()
+        torch.cuda.synchronize()
+        timer = ekh.kernel_timer()
+        timer.__enter__()
+        tot, knn = [], []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            e0.record()
+            (lo, hi, w, st), ek = step()
+            e1.record()
+            torch.cuda.synchronize()
+            tot.append(1000.0 * (time.perf_counter() - t0))
+            knn.append(e0.elapsed_time(ek))
+        tk = timer.read(timer.KNN_TILE)
+        timer.stop()
+        ms_step, ms_knn = float(np.median(tot)), float(np.median(knn))
+        pairs = float(n) * float(n)
+        tfl = tk["flop"] / (tk["ms"] / 1e3) / 1e12 if tk["ms"] else None
+        res = {"n": n, "d": d, "min_samples": ms, "ms_per_step": ms_step, "knn_ms": ms_knn,
+               "pairs_per_s": pairs / (ms_step / 1e3), "knn_pairs_per_s": pairs / (ms_knn / 1e3),
+               "knn_kernel_tflops": tfl, "knn_kernel_frac": tfl / PEAK_FP32_MFMA_TFLOPS if tfl else None,
+               "mst_ms": ms_step - ms_knn, "rounds": st["rounds"], "scanned": st["scanned"]}
+        if oracle_too:
+            import oracle
+            if n <= 5000:
+                t0 = time.perf_counter()
+                core_o = oracle.core_distances(Xh, ms)
+                t1 = time.perf_counter()
+                oracle.mst_prim(Xh, core_o)
+                t2 = time.perf_counter()
+                res["oracle"] = {"core_ms": 1000.0 * (t1 - t0), "prim_ms": 1000.0 * (t2 - t1),
+                                 "threads": oracle.max_threads()}
+            g = os.path.join(ROOT, "tests", "golden", name + "_oracle.json")
+            if os.path.exists(g):
+                res["oracle_stored_seconds"] = json.load(open(g)).get("oracle_seconds")
+        out[name] = res
+        del X, wc, wm
+    return out
 
 
 def time_sections(ekh, datagen, oracle_too=False, reps=5):
@@ -345,7 +416,8 @@ def main():
                      "launches": dom["launches"], "avg_launch_ms": dom["ms"] / max(dom["launches"], 1),
                      "traffic": (stored_traffic() if dom_name == "knn_tile_kernel"
                                  and args.workload == "clips_500000x61" else None),
-                     "traffic_unit": "bytes per launch (HBM, counters scaled by a copy of known size)"},
+                     "traffic_unit": "bytes per launch that miss the L2 (FETCH_SIZE + WRITE_SIZE, scaled by a "
+                                     "copy of known size; served by the MALL or HBM)"},
     }
     # HDBSCAN tail on the host (outside the step): the last step's tree copied to
     # the host and condensed with min_cluster_size 20 (the page's setting)
@@ -358,6 +430,11 @@ def main():
         "noise": int((labels < 0).sum()), "where": "host C++ (ekh_hdbscan_tail), device-to-host copy of the tree included",
         "end_to_end_ms": ms_step + tail_ms}
     if not args.no_sections:
+        result["clip_sets"] = time_clips(ekh, datagen, oracle_too=not args.no_cpu_baseline)
+        g = os.path.join(ROOT, "tests", "golden", args.workload + "_oracle.json")
+        if os.path.exists(g) and not args.no_cpu_baseline:
+            # the oracle's own run on this workload (make_golden.py), as context for the MST time
+            result["mst"]["oracle_stored_seconds"] = json.load(open(g)).get("oracle_seconds")
         result["knn_sections"] = time_sections(ekh, datagen, oracle_too=not args.no_cpu_baseline)
         result["kmeanspp_seeding"] = time_seeding(ekh, datagen, oracle_too=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:

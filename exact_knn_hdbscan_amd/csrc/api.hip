@@ -138,7 +138,8 @@ constexpr int kChunkStreams = 2;          // chunks of one kNN call in flight at
 // three-slot norm ring do not fit that many times (the lists live in registers)
 int64_t knn_groups_per_cu(int K, int QM) {
     const int64_t tr = tile_rows(QM), rs = 4 * QM + 4;
-    const int64_t lds = 2 * tr * rs * 4 + 3 * tr * 4;
+    // tile double buffer, norm ring, and the slow path's dot products (column blocks x rows per lane)
+    const int64_t lds = 2 * tr * rs * 4 + 3 * tr * 4 + knn_col_blocks(K, QM) * 4 * (tr / 16) * kThreads * 4;
     const int64_t by_lds = kLdsPerCu / lds;
     const int64_t want = knn_waves_per_simd(K, QM);
     return by_lds < want ? (by_lds < 1 ? 1 : by_lds) : want;

@@ -41,8 +41,7 @@ inline int pick_k(int k) {
 inline int pick_qm(int d) { return d <= 64 ? 16 : (d <= 128 ? 32 : (d <= 224 ? 56 : 64)); }
 inline int tile_rows(int qm) { return qm == 64 ? 16 : 32; }
 // kNN tile kernel occupancy: three waves per SIMD where the registers fit
-// without spills (d <= 64 and K <= 16: 156 VGPRs at K = 11; d <= 128 and
-// K <= 11: 164), two otherwise
+// without spills (d <= 64 and K <= 16; d <= 128 and K <= 11), two otherwise
 constexpr int knn_waves_per_simd(int K, int QM) { return (QM == 16 && K <= 16) || (QM == 32 && K <= 11) ? 3 : 2; }
 // Boruvka scan kernel occupancy: three waves per SIMD for d <= 128, two otherwise
 constexpr int scan_waves_per_simd(int QM) { return QM <= 32 ? 3 : 2; }

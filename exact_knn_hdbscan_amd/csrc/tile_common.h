@@ -26,6 +26,15 @@ __device__ __forceinline__ f4 mfma16(float a, float b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// A wave-uniform 64-bit value, held in scalar registers (the compiler cannot
+// always prove uniformity through 64-bit arithmetic, and would otherwise keep
+// tile counters and row bases in vector registers).
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // ---------------------------------------------------------------- tile loop
 // Feature order of the contraction: with qs = 4 * ceil(d / 16) k-steps, lane
 // group g supplies feature g * qs + s at k-step s (features >= d are zero).
@@ -56,9 +65,11 @@ template <int QM> struct Tile {
 template <int QM, int CB, bool PAYLOAD, bool FULL, class Epi>
 __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t ldb, int64_t m,
                                           const float *__restrict__ nrm_b, const int32_t *__restrict__ comp_b,
-                                          const float *__restrict__ core_b, int d, int chunks, int64_t t_begin,
-                                          int64_t t_end, const float (&bq)[CB][QM], Epi &epi) {
+                                          const float *__restrict__ core_b, int d, int chunks, int64_t t_begin_,
+                                          int64_t t_end_, const float (&bq)[CB][QM], Epi &epi) {
     using T = Tile<QM>;
+    const int64_t t_begin = uniform64(t_begin_), t_end = uniform64(t_end_);
+    m = uniform64(m);
     __shared__ __align__(16) float sm_tile[2][T::TR * T::RS];
     __shared__ __align__(16) float sm_nrm[3][T::TR];
     __shared__ int32_t sm_comp[3][PAYLOAD ? T::TR : 1];
@@ -78,7 +89,8 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
         float v[T::PF];
         float n, core;
         int32_t comp;
-        bool nv; // row in range
+        bool nv;      // a row of this tile (else an infinite norm)
+        int64_t row0; // first row read
     };
     // Loads: raw buffer loads whose resource is a wave-uniform base per feature
     // row (scalar registers, advanced per tile) and whose per-lane 32-bit offset
@@ -88,22 +100,28 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
     // 4 (64 / TR - 1) ld + TR - 1 floats (the host keeps ld below 2^25).  A
     // feature >= d reads feature d - 1 instead: finite values that meet
     // zero-padded query features, so their products are exactly 0 and no mask
-    // is needed.  Rows at or past m occur only in the last tile; they read row
-    // m - 1 and get an infinite norm, so they never qualify.
+    // is needed.  A partial last tile is read as rows m - TR .. m - 1 (a scalar
+    // change of base); its rows before the tile belong to the previous one and
+    // get an infinite norm, so they never qualify.  In a database of fewer than
+    // TR rows, the lanes past its end read row m - 1 (set once in their
+    // offsets), also with an infinite norm.
     static_assert(64 % T::TR == 0, "a wave covers whole rows of lane groups");
     constexpr int kGroups = 64 / T::TR;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = (tid & 63) / T::TR; // lq == kGroups * wv + grp
     const float *fbase[T::PF];
     uint32_t foff[T::PF];
+    // a database of fewer rows than one tile (one tile, rows 0 .. TR - 1): the
+    // lanes past its end read row m - 1 instead
+    const int64_t lr = m < T::TR && lrow >= m ? m - 1 : lrow;
 #pragma unroll
     for (int p = 0; p < T::PF; ++p) {
         const int f_lo = 4 * (kGroups * wv + (p >> 2) * T::FSTEP) + (p & 3);
         const int fl = f_lo < d ? f_lo : d - 1, fa = f_lo + 4 * grp < d ? f_lo + 4 * grp : d - 1;
         fbase[p] = B + (int64_t)fl * ldb;
-        foff[p] = (uint32_t)((int64_t)(fa - fl) * ldb + lrow) * 4u;
+        foff[p] = (uint32_t)((int64_t)(fa - fl) * ldb + lr) * 4u;
     }
-    const uint32_t noff = (uint32_t)lrow * 4u; // lrow == tid % TR: the thread also loads row lrow's norm
+    const uint32_t noff = (uint32_t)lr * 4u; // lrow == tid % TR: the thread also loads row lrow's norm
     // the tile's base address as an explicit scalar, so that it is not folded
     // into per-lane 64-bit pointers (the load then adds the 32-bit lane offset)
     typedef const char __attribute__((address_space(1))) *gchar;
@@ -120,24 +138,25 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
             (void *)(const char *)base, (short)0, 0x7fffffff, 0x00020000);
         return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
     };
-    // One load sequence for every tile (so that the wait counts stay exact): in
-    // the last tile a row at or past m moves its byte offsets back to row m - 1.
+    // One load sequence for every tile, with no address arithmetic (a branch
+    // around the loads would cost the wait counts that let the next tile's
+    // loads overlap this tile's MFMAs).
     auto load = [&](Pref &P, int64_t t) {
         const int64_t tt = t < t_end ? t : t_end - 1;
-        const int64_t row0 = tt * T::TR;
-        uint32_t back = 0;
-        P.nv = true;
-        if (row0 + T::TR > m) {
-            const int64_t j = row0 + lrow;
-            P.nv = j < m;
-            back = P.nv ? 0u : (uint32_t)(j - (m - 1)) * 4u;
-        }
+        const int64_t rt = tt * T::TR; // the tile's first row
+        const bool part = rt + T::TR > m;
+        const int64_t row0 = uniform64(part && m >= T::TR ? m - T::TR : rt);
+        P.row0 = row0;
+        // rows lrow in [lo, hi) belong to this tile (scalar bounds)
+        const int lo = part && m >= T::TR ? (int)(rt - row0) : 0;
+        const int hi = part && m < T::TR ? (int)m : T::TR;
+        P.nv = lrow >= lo && lrow < hi;
 #pragma unroll
-        for (int p = 0; p < T::PF; ++p) P.v[p] = __uint_as_float(ld32(sbase(fbase[p] + row0), foff[p] - back));
-        P.n = __uint_as_float(ld32(sbase(nrm_b + row0), noff - back));
+        for (int p = 0; p < T::PF; ++p) P.v[p] = __uint_as_float(ld32(sbase(fbase[p] + row0), foff[p]));
+        P.n = __uint_as_float(ld32(sbase(nrm_b + row0), noff));
         if (PAYLOAD) {
-            P.comp = (int32_t)ld32(sbase(comp_b + row0), noff - back);
-            P.core = __uint_as_float(ld32(sbase(core_b + row0), noff - back));
+            P.comp = (int32_t)ld32(sbase(comp_b + row0), noff);
+            P.core = __uint_as_float(ld32(sbase(core_b + row0), noff));
         }
     };
     auto store = [&](const Pref &P, int buf, int slot) {
@@ -200,9 +219,8 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
             }
         }
     };
-    auto finish = [&](const f4 (&acc)[T::RB][CB], int64_t t, int slot) {
-        epi.tile(acc, sm_nrm[slot], PAYLOAD ? sm_comp[slot] : nullptr, PAYLOAD ? sm_core[slot] : nullptr,
-                 t * T::TR);
+    auto finish = [&](const f4 (&acc)[T::RB][CB], int64_t row0, int slot) {
+        epi.tile(acc, sm_nrm[slot], PAYLOAD ? sm_comp[slot] : nullptr, PAYLOAD ? sm_core[slot] : nullptr, row0);
     };
 
     if (t_begin >= t_end) return;
@@ -211,16 +229,18 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
     store(P, 0, 0);
     __syncthreads();
     f4 acc[T::RB][CB];
-    int buf = 0, sl = 0; // tile t's LDS buffer and norm slot
+    int buf = 0, sl = 0;         // tile t's LDS buffer and norm slot
+    int64_t rcur = P.row0;       // and its first row
     for (int64_t t = t_begin; t < t_end; ++t) {
         const int sn = sl == 2 ? 0 : sl + 1;
         if (t + 1 < t_end) load(P, t + 1);
         mma(buf, acc);
-        finish(acc, t, sl);
+        finish(acc, rcur, sl);
         if (t + 1 < t_end) store(P, buf ^ 1, sn);
         __syncthreads();
         buf ^= 1;
         sl = sn;
+        rcur = P.row0;
     }
 }
 
@@ -352,9 +372,9 @@ __device__ __forceinline__ float group_max_nonneg(float v) { return __uint_as_fl
 
 // ---------------------------------------------------------------- kNN epilogue
 // Each lane keeps CB lists (one per query column it owns) in registers.  Per
-// tile every D2 is computed and tested against an admission threshold in
-// straight-line code; a lane that has a candidate inserts its candidates in
-// ascending row order (recomputing the same D2).
+// tile every D2 is tested against an admission threshold in straight-line code
+// (the fast test); only when a lane of the wave passes, the slow path inserts
+// the passing rows of each lane in ascending row order (see slow()).
 //
 // The four lanes of a query column see disjoint rows and keep separate lists
 // that are merged at the end.  Any K real candidates bound the query's final
@@ -377,7 +397,7 @@ template <int K, int CB, int RB> struct EpiKnn {
     float nq[CB];
     float adm[CB];  // admission bound on D2 shared by the column's four lanes
     float admq[CB]; // the same bound moved to nb - 2 s, widened by the rounding margin
-    bool dirty;     // this lane changed a list since adm was last formed
+    bool dirty;     // wave-uniform: a lane of the wave ran the slow path since adm was last formed
     int32_t qrow[CB];
     int g;
 
@@ -396,26 +416,24 @@ template <int K, int CB, int RB> struct EpiKnn {
     __device__ __forceinline__ void load(int cb, TopK<K> &L) { L = lst[cb]; }
     __device__ __forceinline__ void store(int cb, const TopK<K> &L) { lst[cb] = L; }
 
-    __device__ __forceinline__ float dist2(const f4 (&acc)[RB][CB], const f4 (&nb4)[RB], int rb, int r, int cb) const {
-        return fmaf(-2.f, acc[rb][cb][r], nq[cb] + nb4[rb][r]);
-    }
-    // D2 of the pair (i, i) needs no special case: the norms come from the same
-    // MFMA chain as the dot products, so it is fma(-2, n_i, 2 n_i) = 0 exactly.
+    // D2 = fma(-2, s, nq + nb).  The pair (i, i) needs no special case: the
+    // norms come from the same MFMA chain as the dot products, so it is
+    // fma(-2, n_i, 2 n_i) = 0 exactly.
     //
     // Fast test per element: t = fma(-2, s, nb) against admq = adm - nq, widened.
     // If D2 = fma(-2, s, nq + nb) (two roundings) is <= adm, the point lies within
     // sqrt(adm) of the query, so nb <= 2 nq + 2 adm, and every rounding error
     // between D2 and t + nq is at most a few units of 2^-24 (nq + nb + adm); the
     // widening by 2^-20 (adm + nq) covers it with room to spare.  The test only
-    // decides whether a lane looks at its candidates: those are then taken with
-    // the exact D2 and the exact bound, so results do not depend on the margin.
+    // decides which rows a lane inserts (with their exact D2): the margin can
+    // admit a few more rows, which does not change the result (see slow()).
     //
     // prepare() re-forms the bound (only when a list of the wave changed: a
     // wave-uniform test), fast() is the branch-free test, slow() inserts the
     // candidates of the columns that passed; tile() runs the three.
     __device__ __forceinline__ void prepare() {
         constexpr float kWiden = 1.0f / 1048576.0f;
-        if (__builtin_amdgcn_ballot_w64(dirty)) {
+        if (dirty) {
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
                 const float gq = kSecond ? __uint_as_float(group_second_u32(__float_as_uint(qj[cb]),
@@ -438,27 +456,68 @@ template <int K, int CB, int RB> struct EpiKnn {
             hit[cb] = mn <= admq[cb];
         }
     }
+    // Candidates of the lanes that passed, inserted in a loop over the set bits
+    // of a per-lane mask (bit 4 rb + r: ascending rows).  Each trip, every lane
+    // with a bit left takes its lowest, reads that row's dot product back from
+    // LDS ([value][thread], so the row is picked by an address rather than a
+    // chain of selects) and inserts the exact D2.  The fixed insertion network
+    // thus runs as many times as the busiest lane of the wave has candidates,
+    // not once per row position that any lane needs.
+    //
+    // The mask takes the fast test's value per row (t = fma(-2, s, n_b) against
+    // the widened bound), a superset of the rows within the bound.  A row
+    // beyond the bound that enters a list is still a real candidate of the
+    // query, and the merged result stays exact: every row of the final list is
+    // within the bound at every moment (the bound is the K-th smallest of K real
+    // candidates, never below the final K-th), so no lane drops it, whatever
+    // else its list holds.
+    static constexpr int NV = CB * RB * 4;
+    float *sv;  // LDS [NV][kThreads]
+    int tid;
     __device__ __forceinline__ void slow(const f4 (&acc)[RB][CB], const f4 (&nb4)[RB], const bool (&hit)[CB],
-                                         int64_t j0) {
+                                         const float *nrm, int64_t j0) {
+        bool any = false;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            if (!hit[cb]) continue;
-            TopK<K> L;
-            load(cb, L);
+        for (int cb = 0; cb < CB; ++cb) any = any || hit[cb];
+        if (!__builtin_amdgcn_ballot_w64(any)) return;
+        dirty = true; // wave-uniform: the bound is re-formed before the next tile
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int32_t j = (int32_t)(j0 + rb * 16 + 4 * g + r);
-                    const float d2 = dist2(acc, nb4, rb, r, cb);
-                    if (d2 <= adm[cb] && d2 < L.d[K - 1]) L.push_ascending(d2 > 0.f ? d2 : 0.f, j);
+                for (int r = 0; r < 4; ++r) sv[((cb * RB + rb) * 4 + r) * kThreads + tid] = acc[rb][cb][r];
+        __builtin_amdgcn_wave_barrier(); // the LDS stores above before the loads below
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            if (!__builtin_amdgcn_ballot_w64(hit[cb])) continue;
+            uint32_t mk = 0u;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    mk |= hit[cb] && fmaf(-2.f, acc[rb][cb][r], nb4[rb][r]) <= admq[cb] ? (1u << (4 * rb + r)) : 0u;
+            TopK<K> L;
+            load(cb, L);
+            for (int trip = 0; trip < RB * 4; ++trip) {
+                if (!__builtin_amdgcn_ballot_w64(mk != 0u)) break;
+                if (mk != 0u) {
+                    const int e = __builtin_ctz(mk);
+                    mk &= mk - 1u;
+                    const int row = (e >> 2) * 16 + 4 * g + (e & 3);
+                    const float d2 = fmaf(-2.f, sv[((cb * RB + (e >> 2)) * 4 + (e & 3)) * kThreads + tid],
+                                          nq[cb] + nrm[row]);
+                    L.push_ascending(d2 > 0.f ? d2 : 0.f, (int32_t)(j0 + row));
                 }
+            }
             store(cb, L);
-            thr[cb] = L.d[K - 1];
-            qj[cb] = L.d[J];
-            if (kSecond) qj1[cb] = L.d[J - 1];
-            dirty = true;
+            if (hit[cb]) {
+                thr[cb] = L.d[K - 1];
+                qj[cb] = L.d[J];
+                if (kSecond) qj1[cb] = L.d[J - 1];
+            }
         }
+        __builtin_amdgcn_wave_barrier(); // the loads above before the next tile's stores
     }
     __device__ __forceinline__ void tile(const f4 (&acc)[RB][CB], const float *nrm, const int32_t *, const float *,
                                          int64_t j0) {
@@ -468,7 +527,7 @@ template <int K, int CB, int RB> struct EpiKnn {
         prepare();
         bool hit[CB];
         fast(acc, nb4, hit);
-        slow(acc, nb4, hit, j0);
+        slow(acc, nb4, hit, nrm, j0);
     }
 };
 
@@ -519,22 +578,32 @@ void knn_tile_kernel(KnnArgs a) {
     const int nsplit = body ? 1 : a.splits;
     const int64_t qbase = body ? (int64_t)blockIdx.x * QT : tail0 + (h % tail_q) * QT; // local row of the first query
 
-    EpiKnn<K, CB, T::RB> epi;
     float bq[CB][QM];
     bool qv[CB];
+    float nq[CB];
+    int32_t qrow[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         const int64_t ql = qbase + wave * 16 * CB + cb * 16 + li;
         qv[cb] = ql < a.nq;
         const int64_t q = a.q0 + (qv[cb] ? ql : 0);
         load_query<QM>(a.Q, a.ldq, q, qv[cb], a.d, a.chunks, g, bq[cb]);
-        epi.nq[cb] = qv[cb] ? a.nrm_q[q] : 0.f;
-        epi.qrow[cb] = (int32_t)(a.q0 + ql);
+        nq[cb] = qv[cb] ? a.nrm_q[q] : 0.f;
+        qrow[cb] = (int32_t)(a.q0 + ql);
+    }
+    const int64_t tb = a.tiles * split / nsplit, te = a.tiles * (split + 1) / nsplit;
+
+    __shared__ float sv[EpiKnn<K, CB, T::RB>::NV * kThreads];
+    EpiKnn<K, CB, T::RB> epi;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        epi.nq[cb] = nq[cb];
+        epi.qrow[cb] = qrow[cb];
     }
     epi.init();
     epi.g = g;
-
-    const int64_t tb = a.tiles * split / nsplit, te = a.tiles * (split + 1) / nsplit;
+    epi.sv = sv;
+    epi.tid = tid;
     run_tiles<QM, CB, false, FULL>(a.B, a.ldb, a.m, a.nrm_b, nullptr, nullptr, a.d, a.chunks, tb, te, bq, epi);
 
     // merge the four lane groups that share each query column
