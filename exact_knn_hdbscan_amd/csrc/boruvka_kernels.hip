@@ -482,6 +482,7 @@ __global__ void bv_edge_weights_kernel(const float *__restrict__ P, int dp, cons
     const f4 *pa = reinterpret_cast<const f4 *>(P + (int64_t)a * dp);
     const f4 *pb = reinterpret_cast<const f4 *>(P + (int64_t)b * dp);
     float s = 0.f;
+#pragma unroll 4
     for (int f = 0; f < dp / 4; ++f) {
         const f4 x = pa[f], y = pb[f];
 #pragma unroll

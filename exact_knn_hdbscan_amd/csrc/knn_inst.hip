@@ -35,14 +35,17 @@ template <> hipError_t launch_knn_tile_k<EKH_KNN_K>(int QM, const KnnArgs &a, hi
 }
 
 template <> hipError_t launch_knn_rescore_k<EKH_KNN_K>(const KnnArgs &a, hipStream_t s) {
-    const int bs = 128;
-    hipLaunchKernelGGL(knn_rescore_kernel<EKH_KNN_K>, dim3((unsigned)((a.nq + bs - 1) / bs)), dim3(bs), 0, s, a);
+    constexpr int rows = DirectRows<EKH_KNN_K>::kRowsPerBlock;
+    if (a.dp > kDirectMaxDim || a.k_out > EKH_KNN_K) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(knn_rescore_kernel<EKH_KNN_K>, dim3((unsigned)((a.nq + rows - 1) / rows)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 template <> hipError_t launch_knn_core_k<EKH_KNN_K>(const KnnArgs &a, hipStream_t s) {
-    const int bs = 128;
-    hipLaunchKernelGGL(knn_core_kernel<EKH_KNN_K>, dim3((unsigned)((a.nq + bs - 1) / bs)), dim3(bs), 0, s, a);
+    constexpr int rows = DirectRows<EKH_KNN_K>::kRowsPerBlock;
+    if (a.dp > kDirectMaxDim || a.k_out > EKH_KNN_K || a.min_samples < 1 || a.min_samples > a.k_out)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(knn_core_kernel<EKH_KNN_K>, dim3((unsigned)((a.nq + rows - 1) / rows)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -647,113 +647,113 @@ template <int K> __global__ __launch_bounds__(256) void knn_merge_kernel(KnnArgs
     if (ql < a.nq && r == 0) write_list<K>(a, L, a.q0 + ql, 0);
 }
 
-// Reported kNN distances: the selected neighbours' D2 recomputed by direct
-// differences, sum_f (q_f - y_f)^2 with fmaf in feature order, which carries no
-// cancellation error; each row is then sorted by (that D2, index).  The
-// neighbour set itself is the one the GEMM-form D2 selected.  One thread per
-// query row: the query's features are read once, feature by feature (adjacent
-// threads, adjacent rows: coalesced), and each neighbour's from the
-// point-major copy Bt, four features per 16-byte load; the padding features
-// (zero on both sides) add exact zeros.
-template <int K> __global__ void knn_rescore_kernel(KnnArgs a) {
-    const int64_t ql = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (ql >= a.nq) return;
-    const int64_t q = a.q0 + ql;
-    int32_t jr[K], jo[K]; // row read (always in range) and row reported
-    float s[K];
-#pragma unroll
-    for (int t = 0; t < K; ++t) {
-        jo[t] = t < a.k_out ? a.out_idx[q * a.k_out + t] : 0;
-        // a list entry outside [0, m) cannot come from a finished search (k <= m);
-        // it is never used as an address: row 0 is read and the entry ranks last
-        jr[t] = (jo[t] >= 0 && jo[t] < a.m) ? jo[t] : 0;
-        s[t] = 0.f;
+// Direct-difference D2 of the selected neighbours, for the reported kNN
+// distances and the core distances: sum_f (q_f - y_f)^2 with fmaf in feature
+// order, which carries no cancellation error.  One lane per (row, list entry),
+// kRowLanes lanes per row (a power of two >= K), so a row's K gathers run in
+// parallel: the neighbour's features come from the point-major copy Bt, four
+// per 16-byte load, and the query's from LDS, where each wave first stages its
+// rows' features (feature-major source, coalesced).  Padding features are zero
+// on both sides and add exact zeros.  The row's order is then taken across its
+// lanes by ranks (shuffles), with no sort network.
+template <int K> struct DirectRows {
+    static constexpr int kRowLanes = K <= 16 ? 16 : 32;
+    static constexpr int kRowsPerWave = 64 / kRowLanes;
+    static constexpr int kRowsPerBlock = kRowsPerWave * 4; // 256 threads
+};
+constexpr int kDirectMaxDim = 256; // EKH_MAX_DIM rounded to 4
+
+// D2 of this lane's entry (row q, entry t) and its key; returns false for lanes
+// past the rows.  sq: LDS [kRowsPerBlock][kDirectMaxDim].
+template <int K>
+__device__ __forceinline__ bool direct_d2(const KnnArgs &a, float *sq, int64_t &q, int &t, int32_t &jo, float &d2) {
+    using R = DirectRows<K>;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rw = lane / R::kRowLanes; // row within the wave
+    t = lane % R::kRowLanes;
+    const int64_t qb = ((int64_t)blockIdx.x * 4 + wave) * R::kRowsPerWave; // first local row of the wave
+    float *sw = sq + wave * R::kRowsPerWave * kDirectMaxDim;
+    // stage the wave's rows' features: lane l loads row (l % rows) feature (l / rows) + step
+    for (int f = lane / R::kRowsPerWave; f < a.dp; f += 64 / R::kRowsPerWave) {
+        const int r = lane % R::kRowsPerWave;
+        const int64_t qq = qb + r;
+        sw[r * kDirectMaxDim + f] = (qq < a.nq && f < a.d) ? a.Q[(int64_t)f * a.ldq + a.q0 + qq] : 0.f;
     }
-    for (int f = 0; f < a.dp; f += 4) {
-        float qv[4];
+    __builtin_amdgcn_wave_barrier(); // the LDS stores above before the loads below (one wave)
+    const int64_t ql = qb + rw;
+    q = a.q0 + ql;
+    if (ql >= a.nq) return false;
+    jo = t < a.k_out ? a.out_idx[q * a.k_out + t] : 0x7fffffff;
+    // an entry outside [0, m) cannot come from a finished search (k <= m); it is
+    // never used as an address: row 0 is read and the entry ranks last
+    const bool ok = t < a.k_out && jo >= 0 && jo < a.m;
+    const int32_t jr = ok ? jo : 0;
+    const f4 *y = reinterpret_cast<const f4 *>(a.Bt + (int64_t)jr * a.dp);
+    const f4 *x = reinterpret_cast<const f4 *>(sw + rw * kDirectMaxDim);
+    float s = 0.f;
+#pragma unroll 4
+    for (int f = 0; f < a.dp / 4; ++f) {
+        const f4 yv = y[f], xv = x[f];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) qv[e] = f + e < a.d ? a.Q[(int64_t)(f + e) * a.ldq + q] : 0.f;
-#pragma unroll
-        for (int t = 0; t < K; ++t) {
-            if (t < a.k_out) {
-                const f4 y = *reinterpret_cast<const f4 *>(a.Bt + (int64_t)jr[t] * a.dp + f);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float v = qv[e] - y[e];
-                    s[t] = fmaf(v, v, s[t]);
-                }
-            }
+        for (int e = 0; e < 4; ++e) {
+            const float v = xv[e] - yv[e];
+            s = fmaf(v, v, s);
         }
     }
-    TopK<K> L;
-    L.clear();
-#pragma unroll
-    for (int t = 0; t < K; ++t)
-        if (t < a.k_out) L.push_any(jr[t] == jo[t] ? s[t] : INFINITY, jo[t]);
-#pragma unroll
-    for (int t = 0; t < K; ++t) {
-        if (t < a.k_out) {
-            a.out_idx[q * a.k_out + t] = L.i[t];
-            if (a.out_dist) a.out_dist[q * a.k_out + t] = sqrt_rn(L.d[t]);
-        }
-    }
+    d2 = ok ? s : INFINITY;
+    return true;
 }
 
-// Core distances by direct differences: for each row, the squared distance to
-// every entry of its final list as sum_f (q_f - y_f)^2 (fmaf in feature order,
-// no cancellation error), and core = sqrt_rn of the min_samples-th smallest of
-// them (ties by list position).  The list itself was selected with the
-// GEMM-form D2; its first min_samples + 1 entries hold every point within the
-// true rank-min_samples distance unless the GEMM form's rounding exceeds the
-// gap between ranks min_samples and min_samples + 2, so this is the float32
-// value of the exact core distance ("HDBSCAN" page, "The algorithm on the
-// device": the distance to the min_samples-th neighbour, the point itself
-// counted).  Same access pattern as knn_rescore_kernel: one thread per row,
-// the neighbours' features from the point-major copy Bt.
-template <int K> __global__ void knn_core_kernel(KnnArgs a) {
-    const int64_t ql = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (ql >= a.nq) return;
-    const int64_t q = a.q0 + ql;
-    int32_t jr[K];
-    bool ok[K];
-    float s[K];
+// Rank of this lane's (d2, index) among its row's lanes (lanes past k_out hold
+// (inf, INT_MAX)); ties of equal keys go to the lower lane.
+template <int K> __device__ __forceinline__ int direct_rank(float d2, int32_t jo, int t) {
+    using R = DirectRows<K>;
+    const int base = (threadIdx.x & 63) & ~(R::kRowLanes - 1);
+    int rank = 0;
 #pragma unroll
-    for (int t = 0; t < K; ++t) {
-        const int32_t j = t < a.k_out ? a.out_idx[q * a.k_out + t] : -1;
-        ok[t] = t < a.k_out && j >= 0 && j < a.m;
-        jr[t] = ok[t] ? j : 0; // never used as an address out of range
-        s[t] = 0.f;
+    for (int u = 0; u < R::kRowLanes; ++u) {
+        const float du = __shfl(d2, base + u);
+        const int32_t ju = __shfl(jo, base + u);
+        rank += (du < d2 || (du == d2 && (ju < jo || (ju == jo && u < t)))) ? 1 : 0;
     }
-    for (int f = 0; f < a.dp; f += 4) {
-        float qv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qv[e] = f + e < a.d ? a.Q[(int64_t)(f + e) * a.ldq + q] : 0.f;
-#pragma unroll
-        for (int t = 0; t < K; ++t) {
-            if (t < a.k_out) {
-                const f4 y = *reinterpret_cast<const f4 *>(a.Bt + (int64_t)jr[t] * a.dp + f);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float v = qv[e] - y[e];
-                    s[t] = fmaf(v, v, s[t]);
-                }
-            }
-        }
-    }
-    // the min_samples-th smallest (rank min_samples - 1 from 0) of the k_out values
-    float c2 = 0.f;
-#pragma unroll
-    for (int t = 0; t < K; ++t) {
-        if (!ok[t]) s[t] = INFINITY;
-    }
-#pragma unroll
-    for (int t = 0; t < K; ++t) {
-        int r = 0;
-#pragma unroll
-        for (int u = 0; u < K; ++u) r += (u < a.k_out && (s[u] < s[t] || (s[u] == s[t] && u < t))) ? 1 : 0;
-        if (t < a.k_out && r == a.min_samples - 1) c2 = s[t];
-    }
-    a.out_core[q] = sqrt_rn(c2);
+    return rank;
+}
+
+// Reported kNN distances: each row's entries re-ordered by (direct D2, index)
+// and reported as sqrt_rn of the direct D2.  The neighbour set itself is the
+// one the GEMM-form D2 selected.
+template <int K> __global__ __launch_bounds__(256) void knn_rescore_kernel(KnnArgs a) {
+    __shared__ __align__(16) float sq[DirectRows<K>::kRowsPerBlock * kDirectMaxDim];
+    int64_t q;
+    int t;
+    int32_t jo = 0x7fffffff;
+    float d2 = INFINITY;
+    const bool live = direct_d2<K>(a, sq, q, t, jo, d2);
+    const int rank = direct_rank<K>(d2, jo, t); // every lane takes part in the shuffles
+    if (!live || t >= a.k_out) return;
+    // every lane has read its own entry before any lane of the row writes (the
+    // ranks' shuffles order them), and the row's lanes lie in one wave
+    a.out_idx[q * a.k_out + rank] = jo;
+    if (a.out_dist) a.out_dist[q * a.k_out + rank] = sqrt_rn(d2);
+}
+
+// Core distances by direct differences: core = sqrt_rn of the min_samples-th
+// smallest direct D2 among the row's K = min_samples + 1 list entries.  The list
+// was selected with the GEMM-form D2; its first min_samples + 1 entries hold
+// every point within the true rank-min_samples distance unless the GEMM form's
+// rounding exceeds the gap between ranks min_samples and min_samples + 2, so
+// this is the float32 value of the exact core distance ("HDBSCAN" page, "The
+// algorithm on the device": the distance to the min_samples-th neighbour, the
+// point itself counted).
+template <int K> __global__ __launch_bounds__(256) void knn_core_kernel(KnnArgs a) {
+    __shared__ __align__(16) float sq[DirectRows<K>::kRowsPerBlock * kDirectMaxDim];
+    int64_t q;
+    int t;
+    int32_t jo = 0x7fffffff;
+    float d2 = INFINITY;
+    const bool live = direct_d2<K>(a, sq, q, t, jo, d2);
+    const int rank = direct_rank<K>(d2, jo, t);
+    if (live && t < a.k_out && rank == a.min_samples - 1) a.out_core[q] = sqrt_rn(d2);
 }
 
 template <int K> hipError_t launch_knn_tile_k(int QM, const KnnArgs &a, hipStream_t s);

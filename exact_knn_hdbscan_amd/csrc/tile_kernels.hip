@@ -18,6 +18,7 @@ __global__ __launch_bounds__(256) void norms_kernel(const float *__restrict__ X,
     const bool valid = p < n;
     const int qs = 4 * chunks;
     f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
     for (int s = 0; s < qs; ++s) {
         const int f = g * qs + s;
         const float v = (valid && f < d) ? X[(int64_t)f * ldx + p] : 0.f;
