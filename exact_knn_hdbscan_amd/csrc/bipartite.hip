@@ -1,10 +1,11 @@
 // Bipartite kNN-graph assignment of libekh (ekh_bipartite_assign).
 //
 // Kilosort4 clustering page, section "Assignment in parallel: why the graph is
-// bipartite": left nodes are the spikes, right nodes a copy of the subset,
-// every kNN link is an edge.  With the right labels fixed, every spike's best
-// cluster depends only on its own neighbours, so all spikes are assigned at
-// once (left step), then all right nodes (right step), alternately.  The right
+// bipartite".  The graph has the spikes on one side and a copy of the subset on
+// the other, with one edge per kNN link.  Once the subset's labels are held
+// fixed, no spike's choice affects another's, so every spike is relabelled in
+// one parallel step (left step); the subset side is then relabelled the same
+// way (right step), and the two steps alternate.  The right
 // step counts labels with integer atomics into counts[r, label]; each thread
 // takes the label maximising n - gamma k K_c / 2m; one counter of moved spikes
 // is read back per round.  The conventions the page leaves open are listed in
@@ -316,8 +317,8 @@ extern "C" int ekh_bipartite_assign(const int32_t *nbr, int64_t n, int32_t k, in
     return EKH_OK;
 }
 
-// Edge counts between clusters ("Merges and splits": one more atomic kernel,
-// read back once by the caller).  Blocks: the range check reads back three
+// Edge counts between clusters ("Merges and splits": a single pass of atomic
+// adds on the device, whose result the caller reads back once).  Blocks: the range check reads back three
 // counters before any count is added.
 extern "C" int ekh_cluster_edge_counts(const int32_t *nbr, int64_t n, int32_t k, int64_t m, const int32_t *left,
                                        const int32_t *right, int32_t n_clusters, uint32_t *out_counts, void *ws,

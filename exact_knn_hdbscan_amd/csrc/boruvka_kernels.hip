@@ -1,7 +1,7 @@
 // Per-round Boruvka kernels of libekh ("HDBSCAN" page, "The algorithm on the
-// device": each round every component's cheapest edge to another component is
-// found, then components merge; ties broken by (weight, lower index, higher
-// index)).  All of them are O(n) memory passes; the O(|active| n) part is the
+// device": in a round, each component finds the lightest edge that leaves it,
+// and the components joined by those edges merge; edges are ordered by
+// (weight, lower index, higher index)).  All of them are O(n) memory passes; the O(|active| n) part is the
 // MFMA scan in tile_kernels.hip.  Only integer atomics are used, so every
 // result is independent of execution order.
 #include "ekh_internal.h"

@@ -1,10 +1,11 @@
 // Greedy k-means++ seeding of libekh (ekh_kmeanspp).
 //
 // Kilosort4 clustering page, section "The measurement that changed the design:
-// serial chains inside a thread": each new seed is the best of 2 + ln k
-// candidates drawn by squared distance; the uniforms are made on the host and
-// uploaded once, and every draw, score and pick happens on the device with no
-// host sync.  The page's lesson is that no thread may carry a long serial
+// serial chains inside a thread".  The method there: after the first seed,
+// 2 + ln k candidates are sampled with weights given by their squared distance
+// to the nearest seed so far, and the one that leaves the lowest potential is
+// kept.  The random numbers come from the host in one upload, and the device
+// does all sampling, scoring and picking without waiting on the host.  The page's lesson is that no thread may carry a long serial
 // chain.  Seeding is one chain of k dependent steps, each short (sum L
 // candidates' potentials, pick, lower the weights, scan, draw), so what
 // matters is how little latency each step costs.  Two paths, same results:

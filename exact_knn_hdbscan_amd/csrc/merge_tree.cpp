@@ -1,8 +1,8 @@
 // Host merging tree of libekh (ekh_merge_tree).
 //
-// Kilosort4 clustering page, section "Merges and splits": the merging tree
-// needs only the edge counts between clusters (at most 200 x 200 values, read
-// back once); building it is host work.  The merging rule is greedy modularity
+// Kilosort4 clustering page, section "Merges and splits": the tree is built on
+// the host from nothing but the cluster-to-cluster edge counts (a matrix of at
+// most 200 x 200, copied back from the device once).  The merging rule is greedy modularity
 // agglomeration on the undirected cluster graph, with the conventions stated
 // in include/ekh.h.  O(C^3) for C clusters (8e6 steps at C = 200).  Built with
 // -ffp-contract=off so that every gain rounds as written.

@@ -121,8 +121,8 @@ hipError_t launch_knn_merge(int K, const KnnArgs &a, hipStream_t s) {
 
 // ---------------------------------------------------------------- Boruvka scan
 // Cheapest edge from each active point a to another component, over all n
-// points ("HDBSCAN" page, "Exact shortcuts": only the remaining clips are
-// scanned against all others).  Key of an edge seen from a: (W bits << 32 | b);
+// points ("HDBSCAN" page, "Exact shortcuts": the points the shortcuts did not
+// settle are the only ones compared with every other point).  Key of an edge seen from a: (W bits << 32 | b);
 // for a fixed a this order equals the edge order (W, lower, higher index).
 
 // A squared-distance threshold that no improving candidate can exceed: an

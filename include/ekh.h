@@ -11,8 +11,8 @@
  *    so the per-launch scratch stays bounded (MAX_CHUNK_DOTS).
  *  - "HDBSCAN", section "The algorithm on the device": core distance = distance
  *    to the min_samples-th nearest neighbour with the point itself included;
- *    MST of max(core_a, core_b, |a - b|) by Boruvka rounds, ties broken by
- *    (weight, lower index, higher index) so the tree is unique.
+ *    MST of max(core_a, core_b, |a - b|) by Boruvka rounds; ordering edges by
+ *    (weight, lower index, higher index) leaves exactly one minimum tree.
  *  - same page, section "The hang": the nearest list is a fixed,
  *    compile-time-unrolled compare-and-swap sequence, no flag-terminated loop;
  *    every kernel loop is bounded by a counter or a constant.
@@ -22,18 +22,26 @@
  *
  * Conventions shared by every entry point
  *  - Point sets are feature-major: point i of X has feature f at
- *    X[f * ldx + i], with n <= ldx < 2^25 (any n, m, d, ld, odd values
- *    included; the bound keeps the tile loads' byte offsets within 32 bits).
+ *    X[f * ldx + i] (any n, m, d and ld, odd values included, within two
+ *    limits the pages do not set): d <= EKH_MAX_DIM = 256, the widest form
+ *    the tile kernels hold in registers (the pages' sets have 60 to 200
+ *    features); and n <= ldx < 2^25 (33.5 million points), which keeps the
+ *    tile loads' byte offsets within 32 bits, far past where an exact O(n^2)
+ *    search is practical.
  *    X, Y, outputs and the workspace are DEVICE pointers owned by the caller;
- *    the library never allocates or frees caller memory and keeps no state
- *    between calls, except the optional kernel timer below and one extra
- *    stream per device (non-blocking, default priority, created on the first
- *    chunked ekh_knn call and kept to the end of the process) on which a
- *    second row chunk runs beside the caller's stream, joined back to it with
- *    events before the call's later work.
+ *    the library never allocates or frees caller memory.
+ *  - State kept between calls (a reading; the pages are silent on it): the
+ *    optional kernel timer below, the static scratch of ekh_knn_noalloc, and
+ *    one extra stream per device (non-blocking, default priority, created on
+ *    the first chunked ekh_knn call and kept to the end of the process).  On
+ *    it a second row chunk runs beside the caller's stream, forked from and
+ *    joined back to the caller's stream with events, so to the caller all
+ *    work is ordered on `stream`.  Two chunks in flight took the wide section
+ *    (200,000 x 20,000, 63 chunks) from 24.9 to 21.3 ms; taking the stream
+ *    from the caller instead would add an argument for that one case.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
  *    ekh_knn and ekh_core_distances do not synchronise the host.
- *    ekh_mst_boruvka blocks: it reads a few counters back after each round.
+ *    ekh_mst_boruvka blocks: it reads its counters back once per round.
  *  - Squared distances are float32, D2 = max(0, (|x|^2 + |y|^2) - 2 x.y), with
  *    the product on MFMA and the norms computed by the same MFMA contraction
  *    (same feature order), so that D2(a, b) is bitwise symmetric, identical in
@@ -270,9 +278,9 @@ int ekh_bipartite_assign(const int32_t *nbr, int64_t n, int32_t k, int64_t m, in
 
 /*
  * Edge counts between clusters (device).  Source: "Kilosort4 clustering and
- * matching", section "Merges and splits": the merging tree needs only the edge
- * counts between clusters, counted on the device with one more atomic kernel
- * and read back once.  out_counts [C, C] u32 (device, row-major, written
+ * matching", section "Merges and splits": the merging tree is built from the
+ * cluster-to-cluster edge counts alone, which one pass of atomic adds fills on
+ * the device and the host copies back once.  out_counts [C, C] u32 (device, row-major, written
  * whole): out_counts[a * C + b] = number of edges (spike i, subset point r) of
  * nbr [n, k] with left[i] = a and right[r] = b.  ws: at least 16 bytes of device
  * memory.  Blocks: three range counters are read back before any count is
@@ -307,9 +315,11 @@ int ekh_merge_tree(const uint32_t *counts, int32_t n_clusters, double gamma, int
 /*
  * Greedy k-means++ seeding of a section.  Source: "Kilosort4 clustering and
  * matching", section "The measurement that changed the design: serial chains
- * inside a thread": each new seed is the best of 2 + ln k candidates drawn by
- * squared distance, from uniforms made on the host and uploaded once; every
- * draw, score and pick runs on the device, with no host sync.  The page leaves
+ * inside a thread": every seed after the first is picked from 2 + ln k
+ * candidates sampled with squared-distance weights, keeping the one that
+ * leaves the lowest potential; the random numbers come from the host in one
+ * upload, and sampling, scoring and picking all run on the device without
+ * waiting on the host.  The page leaves
  * the arithmetic open; the conventions here make every decision exact:
  *  - L = 2 + floor(ln k) candidates per seed after the first (7 at k = 200);
  *  - squared distances are float32, summed over features in order from 0,
@@ -352,8 +362,9 @@ int ekh_kmeanspp(const float *X, int64_t ldx, int64_t n, int32_t d, int32_t k, c
  * HDBSCAN tail, on the HOST: spanning tree -> single-linkage hierarchy ->
  * condensed tree -> excess-of-mass selection -> cluster labels.
  * Source: "HDBSCAN", section "The algorithm on the device", last item (the
- * hierarchy, its condensed tree and the excess-of-mass selection run on the
- * host, in linear time) with the edge order of the same section; the steps
+ * page does the single-linkage hierarchy, its condensing and the
+ * excess-of-mass choice on the CPU, in time linear in n) with the edge order
+ * of the same section; the steps
  * are the standard HDBSCAN* definitions, with these conventions:
  *  - the n - 1 edges are merged in ascending (w, lo, hi) order, one union each
  *    (equal weights thus merge in index order, like the tree's own tie rule);

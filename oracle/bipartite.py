@@ -4,11 +4,11 @@ TEST INFRASTRUCTURE ONLY.  Imported by tests/ and bench.py's baseline leg;
 never by the product path.  Plain Python and numpy, float64.
 
 Source: the Kilosort4 clustering page, section "Assignment in parallel: why
-the graph is bipartite".  Left nodes are the spikes, right nodes a copy of the
-subset, and every kNN link (spike i, its neighbour r among the subset) is an
-edge.  With the right labels fixed, each spike's best cluster depends only on
-its own neighbours, so all left nodes are assigned at once, then all right
-nodes, alternately.
+the graph is bipartite".  The spikes form the left side of the graph and a
+copy of the subset the right side; each kNN link (spike i, its neighbour r
+among the subset) is an edge.  Holding the right labels fixed makes the spikes' choices independent of
+one another, so the left side is relabelled in one step, then the right side,
+and the two steps alternate.
 
 The page gives the right step's score, n_rc - gamma k_r K_c / 2m, and says that
 the left step counts a spike's neighbours' labels and takes the best.  The

@@ -4,10 +4,11 @@ TEST INFRASTRUCTURE ONLY.  Imported by tests/ and bench.py's baseline leg;
 never by the product path.  Plain Python and numpy.
 
 Source: the Kilosort4 clustering page, section "The measurement that changed
-the design: serial chains inside a thread": k-means++ picks its seeds one at a
-time, each new seed the best of 2 + ln k candidates drawn with probability
-proportional to the squared distance to the seeds so far, from uniforms made on
-the host and uploaded once.  The page states the method, not its arithmetic;
+the design: serial chains inside a thread".  Seeds are chosen one after
+another; for each seed after the first, 2 + ln k candidates are sampled with
+weights proportional to their squared distance to the closest seed chosen so
+far, and the candidate giving the lowest potential wins.  The random numbers
+are generated on the host and uploaded in one go.  The page states the method, not its arithmetic;
 the readings taken here:
 
 * k seeds over the n points (columns) of a feature-major section X [d, n];

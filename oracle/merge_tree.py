@@ -3,9 +3,9 @@
 TEST INFRASTRUCTURE ONLY.  Imported by tests/ and bench.py's baseline leg;
 never by the product path.  Plain Python and numpy, float64.
 
-Source: the Kilosort4 clustering page, section "Merges and splits": the merging
-tree needs only the edge counts between clusters, counted on the device and
-read back once (at most 200 x 200 values); building the tree is host work.  The
+Source: the Kilosort4 clustering page, section "Merges and splits": the tree is
+built on the host from the cluster-to-cluster edge counts alone (a matrix of at
+most 200 x 200 that the device fills and the host copies back once).  The
 page does not give the merging rule; the reading taken here stays in the
 section "Assignment in parallel"'s modularity terms:
 

@@ -8,7 +8,7 @@ total tree weight within 1e-5 relative):
   cannot hold where D is near 0 for the GEMM form (|x|^2 + |y|^2) - 2 x.y, so
   a distance also passes when its square is within an absolute floor
   eps = 4 u (|x|^2 + |y|^2), u = 2^-24, of the true square (the search page's
-  "one in ten thousand with an absolute floor" policy, with the floor sized to
+  policy of a relative 1e-4 equivalence with an absolute floor, the floor sized to
   a few float32 roundings of the norms).  Only distances near 0 can need the
   floor: if the relative test fails and the floor test passes, then
   2e-5 D^2 < |D_gpu^2 - D^2| <= eps.  Every check counts the entries that

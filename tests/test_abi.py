@@ -178,3 +178,30 @@ def test_kmeanspp_rejects_bad_arguments(lib):
     assert lib.ekh_kmeanspp_workspace_bytes(0, 200, 0) == 0
     assert lib.ekh_kmeanspp_workspace_bytes(1416, 0, 0) == 0
     assert lib.ekh_kmeanspp_workspace_bytes(1416, 200, 4) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(n=0), -1), (dict(d=257), -1), (dict(k=33), -1), (dict(ldx=1 << 25), -1), (dict(X=None), -1),
+    # sizes whose scratch exceeds the static array: refused before any GPU call
+    (dict(n=400000, ldx=400000, m=400000, ldy=400000, d=61, k=11), -2),
+])
+def test_knn_noalloc_rejects_bad_arguments(lib, args, code):
+    lib.ekh_knn_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_int64, ctypes.c_void_p]
+    a = dict(X=BOGUS, ldx=100, n=100, Y=BOGUS, ldy=50, m=50, d=8, k=5)
+    a.update(args)
+    rc = lib.ekh_knn_noalloc(a["X"], a["ldx"], a["n"], a["Y"], a["ldy"], a["m"], a["d"], a["k"], BOGUS, BOGUS, 0,
+                             None)
+    assert rc == code
+    assert lib.ekh_last_error()
+
+
+def test_knn_noalloc_scratch_sizes(lib):
+    lib.ekh_knn_noalloc_bytes.restype = ctypes.c_size_t
+    lib.ekh_knn_noalloc_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int64]
+    # the two section workloads fit the 64 MiB array, a 500,000-point self-kNN does not
+    assert 0 < lib.ekh_knn_noalloc_bytes(50000, 5000, 102, 10, 0) < (64 << 20)
+    assert 0 < lib.ekh_knn_noalloc_bytes(200000, 20000, 200, 10, 64000000) < (64 << 20)
+    assert lib.ekh_knn_noalloc_bytes(500000, 500000, 61, 11, 0) > (64 << 20)
