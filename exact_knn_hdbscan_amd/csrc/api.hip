@@ -69,12 +69,30 @@ struct Carver {
 // ---- kernel timer -----------------------------------------------------------
 struct TimerRec {
     int id;
+    int dev; // device the events belong to
     hipEvent_t e0, e1;
     double flop;
 };
 std::mutex g_tmu;
 bool g_timer_on = false;
 std::vector<TimerRec> g_trecs;
+// events of finished records, kept per device for reuse (creating two events
+// per timed launch would put host work between the launches)
+std::vector<std::pair<int, hipEvent_t>> g_evpool;
+
+// called with g_tmu held
+bool take_event(hipEvent_t *e) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    for (size_t k = g_evpool.size(); k-- > 0;) {
+        if (g_evpool[k].first == dev) {
+            *e = g_evpool[k].second;
+            g_evpool.erase(g_evpool.begin() + (std::ptrdiff_t)k);
+            return true;
+        }
+    }
+    return hipEventCreate(e) == hipSuccess;
+}
 
 struct TimedLaunch {
     TimerRec rec{};
@@ -85,8 +103,17 @@ struct TimedLaunch {
         if (!g_timer_on) return;
         rec.id = id;
         rec.flop = flop;
-        if (hipEventCreate(&rec.e0) != hipSuccess || hipEventCreate(&rec.e1) != hipSuccess) return;
+        if (!take_event(&rec.e0)) return;
+        if (!take_event(&rec.e1)) {
+            hipEventDestroy(rec.e0);
+            return;
+        }
+        hipGetDevice(&rec.dev);
         on = hipEventRecord(rec.e0, s) == hipSuccess;
+        if (!on) {
+            hipEventDestroy(rec.e0);
+            hipEventDestroy(rec.e1);
+        }
     }
     // returns the record's position (for timer_set_flop), or -1 when the timer is off
     int64_t done() {
@@ -301,9 +328,9 @@ int stream_wait(hipStream_t waiter, hipStream_t from) {
 int run_knn(const KnnPlan &p, const float *X, int64_t ldx, int64_t n, const float *Y, int64_t ldy, int64_t m, int d,
             bool self, int out_mode, int k_out, int min_samples, int32_t *out_idx, float *out_dist, float *out_core,
             float *nx, float *ny, Entry *part, float *bt, hipStream_t s, bool core_direct = false) {
-    EKH_HIP(launch_norms(X, ldx, n, d, nx, s));
-    if (!self) EKH_HIP(launch_norms(Y, ldy, m, d, ny, s));
-    if (out_mode == kOutKnn || core_direct) EKH_HIP(launch_point_major(Y, ldy, m, d, padded_dim(d), bt, s));
+    // norms of both sets and the database's point-major copy, in one launch
+    EKH_HIP(launch_prep(X, ldx, n, nx, Y, ldy, m, self ? nullptr : ny, (out_mode == kOutKnn || core_direct) ? bt : nullptr,
+                        d, padded_dim(d), s));
     hipStream_t cs[kChunkStreams] = {s};
     int forked = 1; // streams in use: the caller's, then those made to wait for it
     // After the fork every exit, an error included, first makes the caller's
@@ -840,9 +867,11 @@ int ekh_knn_noalloc(const float *X, int64_t ldx, int64_t n, const float *Y, int6
 
 int ekh_timer_enable(int on) {
     std::lock_guard<std::mutex> lk(g_tmu);
+    // the records' events go back to the pool (the caller reads the timer after
+    // synchronising, so their work has completed)
     for (auto &r : g_trecs) {
-        hipEventDestroy(r.e0);
-        hipEventDestroy(r.e1);
+        g_evpool.emplace_back(r.dev, r.e0);
+        g_evpool.emplace_back(r.dev, r.e1);
     }
     g_trecs.clear();
     g_timer_on = on != 0;

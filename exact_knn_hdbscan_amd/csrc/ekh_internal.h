@@ -103,6 +103,10 @@ struct KnnArgs {
 
 // host launchers (return hipError_t of the launch)
 hipError_t launch_norms(const float *X, int64_t ldx, int64_t n, int d, float *out, hipStream_t s);
+// Norms of X (into nx), of Y when ny is set, and Y's point-major copy when Bt is
+// set, in one launch.
+hipError_t launch_prep(const float *X, int64_t ldx, int64_t n, float *nx, const float *Y, int64_t ldy, int64_t m,
+                       float *ny, float *Bt, int d, int dp, hipStream_t s);
 hipError_t launch_knn_tile(int K, int QM, const KnnArgs &a, hipStream_t s);
 hipError_t launch_knn_merge(int K, const KnnArgs &a, hipStream_t s);
 hipError_t launch_knn_rescore(int K, const KnnArgs &a, hipStream_t s);

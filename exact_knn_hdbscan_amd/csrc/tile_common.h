@@ -298,23 +298,48 @@ template <int K> struct TopK {
             i[t] = ni[t];
         }
     }
-    __device__ __forceinline__ static bool less(float a, int32_t ia, float b, int32_t ib) {
-        return a < b || (a == b && ia < ib);
+    // (d2, idx) order as one 64-bit comparison: for d2 >= 0 (or +inf) the float
+    // bits order like the values, and indices are non-negative.
+    __device__ __forceinline__ static uint64_t key(float a, int32_t ia) {
+        return ((uint64_t)__float_as_uint(a) << 32) | (uint32_t)ia;
     }
-    // Candidate in any order: full (d2, idx) comparison.
+    __device__ __forceinline__ static bool less(float a, int32_t ia, float b, int32_t ib) {
+        return key(a, ia) < key(b, ib);
+    }
+    // Candidate in any order: the same fixed network as push_ascending, with the
+    // full (d2, idx) comparison deciding where the candidate goes.  med3 still
+    // yields the right value in every slot (where the candidate ties a
+    // neighbour on d2, either choice is the same value); the indices follow the
+    // full comparisons.  No serial chain, so the K slots update in parallel.
     __device__ __forceinline__ void push_any(float v, int32_t j) {
-        if (!less(v, j, d[K - 1], i[K - 1])) return;
-        d[K - 1] = v;
-        i[K - 1] = j;
+        bool lt[K];
 #pragma unroll
-        for (int t = K - 1; t > 0; --t) {
-            const bool sw = less(d[t], i[t], d[t - 1], i[t - 1]);
-            const float a = sw ? d[t] : d[t - 1], b = sw ? d[t - 1] : d[t];
-            const int32_t ia = sw ? i[t] : i[t - 1], ib = sw ? i[t - 1] : i[t];
-            d[t - 1] = a;
-            d[t] = b;
-            i[t - 1] = ia;
-            i[t] = ib;
+        for (int t = 0; t < K; ++t) lt[t] = less(v, j, d[t], i[t]);
+        float nd[K];
+        int32_t ni[K];
+        nd[0] = lt[0] ? v : d[0];
+        ni[0] = lt[0] ? j : i[0];
+#pragma unroll
+        for (int t = 1; t < K; ++t) {
+            nd[t] = __builtin_amdgcn_fmed3f(d[t - 1], v, d[t]);
+            ni[t] = lt[t - 1] ? i[t - 1] : (lt[t] ? j : i[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < K; ++t) {
+            d[t] = nd[t];
+            i[t] = ni[t];
+        }
+    }
+    // Whether (v, j) would enter the list.
+    __device__ __forceinline__ bool admits(float v, int32_t j) const { return less(v, j, d[K - 1], i[K - 1]); }
+    // Pushes a list that ascends in (d2, idx): once no lane of the wave admits
+    // its next entry, no later entry can enter either (each lane's last entry
+    // only falls), so the wave stops there.
+    __device__ __forceinline__ void push_sorted(const float (&od)[K], const int32_t (&oi)[K]) {
+#pragma unroll
+        for (int t = 0; t < K; ++t) {
+            if (!__builtin_amdgcn_ballot_w64(admits(od[t], oi[t]))) break;
+            push_any(od[t], oi[t]);
         }
     }
     // Merge with the list held by lane (lane ^ mask); both lanes end equal.
@@ -326,8 +351,7 @@ template <int K> struct TopK {
             od[t] = __shfl_xor(d[t], mask);
             oi[t] = __shfl_xor(i[t], mask);
         }
-#pragma unroll
-        for (int t = 0; t < K; ++t) push_any(od[t], oi[t]);
+        push_sorted(od, oi);
     }
 };
 
@@ -631,15 +655,21 @@ template <int K> __global__ __launch_bounds__(256) void knn_merge_kernel(KnnArgs
     const int r = (int)(gid % kMergeLanes);
     TopK<K> L;
     L.clear();
-    if (ql < a.nq) {
-        for (int s = r; s < a.splits; s += kMergeLanes) {
-            const Entry *src = a.part + ((int64_t)s * a.nq + ql) * K;
+    // the lanes of a wave run the same number of trips (a.splits is uniform and
+    // r < kMergeLanes): lanes past their last split push empty lists
+    for (int s0 = 0; s0 < a.splits; s0 += kMergeLanes) {
+        const int s = s0 + r;
+        float od[K];
+        int32_t oi[K];
+        const bool have = ql < a.nq && s < a.splits;
+        const Entry *src = a.part + ((int64_t)(have ? s : 0) * a.nq + (have ? ql : 0)) * K;
 #pragma unroll
-            for (int t = 0; t < K; ++t) {
-                const Entry e = src[t];
-                L.push_any(e.d2, e.idx);
-            }
+        for (int t = 0; t < K; ++t) {
+            const Entry e = have ? src[t] : Entry{INFINITY, 0x7fffffff};
+            od[t] = e.d2;
+            oi[t] = e.idx;
         }
+        L.push_sorted(od, oi);
     }
     // every lane of the wave takes part in the shuffles (rows past the end hold empty lists)
 #pragma unroll

@@ -11,10 +11,13 @@ namespace ekh {
 // from 0).  So the norm of x equals, bit for bit, the dot product the tile
 // kernels compute for x against any bitwise-identical point, and identical
 // points get D2 = fma(-2, n, 2n) = 0 exactly.
-__global__ __launch_bounds__(256) void norms_kernel(const float *__restrict__ X, int64_t ldx, int64_t n, int d,
-                                                    int chunks, float *__restrict__ out) {
+// Squared norms of 64 points per workgroup (16 per wave), as the diagonal of
+// the same MFMA chain the tile kernels run, so that a point's distance to
+// itself is exactly 0.
+__device__ __forceinline__ void norms_block(const float *__restrict__ X, int64_t ldx, int64_t n, int d, int chunks,
+                                            float *__restrict__ out, int64_t block) {
     const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
-    const int64_t p = ((int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 16 + li;
+    const int64_t p = (block * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 16 + li;
     const bool valid = p < n;
     const int qs = 4 * chunks;
     f4 acc = f4{0.f, 0.f, 0.f, 0.f};
@@ -29,22 +32,14 @@ __global__ __launch_bounds__(256) void norms_kernel(const float *__restrict__ X,
     if (valid && (li >> 2) == g) out[p] = acc[li & 3];
 }
 
-hipError_t launch_norms(const float *X, int64_t ldx, int64_t n, int d, float *out, hipStream_t s) {
-    if (n <= 0) return hipSuccess;
-    const int64_t waves = (n + 15) / 16;
-    hipLaunchKernelGGL(norms_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, X, ldx, n, d,
-                       feature_chunks(d), out);
-    return hipGetLastError();
-}
-
 // Point-major copy of a feature-major point set, for gathers of whole points:
-// Bt[j * dp + f] = B[f * ldb + j] for f < d, 0 for d <= f < dp.  32 x 32 tiles
-// through LDS (one padding column), coalesced on both sides.
-__global__ void point_major_kernel(const float *__restrict__ B, int64_t ldb, int64_t m, int d, int dp,
-                                   float *__restrict__ Bt) {
+// Bt[j * dp + f] = B[f * ldb + j] for f < d, 0 for d <= f < dp.  One 32 x 32
+// tile per workgroup, through LDS (one padding column), coalesced on both sides.
+__device__ __forceinline__ void point_major_block(const float *__restrict__ B, int64_t ldb, int64_t m, int d, int dp,
+                                                  float *__restrict__ Bt, int64_t bx, int by) {
     __shared__ float t[32][33];
-    const int64_t j0 = (int64_t)blockIdx.x * 32;
-    const int f0 = blockIdx.y * 32;
+    const int64_t j0 = bx * 32;
+    const int f0 = by * 32;
     const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
     for (int r = ty; r < 32; r += 8) {
         const int f = f0 + r;
@@ -59,11 +54,66 @@ __global__ void point_major_kernel(const float *__restrict__ B, int64_t ldb, int
     }
 }
 
-hipError_t launch_point_major(const float *B, int64_t ldb, int64_t m, int d, int dp, float *Bt, hipStream_t s) {
-    if (m <= 0) return hipSuccess;
-    hipLaunchKernelGGL(point_major_kernel, dim3((unsigned)((m + 31) / 32), (unsigned)((dp + 31) / 32)), dim3(256), 0,
-                       s, B, ldb, m, d, dp, Bt);
+namespace {
+constexpr int kNormPoints = 64; // points per norms workgroup
+int64_t norm_blocks(int64_t n) { return (n + kNormPoints - 1) / kNormPoints; }
+
+// The preparation of one kNN call in a single launch: norms of the queries,
+// norms of the database (unless it is the query set), and the database's
+// point-major copy (when Bt is set).  The workgroup index picks the part.
+struct PrepArgs {
+    const float *X, *Y;
+    int64_t ldx, n, ldy, m;
+    float *nx, *ny, *Bt;
+    int d, dp, chunks;
+    int64_t bx, by, tiles_x; // workgroups of the X norms, of the Y norms; point-major tiles per feature block
+};
+
+__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
+    const int64_t b = blockIdx.x;
+    if (b < a.bx) {
+        norms_block(a.X, a.ldx, a.n, a.d, a.chunks, a.nx, b);
+    } else if (b < a.bx + a.by) {
+        norms_block(a.Y, a.ldy, a.m, a.d, a.chunks, a.ny, b - a.bx);
+    } else {
+        const int64_t t = b - a.bx - a.by;
+        point_major_block(a.Y, a.ldy, a.m, a.d, a.dp, a.Bt, t % a.tiles_x, (int)(t / a.tiles_x));
+    }
+}
+} // namespace
+
+hipError_t launch_prep(const float *X, int64_t ldx, int64_t n, float *nx, const float *Y, int64_t ldy, int64_t m,
+                       float *ny, float *Bt, int d, int dp, hipStream_t s) {
+    PrepArgs a{};
+    a.X = X;
+    a.Y = Y;
+    a.ldx = ldx;
+    a.n = n;
+    a.ldy = ldy;
+    a.m = m;
+    a.nx = nx;
+    a.ny = ny;
+    a.Bt = Bt;
+    a.d = d;
+    a.dp = dp;
+    a.chunks = feature_chunks(d);
+    a.bx = nx ? norm_blocks(n) : 0;
+    a.by = ny ? norm_blocks(m) : 0;
+    a.tiles_x = (m + 31) / 32;
+    const int64_t pm = Bt ? a.tiles_x * ((dp + 31) / 32) : 0;
+    const int64_t blocks = a.bx + a.by + pm;
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
     return hipGetLastError();
+}
+
+hipError_t launch_norms(const float *X, int64_t ldx, int64_t n, int d, float *out, hipStream_t s) {
+    return launch_prep(X, ldx, n, out, X, ldx, 0, nullptr, nullptr, d, d, s);
+}
+
+hipError_t launch_point_major(const float *B, int64_t ldb, int64_t m, int d, int dp, float *Bt, hipStream_t s) {
+    return launch_prep(B, ldb, 0, nullptr, B, ldb, m, nullptr, Bt, d, dp, s);
 }
 
 // ---------------------------------------------------------------- kNN dispatch
