@@ -151,7 +151,7 @@ struct ChunkPlan {
     int splits;
 };
 
-constexpr int64_t kMaxLd = int64_t(1) << 25;
+constexpr int64_t kMaxLd = int64_t(1) << 48; // keeps f * ld + i within int64 for every f < EKH_MAX_DIM
 constexpr int64_t kMinTilesPerSplit = 4;
 constexpr int64_t kMaxSplits = 1024;     // a few query tiles against a long database fill the chip
 constexpr int64_t kCUs = 256;             // MI355X compute units (fixed, so that a workspace
@@ -253,9 +253,9 @@ KnnPlan plan_knn(int64_t n, int64_t m, int d, int k, int64_t max_chunk_dots, int
     return p;
 }
 
-inline int padded_dim(int d) { return (d + 3) & ~3; }
 
-// bt (kNN outputs only): point-major copy of the database for the rescore
+// bt: point-major copy of the database [m, tile_dim(d)], which the tiles and
+// the direct-difference kernels read
 size_t knn_ws(const KnnPlan &p, int64_t n, int64_t m, bool self, Carver &c, float **nx, float **ny, Entry **part,
               int32_t **idx_scratch = nullptr, int k = 0, float **bt = nullptr, int d = 0) {
     *nx = c.take<float>(n);
@@ -263,7 +263,7 @@ size_t knn_ws(const KnnPlan &p, int64_t n, int64_t m, bool self, Carver &c, floa
     // one split-list scratch per chunk in flight
     *part = p.part_entries ? c.take<Entry>((size_t)p.part_entries * p.conc) : nullptr;
     if (idx_scratch) *idx_scratch = c.take<int32_t>((size_t)n * k);
-    if (bt) *bt = c.take<float>((size_t)m * padded_dim(d));
+    if (bt) *bt = c.take<float>((size_t)m * tile_dim(d));
     return c.used;
 }
 
@@ -272,8 +272,7 @@ int check_points(const float *X, int64_t ld, int64_t n, int d, const char *name)
     if (n < 1 || n > INT32_MAX) return fail(EKH_EINVAL, "%s: number of points %lld out of range", name, (long long)n);
     if (d < 1 || d > EKH_MAX_DIM) return fail(EKH_EINVAL, "%s: d = %d out of range [1, %d]", name, d, EKH_MAX_DIM);
     if (ld < n) return fail(EKH_EINVAL, "%s: leading dimension %lld < n = %lld", name, (long long)ld, (long long)n);
-    // the tile loads address four feature rows with a 32-bit byte offset
-    if (ld >= kMaxLd) return fail(EKH_EINVAL, "%s: leading dimension %lld >= 2^25 is not supported", name, (long long)ld);
+    if (ld >= kMaxLd) return fail(EKH_EINVAL, "%s: leading dimension %lld >= 2^48", name, (long long)ld);
     return EKH_OK;
 }
 
@@ -329,8 +328,8 @@ int run_knn(const KnnPlan &p, const float *X, int64_t ldx, int64_t n, const floa
             bool self, int out_mode, int k_out, int min_samples, int32_t *out_idx, float *out_dist, float *out_core,
             float *nx, float *ny, Entry *part, float *bt, hipStream_t s, bool core_direct = false) {
     // norms of both sets and the database's point-major copy, in one launch
-    EKH_HIP(launch_prep(X, ldx, n, nx, Y, ldy, m, self ? nullptr : ny, (out_mode == kOutKnn || core_direct) ? bt : nullptr,
-                        d, padded_dim(d), s));
+    if (!bt) return fail(EKH_EINTERNAL, "no point-major scratch for the database");
+    EKH_HIP(launch_prep(X, ldx, n, nx, Y, ldy, m, self ? nullptr : ny, bt, d, tile_dim(d), s));
     hipStream_t cs[kChunkStreams] = {s};
     int forked = 1; // streams in use: the caller's, then those made to wait for it
     // After the fork every exit, an error included, first makes the caller's
@@ -368,8 +367,8 @@ int run_knn(const KnnPlan &p, const float *X, int64_t ldx, int64_t n, const floa
         a.q0 = q0;
         a.nq = std::min<int64_t>(p.rows, n - q0);
         a.nrm_q = nx;
-        a.B = Y;
-        a.ldb = ldy;
+        a.Bt = bt;
+        a.dp = tile_dim(d);
         a.m = m;
         a.nrm_b = ny;
         a.d = d;
@@ -414,7 +413,7 @@ int run_knn(const KnnPlan &p, const float *X, int64_t ldx, int64_t n, const floa
         a.out_idx = out_idx;
         a.out_dist = out_dist;
         a.Bt = bt;
-        a.dp = padded_dim(d);
+        a.dp = tile_dim(d);
         EKH_HIP(launch_knn_rescore(p.K, a, s));
     } else if (core_direct) {
         KnnArgs a{};
@@ -429,7 +428,7 @@ int run_knn(const KnnPlan &p, const float *X, int64_t ldx, int64_t n, const floa
         a.out_idx = out_idx;
         a.out_core = out_core;
         a.Bt = bt;
-        a.dp = padded_dim(d);
+        a.dp = tile_dim(d);
         EKH_HIP(launch_knn_core(p.K, a, s));
     }
     return EKH_OK;
@@ -454,8 +453,8 @@ struct MstWs {
     float *nbr_d2;
     float *knn_nx;
     Entry *knn_part;
-    float *xs; // points outside the largest component, feature-major [d, <= n / 2]
-    float *pm; // point-major copy [n, padded_dim(d)] for the reported edge weights
+    float *xs; // points outside the largest component, point-major [<= n / 2, tile_dim(d)]
+    float *pm; // point-major copy [n, tile_dim(d)]: the scans' database and the reported edge weights
 };
 
 size_t carve_mst(Carver &c, int64_t n, int d, int ms, bool with_nb, MstWs &w) {
@@ -486,8 +485,8 @@ size_t carve_mst(Carver &c, int64_t n, int d, int ms, bool with_nb, MstWs &w) {
     // its points' features here; orig, labels, sizes and the second active list
     // in the edge sort's u32 scratch (sb, sc, sd, sa), norms and core distances
     // in s64a -- all idle until the final sort
-    w.xs = c.take<float>((size_t)d * (size_t)(n / 2 + 1));
-    w.pm = c.take<float>((size_t)n * (size_t)padded_dim(d));
+    w.xs = c.take<float>((size_t)tile_dim(d) * (size_t)(n / 2 + 1));
+    w.pm = c.take<float>((size_t)n * (size_t)tile_dim(d));
     w.nbr_idx = nullptr;
     w.nbr_d2 = nullptr;
     w.knn_nx = nullptr;
@@ -497,7 +496,7 @@ size_t carve_mst(Carver &c, int64_t n, int d, int ms, bool with_nb, MstWs &w) {
         w.nbr_idx = c.take<int32_t>((size_t)n * K);
         w.nbr_d2 = c.take<float>((size_t)n * K);
         const KnnPlan p = plan_knn(n, n, d, K, 0);
-        float *ny;
+        float *ny; // knn_ws also carves norms, unused here: the call writes w.nrm
         knn_ws(p, n, n, true, c, &w.knn_nx, &ny, &w.knn_part);
     }
     return c.used;
@@ -674,16 +673,19 @@ int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const flo
     const int K = min_samples + 1;
 
     if (!with_nb) {
-        // the self-kNN rows (K = min_samples + 1) the shortcuts read
+        // the self-kNN rows (K = min_samples + 1) the shortcuts read; the call
+        // also leaves the norms and the point-major copy of X
         const KnnPlan p = plan_knn(n, n, d, K, 0);
         float *scratch_core = (float *)w.sa; // core as computed here is not used: the caller's core rules
         if ((rc = run_knn(p, X, ldx, n, X, ldx, n, d, true, kOutCore, K, min_samples, w.nbr_idx, w.nbr_d2,
-                          scratch_core, w.knn_nx, w.knn_nx, w.knn_part, nullptr, s)) != EKH_OK)
+                          scratch_core, w.nrm, w.nrm, w.knn_part, w.pm, s)) != EKH_OK)
             return rc;
         nbr_idx = w.nbr_idx;
         nbr_d2 = w.nbr_d2;
+    } else {
+        // norms and the point-major copy of X, in one launch
+        EKH_HIP(launch_prep(X, ldx, n, w.nrm, X, ldx, n, nullptr, w.pm, d, tile_dim(d), s));
     }
-    EKH_HIP(launch_norms(X, ldx, n, d, w.nrm, s));
 
     BvState st{};
     st.n = n;
@@ -750,8 +752,8 @@ int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const flo
         EKH_HIP(bv_reset_counters(st, s));
         EKH_HIP(bv_candidates(st, use_nb, use_bound, s));
         EKH_HIP(bv_select_active(st, use_bound, split_giant, s));
-        sa.Xb = X;
-        sa.ldb = ldx;
+        sa.Xb = w.pm;
+        sa.dp = tile_dim(d);
         sa.nb = n;
         sa.nrm_b = w.nrm;
         sa.core_b = core;
@@ -770,10 +772,9 @@ int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const flo
             float *nrm_s = reinterpret_cast<float *>(w.s64a), *core_s = nrm_s + (n / 2 + 1);
             // both do nothing when no active point of the component was listed
             EKH_HIP(bv_complement(st, g, orig, s));
-            EKH_HIP(bv_gather_points(X, ldx, d, orig, ns, w.nrm, core, w.comp, w.xs, nrm_s, core_s, comp_s,
+            EKH_HIP(bv_gather_points(w.pm, tile_dim(d), orig, ns, w.nrm, core, w.comp, w.xs, nrm_s, core_s, comp_s,
                                      &w.ctr->n_comp_g, &w.ctr->n_active_g, s));
             sa.Xb = w.xs;
-            sa.ldb = ns;
             sa.nb = ns;
             sa.nrm_b = nrm_s;
             sa.core_b = core_s;
@@ -821,8 +822,7 @@ int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const flo
     if ((int64_t)h.n_edges != n - 1)
         return fail(EKH_EINTERNAL, "tree has %u edges, expected %lld", h.n_edges, (long long)(n - 1));
     // each edge's reported weight by direct differences, then the (w, lo, hi) order
-    EKH_HIP(launch_point_major(X, ldx, n, d, padded_dim(d), w.pm, s));
-    EKH_HIP(bv_edge_weights(w.pm, padded_dim(d), core, w.e_lo, w.e_hi, n - 1, n, w.e_w, s));
+    EKH_HIP(bv_edge_weights(w.pm, tile_dim(d), core, w.e_lo, w.e_hi, n - 1, n, w.e_w, s));
     EKH_HIP(edge_sort(w.e_lo, w.e_hi, w.e_w, n - 1, w.sort_tmp, w.sort_tmp_bytes, w.sa, w.sb, w.sc, w.sd, w.s64a,
                       w.s64b, out_lo, out_hi, out_w, s));
     return EKH_OK;

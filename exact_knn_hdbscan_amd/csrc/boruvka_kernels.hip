@@ -13,6 +13,7 @@
 namespace ekh {
 
 static inline dim3 grid_for(int64_t n, int bs) { return dim3((unsigned)((n + bs - 1) / bs)); }
+typedef float f4v __attribute__((ext_vector_type(4)));
 constexpr int kBs = 256;
 // Per-point passes whose atomics go to few addresses late in the run (a
 // component's minimum, a global counter) combine them per workgroup in LDS
@@ -312,37 +313,50 @@ hipError_t bv_complement(const BvState &st, int32_t giant, int32_t *orig, hipStr
 // Feature-major copy [d, ns] of the listed points with their norms, core
 // distances and labels (writes coalesced along the list).  Only the first
 // *count (<= ns) list entries are read; with *gate == 0 nothing is done.
-__global__ __launch_bounds__(kBs) void bv_gather_points_kernel(const float *X, int64_t ldx, int d,
-                                                                const int32_t *orig, int64_t ns, const float *nrm,
-                                                                const float *core, const int32_t *comp, float *xs,
-                                                                float *nrm_s, float *core_s, int32_t *comp_s,
-                                                                const uint32_t *count, const uint32_t *gate) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// One thread per 16-byte piece of a gathered row (dp / 4 pieces per row, so a
+// wave copies whole rows contiguously); the row's first thread also copies its
+// norm, core distance and label.
+__global__ __launch_bounds__(kBs) void bv_gather_points_kernel(const float *P, int dp, const int32_t *orig,
+                                                                int64_t ns, const float *nrm, const float *core,
+                                                                const int32_t *comp, float *xs, float *nrm_s,
+                                                                float *core_s, int32_t *comp_s, const uint32_t *count,
+                                                                const uint32_t *gate) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gate && __hip_atomic_load(gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) return;
     const int64_t listed = count ? (int64_t)__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : ns;
+    const int ppr = dp / 4;
+    const int64_t i = t / ppr;
+    const int piece = (int)(t - i * ppr);
     if (i >= ns) return;
+    f4v *dst = reinterpret_cast<f4v *>(xs + i * dp) + piece;
     if (i >= listed) {
         // fewer points listed than the host sized the copy for (it reports the
         // mismatch after the round): such rows carry the padding label and
         // never form an edge
-        nrm_s[i] = INFINITY;
-        core_s[i] = INFINITY;
-        comp_s[i] = -1;
+        *dst = f4v{0.f, 0.f, 0.f, 0.f};
+        if (piece == 0) {
+            nrm_s[i] = INFINITY;
+            core_s[i] = INFINITY;
+            comp_s[i] = -1;
+        }
         return;
     }
     const int32_t p = orig[i];
-    for (int f = 0; f < d; ++f) xs[(int64_t)f * ns + i] = X[(int64_t)f * ldx + p];
-    nrm_s[i] = nrm[p];
-    core_s[i] = core[p];
-    comp_s[i] = comp[p];
+    *dst = reinterpret_cast<const f4v *>(P + (int64_t)p * dp)[piece];
+    if (piece == 0) {
+        nrm_s[i] = nrm[p];
+        core_s[i] = core[p];
+        comp_s[i] = comp[p];
+    }
 }
 
-hipError_t bv_gather_points(const float *X, int64_t ldx, int d, const int32_t *orig, int64_t ns, const float *nrm,
+hipError_t bv_gather_points(const float *P, int dp, const int32_t *orig, int64_t ns, const float *nrm,
                             const float *core, const int32_t *comp, float *xs, float *nrm_s, float *core_s,
                             int32_t *comp_s, const uint32_t *count, const uint32_t *gate, hipStream_t s) {
     if (ns <= 0) return hipSuccess;
-    hipLaunchKernelGGL(bv_gather_points_kernel, grid_for(ns, kBs), dim3(kBs), 0, s, X, ldx, d, orig, ns, nrm, core,
-                       comp, xs, nrm_s, core_s, comp_s, count, gate);
+    if (dp <= 0 || dp % 4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(bv_gather_points_kernel, grid_for(ns * (dp / 4), kBs), dim3(kBs), 0, s, P, dp, orig, ns, nrm,
+                       core, comp, xs, nrm_s, core_s, comp_s, count, gate);
     return hipGetLastError();
 }
 

@@ -53,6 +53,9 @@ inline int scan_query_tile(int QM) { return kWaves * 16 * scan_col_blocks(QM); }
 // 16-feature chunks actually run for dimension d (identical in every kernel,
 // which keeps D2 bitwise the same everywhere)
 inline int feature_chunks(int d) { return (d + 15) / 16; }
+// row stride (floats) of the point-major copies the tiles read: every feature a
+// tile loads, zero past d
+inline int tile_dim(int d) { return 16 * feature_chunks(d); }
 
 // Correctly rounded float32 square root.  (__fsqrt_rn lowers to the native,
 // approximate instruction in this toolchain; __builtin_sqrtf gets the correctly
@@ -80,9 +83,7 @@ struct KnnArgs {
     int64_t q0;       // first query row of this chunk
     int64_t nq;       // rows in this chunk
     const float *nrm_q; // |q|^2, indexed by absolute row
-    const float *B;   // database [d, m] (ld ldb)
-    int64_t ldb;
-    int64_t m;
+    int64_t m;        // database points
     const float *nrm_b; // |b|^2 [m]
     int d;
     int chunks;       // feature_chunks(d)
@@ -97,12 +98,11 @@ struct KnnArgs {
     int32_t *out_idx; // [n, k_out] absolute rows
     float *out_dist;  // [n, k_out] (kOutKnn) or d2 lists (kOutCore)
     float *out_core;  // [n]
-    const float *Bt;  // database point-major [m, dp] (rescore only)
-    int dp;           // row stride of Bt: d rounded up to a multiple of 4, zero padded
+    const float *Bt;  // database point-major [m, dp], features >= d zero (the tiles and the direct differences read it)
+    int dp;           // row stride of Bt: tile_dim(d) = 16 * feature_chunks(d)
 };
 
 // host launchers (return hipError_t of the launch)
-hipError_t launch_norms(const float *X, int64_t ldx, int64_t n, int d, float *out, hipStream_t s);
 // Norms of X (into nx), of Y when ny is set, and Y's point-major copy when Bt is
 // set, in one launch.
 hipError_t launch_prep(const float *X, int64_t ldx, int64_t n, float *nx, const float *Y, int64_t ldy, int64_t m,
@@ -111,7 +111,6 @@ hipError_t launch_knn_tile(int K, int QM, const KnnArgs &a, hipStream_t s);
 hipError_t launch_knn_merge(int K, const KnnArgs &a, hipStream_t s);
 hipError_t launch_knn_rescore(int K, const KnnArgs &a, hipStream_t s);
 hipError_t launch_knn_core(int K, const KnnArgs &a, hipStream_t s);
-hipError_t launch_point_major(const float *B, int64_t ldb, int64_t m, int d, int dp, float *Bt, hipStream_t s);
 
 // ---- Boruvka ---------------------------------------------------------------
 constexpr uint64_t kNoEdge = ~0ull;
@@ -137,9 +136,10 @@ struct ScanArgs {
     const float *nrm;     // |x|^2 [n]
     const float *core;    // [n]
     const int32_t *comp;  // component label of every point
-    // database side: all points, or a gathered subset whose row j is point orig[j]
+    // database side, point-major rows [nb, dp] (features >= d zero): all
+    // points, or a gathered subset whose row j is point orig[j]
     const float *Xb;
-    int64_t ldb;
+    int dp;
     int64_t nb;
     const float *nrm_b;
     const float *core_b;
@@ -191,7 +191,8 @@ hipError_t bv_candidates(const BvState &st, int use_neighbour_edges, int use_bou
 hipError_t bv_select_active(const BvState &st, int use_bound, int split_giant, hipStream_t s);
 hipError_t bv_giant(const BvState &st, hipStream_t s);
 hipError_t bv_complement(const BvState &st, int32_t giant, int32_t *orig, hipStream_t s);
-hipError_t bv_gather_points(const float *X, int64_t ldx, int d, const int32_t *orig, int64_t ns, const float *nrm,
+// rows orig[0 .. ns) of the point-major copy P [n, dp] into xs [ns, dp], with their norms, core distances and labels
+hipError_t bv_gather_points(const float *P, int dp, const int32_t *orig, int64_t ns, const float *nrm,
                             const float *core, const int32_t *comp, float *xs, float *nrm_s, float *core_s,
                             int32_t *comp_s, const uint32_t *count, const uint32_t *gate, hipStream_t s);
 hipError_t bv_component_min(const BvState &st, hipStream_t s);

@@ -47,9 +47,8 @@ template <int QM> struct Tile {
     static constexpr int RB = TR / 16;          // 16-row blocks per tile
     static constexpr int FD = QM * 4;           // features held (d <= FD)
     static constexpr int RS = FD + 4;           // LDS row stride in floats: 16-byte reads of 8 rows hit distinct banks
-    static constexpr int FSTEP = kThreads / TR; // threads per row: thread q of a row holds feature chunks q, q + FSTEP, ...
-    static constexpr int PF = FD / FSTEP;       // prefetch registers per thread
-    static_assert(FD % (4 * FSTEP) == 0, "tile shape");
+    static constexpr int NL = TR * QM / kThreads; // 16-byte pieces each thread loads per tile (at d = FD)
+    static_assert((TR * QM) % kThreads == 0, "tile shape");
 };
 
 // Streams database tiles [t_begin, t_end) through a double-buffered LDS tile
@@ -62,14 +61,23 @@ template <int QM> struct Tile {
 // norms (and, with PAYLOAD, component labels and core distances) live in a
 // three-slot ring; tile t's are in slot (t - t_begin) mod 3.  FULL: the
 // dimension fills all QM k-steps, so the k-loop has no runtime guard.
+//
+// The database is read from its point-major copy Bp: row j holds features
+// 0 .. dp - 1 of point j with dp = 16 * chunks (features >= d are zero), so a
+// tile is one contiguous block of TR * dp floats.  Thread tid loads its 16-byte
+// pieces tid, tid + 256, ... of the block (coalesced) with buffer loads whose
+// base is the tile's first row (a scalar) and whose lane offsets never change;
+// each piece goes to LDS with one 16-byte store.  Point counts are below 2^31,
+// so tile and row counters are 32-bit scalars.
 template <int QM, int CB, bool PAYLOAD, bool FULL, class Epi>
-__device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t ldb, int64_t m,
+__device__ __forceinline__ void run_tiles(const float *__restrict__ Bp, int dp, int32_t m_,
                                           const float *__restrict__ nrm_b, const int32_t *__restrict__ comp_b,
-                                          const float *__restrict__ core_b, int d, int chunks, int64_t t_begin_,
-                                          int64_t t_end_, const float (&bq)[CB][QM], Epi &epi) {
+                                          const float *__restrict__ core_b, int chunks, int32_t t_begin_,
+                                          int32_t t_end_, const float (&bq)[CB][QM], Epi &epi) {
     using T = Tile<QM>;
-    const int64_t t_begin = uniform64(t_begin_), t_end = uniform64(t_end_);
-    m = uniform64(m);
+    const uint32_t t_begin = __builtin_amdgcn_readfirstlane((uint32_t)t_begin_);
+    const uint32_t t_end = __builtin_amdgcn_readfirstlane((uint32_t)t_end_);
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)m_);
     __shared__ __align__(16) float sm_tile[2][T::TR * T::RS];
     __shared__ __align__(16) float sm_nrm[3][T::TR];
     __shared__ int32_t sm_comp[3][PAYLOAD ? T::TR : 1];
@@ -77,53 +85,33 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, g = lane >> 4, li = lane & 15;
-    // loader: thread (lrow, lq) reads 4-feature chunks lq, lq + FSTEP, ... of row
-    // lrow; a wave's loads cover 32 consecutive rows of two feature rows each
-    // (coalesced), and each chunk goes to LDS as one 16-byte store (eight
-    // consecutive rows of one chunk lie in distinct banks, RS = 4 mod 32).
-    const int lrow = tid % T::TR, lq = tid / T::TR;
     const int qs = FULL ? QM : 4 * chunks; // k-steps run
-    const int fused = 4 * qs;
+    const int ppr = FULL ? QM : qs;        // 16-byte pieces per row (dp / 4)
+    const int pieces = T::TR * ppr;        // per tile
+
+    // this thread's pieces: LDS position (row * RS + 4 * column) and whether
+    // the piece exists at this dimension
+    int lds_off[T::NL];
+    bool has[T::NL];
+#pragma unroll
+    for (int h = 0; h < T::NL; ++h) {
+        const int c = tid + kThreads * h;
+        has[h] = FULL || c < pieces;
+        const int row = c / ppr, col = c - row * ppr;
+        lds_off[h] = row * T::RS + 4 * col;
+    }
+    const int lrow = tid % T::TR; // the thread also loads row lrow's norm (and payload)
+    // in a database of fewer rows than one tile, the lanes past its end read
+    // row m - 1 instead (with an infinite norm)
+    const uint32_t lr = m < (uint32_t)T::TR && (uint32_t)lrow >= m ? m - 1 : (uint32_t)lrow;
 
     struct Pref {
-        float v[T::PF];
+        f4 v[T::NL];
         float n, core;
         int32_t comp;
-        bool nv;      // a row of this tile (else an infinite norm)
-        int64_t row0; // first row read
+        bool nv;       // a row of this tile (else an infinite norm)
+        uint32_t row0; // first row read
     };
-    // Loads: raw buffer loads whose resource is a wave-uniform base per feature
-    // row (scalar registers, advanced per tile) and whose per-lane 32-bit offset
-    // never changes, so a tile's loads take no vector address arithmetic.  The
-    // 64 / TR lane groups of a wave read rows lrow of feature rows f, f + 4,
-    // f + 8, ... (lq = (64 / TR) w + group), so an offset is at most
-    // 4 (64 / TR - 1) ld + TR - 1 floats (the host keeps ld below 2^25).  A
-    // feature >= d reads feature d - 1 instead: finite values that meet
-    // zero-padded query features, so their products are exactly 0 and no mask
-    // is needed.  A partial last tile is read as rows m - TR .. m - 1 (a scalar
-    // change of base); its rows before the tile belong to the previous one and
-    // get an infinite norm, so they never qualify.  In a database of fewer than
-    // TR rows, the lanes past its end read row m - 1 (set once in their
-    // offsets), also with an infinite norm.
-    static_assert(64 % T::TR == 0, "a wave covers whole rows of lane groups");
-    constexpr int kGroups = 64 / T::TR;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = (tid & 63) / T::TR; // lq == kGroups * wv + grp
-    const float *fbase[T::PF];
-    uint32_t foff[T::PF];
-    // a database of fewer rows than one tile (one tile, rows 0 .. TR - 1): the
-    // lanes past its end read row m - 1 instead
-    const int64_t lr = m < T::TR && lrow >= m ? m - 1 : lrow;
-#pragma unroll
-    for (int p = 0; p < T::PF; ++p) {
-        const int f_lo = 4 * (kGroups * wv + (p >> 2) * T::FSTEP) + (p & 3);
-        const int fl = f_lo < d ? f_lo : d - 1, fa = f_lo + 4 * grp < d ? f_lo + 4 * grp : d - 1;
-        fbase[p] = B + (int64_t)fl * ldb;
-        foff[p] = (uint32_t)((int64_t)(fa - fl) * ldb + lr) * 4u;
-    }
-    const uint32_t noff = (uint32_t)lr * 4u; // lrow == tid % TR: the thread also loads row lrow's norm
-    // the tile's base address as an explicit scalar, so that it is not folded
-    // into per-lane 64-bit pointers (the load then adds the 32-bit lane offset)
     typedef const char __attribute__((address_space(1))) *gchar;
     auto sbase = [](const void *ptr) {
         const uint64_t x = reinterpret_cast<uint64_t>(ptr);
@@ -131,42 +119,47 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
         const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
         return (gchar)(((uint64_t)hi << 32) | lo);
     };
-    // raw buffer load: resource from the scalar base (2^31 bytes of range), the
-    // 32-bit lane offset in voffset; a full tile never leaves the buffer
-    auto ld32 = [](gchar base, uint32_t off) {
-        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(const char *)base, (short)0, 0x7fffffff, 0x00020000);
-        return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    // raw buffer loads from a scalar base; bytes past `bytes` read as zero
+    auto rsrc = [](gchar base, uint32_t bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc((void *)(const char *)base, (short)0, (int)bytes, 0x00020000);
     };
+    const uint32_t row_bytes = __builtin_amdgcn_readfirstlane((uint32_t)dp * 4u);
     // One load sequence for every tile, with no address arithmetic (a branch
     // around the loads would cost the wait counts that let the next tile's
-    // loads overlap this tile's MFMAs).
-    auto load = [&](Pref &P, int64_t t) {
-        const int64_t tt = t < t_end ? t : t_end - 1;
-        const int64_t rt = tt * T::TR; // the tile's first row
-        const bool part = rt + T::TR > m;
-        const int64_t row0 = uniform64(part && m >= T::TR ? m - T::TR : rt);
+    // loads overlap this tile's MFMAs).  A partial last tile is read as rows
+    // m - TR .. m - 1 (a change of base); its rows before the tile belong to
+    // the previous one and get an infinite norm, so they never qualify.
+    auto load = [&](Pref &P, uint32_t t) {
+        const uint32_t tt = t < t_end ? t : t_end - 1;
+        const uint32_t rt = tt * (uint32_t)T::TR; // the tile's first row (< 2^32: m < 2^31)
+        const bool part = rt + (uint32_t)T::TR > m;
+        const uint32_t row0 = __builtin_amdgcn_readfirstlane(part && m >= (uint32_t)T::TR ? m - T::TR : rt);
         P.row0 = row0;
         // rows lrow in [lo, hi) belong to this tile (scalar bounds)
-        const int lo = part && m >= T::TR ? (int)(rt - row0) : 0;
-        const int hi = part && m < T::TR ? (int)m : T::TR;
-        P.nv = lrow >= lo && lrow < hi;
+        const uint32_t lo = part && m >= (uint32_t)T::TR ? rt - row0 : 0u;
+        const uint32_t hi = part && m < (uint32_t)T::TR ? m : (uint32_t)T::TR;
+        P.nv = (uint32_t)lrow >= lo && (uint32_t)lrow < hi;
+        const uint32_t rows = m - row0 < (uint32_t)T::TR ? m - row0 : (uint32_t)T::TR;
+        const auto r = rsrc(sbase(Bp + (uint64_t)row0 * (uint32_t)dp), rows * row_bytes);
+        // pieces past the tile (a dimension below FD) lie past the resource's
+        // end: they read as zeros and are not stored
 #pragma unroll
-        for (int p = 0; p < T::PF; ++p) P.v[p] = __uint_as_float(ld32(sbase(fbase[p] + row0), foff[p]));
-        P.n = __uint_as_float(ld32(sbase(nrm_b + row0), noff));
+        for (int h = 0; h < T::NL; ++h) {
+            const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (tid + kThreads * h) * 16, 0, 0);
+            P.v[h] = f4{__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]), __uint_as_float(x[3])};
+        }
+        const auto rn = rsrc(sbase(nrm_b + row0), 0x7fffffff);
+        P.n = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rn, lr * 4u, 0, 0));
         if (PAYLOAD) {
-            P.comp = (int32_t)ld32(sbase(comp_b + row0), noff);
-            P.core = __uint_as_float(ld32(sbase(core_b + row0), noff));
+            P.comp = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc(sbase(comp_b + row0), 0x7fffffff), lr * 4u, 0, 0);
+            P.core = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rsrc(sbase(core_b + row0), 0x7fffffff), lr * 4u, 0, 0));
         }
     };
     auto store = [&](const Pref &P, int buf, int slot) {
 #pragma unroll
-        for (int h = 0; h < T::PF / 4; ++h) {
-            const int f0 = 4 * (lq + h * T::FSTEP);
-            if (FULL || f0 < fused)
-                *reinterpret_cast<f4 *>(sm_tile[buf] + lrow * T::RS + f0) =
-                    f4{P.v[4 * h], P.v[4 * h + 1], P.v[4 * h + 2], P.v[4 * h + 3]};
-        }
+        for (int h = 0; h < T::NL; ++h)
+            if (has[h]) *reinterpret_cast<f4 *>(sm_tile[buf] + lds_off[h]) = P.v[h];
         if (tid < T::TR) {
             sm_nrm[slot][tid] = P.nv ? P.n : INFINITY; // padding rows never qualify
             if (PAYLOAD) {
@@ -219,8 +212,9 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
             }
         }
     };
-    auto finish = [&](const f4 (&acc)[T::RB][CB], int64_t row0, int slot) {
-        epi.tile(acc, sm_nrm[slot], PAYLOAD ? sm_comp[slot] : nullptr, PAYLOAD ? sm_core[slot] : nullptr, row0);
+    auto finish = [&](const f4 (&acc)[T::RB][CB], uint32_t row0, int slot) {
+        epi.tile(acc, sm_nrm[slot], PAYLOAD ? sm_comp[slot] : nullptr, PAYLOAD ? sm_core[slot] : nullptr,
+                 (int64_t)row0);
     };
 
     if (t_begin >= t_end) return;
@@ -229,9 +223,9 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ B, int64_t l
     store(P, 0, 0);
     __syncthreads();
     f4 acc[T::RB][CB];
-    int buf = 0, sl = 0;         // tile t's LDS buffer and norm slot
-    int64_t rcur = P.row0;       // and its first row
-    for (int64_t t = t_begin; t < t_end; ++t) {
+    int buf = 0, sl = 0;    // tile t's LDS buffer and norm slot
+    uint32_t rcur = P.row0; // and its first row
+    for (uint32_t t = t_begin; t < t_end; ++t) {
         const int sn = sl == 2 ? 0 : sl + 1;
         if (t + 1 < t_end) load(P, t + 1);
         mma(buf, acc);
@@ -628,7 +622,8 @@ void knn_tile_kernel(KnnArgs a) {
     epi.g = g;
     epi.sv = sv;
     epi.tid = tid;
-    run_tiles<QM, CB, false, FULL>(a.B, a.ldb, a.m, a.nrm_b, nullptr, nullptr, a.d, a.chunks, tb, te, bq, epi);
+    run_tiles<QM, CB, false, FULL>(a.Bt, a.dp, (int32_t)a.m, a.nrm_b, nullptr, nullptr, a.chunks, (int32_t)tb,
+                                   (int32_t)te, bq, epi);
 
     // merge the four lane groups that share each query column
 #pragma unroll

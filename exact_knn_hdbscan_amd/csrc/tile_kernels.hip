@@ -108,13 +108,6 @@ hipError_t launch_prep(const float *X, int64_t ldx, int64_t n, float *nx, const 
     return hipGetLastError();
 }
 
-hipError_t launch_norms(const float *X, int64_t ldx, int64_t n, int d, float *out, hipStream_t s) {
-    return launch_prep(X, ldx, n, out, X, ldx, 0, nullptr, nullptr, d, d, s);
-}
-
-hipError_t launch_point_major(const float *B, int64_t ldb, int64_t m, int d, int dp, float *Bt, hipStream_t s) {
-    return launch_prep(B, ldb, 0, nullptr, B, ldb, m, nullptr, Bt, d, dp, s);
-}
 
 // ---------------------------------------------------------------- kNN dispatch
 hipError_t launch_knn_tile(int K, int QM, const KnnArgs &a, hipStream_t s) {
@@ -285,8 +278,8 @@ void scan_tile_kernel(ScanArgs a) {
             epi.thr[cb] = (!valid[cb] || epi.corea[cb] > w0) ? -INFINITY : scan_threshold(w0);
         }
         const int64_t tb = a.tiles * split / sp, te = a.tiles * (split + 1) / sp;
-        run_tiles<QM, CB, true, FULL>(a.Xb, a.ldb, a.nb, a.nrm_b, a.comp_b, a.core_b, a.d, a.chunks, tb, te, bq,
-                                      epi);
+        run_tiles<QM, CB, true, FULL>(a.Xb, a.dp, (int32_t)a.nb, a.nrm_b, a.comp_b, a.core_b, a.chunks, (int32_t)tb,
+                                      (int32_t)te, bq, epi);
 
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {

@@ -22,12 +22,12 @@
  *
  * Conventions shared by every entry point
  *  - Point sets are feature-major: point i of X has feature f at
- *    X[f * ldx + i] (any n, m, d and ld, odd values included, within two
- *    limits the pages do not set): d <= EKH_MAX_DIM = 256, the widest form
- *    the tile kernels hold in registers (the pages' sets have 60 to 200
- *    features); and n <= ldx < 2^25 (33.5 million points), which keeps the
- *    tile loads' byte offsets within 32 bits, far past where an exact O(n^2)
- *    search is practical.
+ *    X[f * ldx + i] (any n, m, d and ld, odd values included), with
+ *    n <= ldx < 2^48 and d <= EKH_MAX_DIM = 256, the widest form the tile
+ *    kernels hold in registers (a limit the pages do not set; their sets
+ *    have 60 to 200 features).  The calls read the database through a
+ *    point-major copy in the workspace, so the leading dimension does not
+ *    enter any tile address.
  *    X, Y, outputs and the workspace are DEVICE pointers owned by the caller;
  *    the library never allocates or frees caller memory.
  *  - State kept between calls (a reading; the pages are silent on it): the
@@ -104,7 +104,10 @@ size_t ekh_knn_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t k, int64
  *      max_chunk_dots / m rows (at least one row tile), each chunk a separate
  *      launch sequence whose scratch is sized for that chunk (MAX_CHUNK_DOTS on
  *      the page); 0 = one chunk.  Results do not depend on it.
- *  ws, ws_bytes: device scratch of at least ekh_knn_workspace_bytes().
+ *  ws, ws_bytes: device scratch of at least ekh_knn_workspace_bytes() (norms,
+ *      split lists, the list indices when out_idx is NULL, and a point-major
+ *      copy of Y [m, 16 ceil(d / 16)] that the tiles stream and the reported
+ *      distances gather from).
  */
 int ekh_knn(const float *X, int64_t ldx, int64_t n, const float *Y, int64_t ldy, int64_t m, int32_t d, int32_t k,
             int32_t *out_idx, float *out_dist, int64_t max_chunk_dots, void *ws, size_t ws_bytes, void *stream);
@@ -170,7 +173,8 @@ size_t ekh_core_workspace_bytes(int64_t n, int32_t d, int32_t min_samples);
  *      (D2, index), self included with D2 = 0; D2 here is the GEMM form, the
  *      value ekh_mst_boruvka's scan computes for the same pair bit for bit.
  *  ws: at least ekh_core_workspace_bytes() (norms, split lists, a point-major
- *      copy of X for the direct differences and the list indices).
+ *      copy of X [n, 16 ceil(d / 16)] that the tiles stream and the direct
+ *      differences gather from, and the list indices).
  */
 int ekh_core_distances(const float *X, int64_t ldx, int64_t n, int32_t d, int32_t min_samples, float *out_core,
                        int32_t *out_nbr_idx, float *out_nbr_d2, void *ws, size_t ws_bytes, void *stream);
@@ -230,9 +234,10 @@ size_t ekh_mst_workspace_bytes(int64_t n, int32_t d, int32_t min_samples, int wi
  *  stats: optional host struct filled per round.
  *  Blocks the host once per round (one read-back of the round's counters);
  *  the scans find the number of points to scan on the device.
- *  ws: at least ekh_mst_workspace_bytes() (round state, the complement copy,
- *      a point-major copy of X for the reported weights, sort buffers, and the
- *      lists when they are recomputed).
+ *  ws: at least ekh_mst_workspace_bytes() (round state, a point-major copy
+ *      of X [n, 16 ceil(d / 16)] that the scans stream and the reported weights
+ *      gather from, the gathered complement of the largest component, sort
+ *      buffers, and the lists when they are recomputed).
  *  Requires 1 <= min_samples < n for n >= 2.  At most ceil(log2 n) rounds;
  *  more returns EKH_EINTERNAL.
  */

@@ -113,7 +113,7 @@ BOGUS = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
 
 @pytest.mark.parametrize("args,code", [
     (dict(n=0), -1), (dict(d=0), -1), (dict(d=257), -1), (dict(k=0), -1), (dict(k=33), -1),
-    (dict(k=11, m=10), -1), (dict(ldx=99), -1), (dict(ldx=1 << 25), -1), (dict(ldy=1 << 25), -1),
+    (dict(k=11, m=10), -1), (dict(ldx=99), -1), (dict(ldx=1 << 48), -1), (dict(ldy=1 << 48), -1),
     (dict(X=None), -1), (dict(ws_bytes=1), -2),
 ])
 def test_knn_rejects_bad_arguments(lib, args, code):
@@ -181,7 +181,7 @@ def test_kmeanspp_rejects_bad_arguments(lib):
 
 
 @pytest.mark.parametrize("args,code", [
-    (dict(n=0), -1), (dict(d=257), -1), (dict(k=33), -1), (dict(ldx=1 << 25), -1), (dict(X=None), -1),
+    (dict(n=0), -1), (dict(d=257), -1), (dict(k=33), -1), (dict(ldx=1 << 48), -1), (dict(X=None), -1),
     # sizes whose scratch exceeds the static array: refused before any GPU call
     (dict(n=400000, ldx=400000, m=400000, ldy=400000, d=61, k=11), -2),
 ])

@@ -6,7 +6,7 @@ import exact_knn_hdbscan_amd as ekh
 import oracle
 from exact_knn_hdbscan_amd import datagen
 from gpu_util import dev, host, say
-from parity import check_core, check_knn
+from parity import REL_D, check_core, check_knn
 
 pytestmark = pytest.mark.gpu
 
@@ -34,6 +34,21 @@ def test_knn_odd_sizes_and_leading_dimension():
     say("knn odd n=2001 m=777 d=61 ld padded")
     i, dd = ekh.knn(dev(X, ld=2011), dev(Y, ld=781), 10)
     check_knn(X, Y, 10, host(i), host(dd), rescored=True)
+
+
+def test_knn_and_core_leading_dimension_past_2_25():
+    """A leading dimension of 2^25 + 17 floats (the tiles read the point-major
+    copy, so no tile address depends on it): ekh_knn and ekh_core_distances."""
+    ld = (1 << 25) + 17
+    X = datagen.gaussian_mixture(1500, 3, 4, seed=11)
+    Y = datagen.gaussian_mixture(1201, 3, 4, seed=12)
+    say("knn and core, d=3, ld = 2^25 + 17")
+    i, dd = ekh.knn(dev(X, ld=ld), dev(Y, ld=ld), 7)
+    check_knn(X, Y, 7, host(i), host(dd), rescored=True)
+    rep = {}
+    core = ekh.core_distances(dev(X, ld=ld), 5)
+    check_core(X, 5, host(core), report=rep)
+    assert rep["max_rel_core"] <= REL_D
 
 
 @pytest.mark.parametrize("d", [1, 3, 17, 60, 64, 65, 102, 128, 129, 200, 256])
