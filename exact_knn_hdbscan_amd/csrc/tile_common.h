@@ -409,13 +409,10 @@ template <int K, int CB, int RB> struct EpiKnn {
     static constexpr int J = (K + 3) / 4 - 1;
     static constexpr bool kSecond = 4 * (J + 1) == K + 1 && J >= 1;
     TopK<K> lst[CB]; // this lane's lists, in registers
-    float thr[CB]; // this lane's last entry
-    float qj[CB];  // this lane's J-th entry
-    float qj1[CB]; // this lane's (J - 1)-th entry (used when kSecond)
     float nq[CB];
-    float adm[CB];  // admission bound on D2 shared by the column's four lanes
-    float admq[CB]; // the same bound moved to nb - 2 s, widened by the rounding margin
-    bool dirty;     // wave-uniform: a lane of the wave ran the slow path since adm was last formed
+    float admq[CB]; // admission bound on D2 shared by the column's four lanes, moved to nb - 2 s and widened
+                    // by the rounding margin
+    bool dirty[CB]; // wave-uniform: a lane of the wave inserted into list cb since its bound was last formed
     int32_t qrow[CB];
     int g;
 
@@ -423,13 +420,9 @@ template <int K, int CB, int RB> struct EpiKnn {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             lst[cb].clear();
-            thr[cb] = INFINITY;
-            qj[cb] = INFINITY;
-            qj1[cb] = INFINITY;
-            adm[cb] = INFINITY;
             admq[cb] = INFINITY;
+            dirty[cb] = false;
         }
-        dirty = false;
     }
     __device__ __forceinline__ void load(int cb, TopK<K> &L) { L = lst[cb]; }
     __device__ __forceinline__ void store(int cb, const TopK<K> &L) { lst[cb] = L; }
@@ -446,21 +439,24 @@ template <int K, int CB, int RB> struct EpiKnn {
     // decides which rows a lane inserts (with their exact D2): the margin can
     // admit a few more rows, which does not change the result (see slow()).
     //
-    // prepare() re-forms the bound (only when a list of the wave changed: a
-    // wave-uniform test), fast() is the branch-free test, slow() inserts the
-    // candidates of the columns that passed; tile() runs the three.
+    // prepare() re-forms the bound of each list block a lane of the wave
+    // inserted into (a wave-uniform test per block), fast() is the branch-free
+    // test, slow() inserts the candidates of the columns that passed; tile()
+    // runs the three.  The bound comes from the lists' last, J-th and
+    // (J - 1)-th entries.
     __device__ __forceinline__ void prepare() {
         constexpr float kWiden = 1.0f / 1048576.0f;
-        if (dirty) {
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-                const float gq = kSecond ? __uint_as_float(group_second_u32(__float_as_uint(qj[cb]),
-                                                                             __float_as_uint(qj1[cb])))
-                                         : group_max_nonneg(qj[cb]);
-                adm[cb] = fminf(group_min_nonneg(thr[cb]), gq);
-                admq[cb] = fmaf(adm[cb], 1.0f + kWiden, -nq[cb] * (1.0f - kWiden));
+        for (int cb = 0; cb < CB; ++cb) {
+            if (dirty[cb]) {
+                const TopK<K> &L = lst[cb];
+                const float gq = kSecond ? __uint_as_float(group_second_u32(__float_as_uint(L.d[J]),
+                                                                             __float_as_uint(L.d[J - 1])))
+                                         : group_max_nonneg(L.d[J]);
+                const float adm = fminf(group_min_nonneg(L.d[K - 1]), gq);
+                admq[cb] = fmaf(adm, 1.0f + kWiden, -nq[cb] * (1.0f - kWiden));
+                dirty[cb] = false;
             }
-            dirty = false;
         }
     }
     __device__ __forceinline__ void fast(const f4 (&acc)[RB][CB], const f4 (&nb4)[RB], bool (&hit)[CB]) const {
@@ -498,7 +494,6 @@ template <int K, int CB, int RB> struct EpiKnn {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) any = any || hit[cb];
         if (!__builtin_amdgcn_ballot_w64(any)) return;
-        dirty = true; // wave-uniform: the bound is re-formed before the next tile
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -509,12 +504,13 @@ template <int K, int CB, int RB> struct EpiKnn {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             if (!__builtin_amdgcn_ballot_w64(hit[cb])) continue;
+            dirty[cb] = true; // wave-uniform: this block's bound is re-formed before the next tile
             uint32_t mk = 0u;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    mk |= hit[cb] && fmaf(-2.f, acc[rb][cb][r], nb4[rb][r]) <= admq[cb] ? (1u << (4 * rb + r)) : 0u;
+                    mk |= fmaf(-2.f, acc[rb][cb][r], nb4[rb][r]) <= admq[cb] ? (1u << (4 * rb + r)) : 0u;
             TopK<K> L;
             load(cb, L);
             for (int trip = 0; trip < RB * 4; ++trip) {
@@ -529,11 +525,6 @@ template <int K, int CB, int RB> struct EpiKnn {
                 }
             }
             store(cb, L);
-            if (hit[cb]) {
-                thr[cb] = L.d[K - 1];
-                qj[cb] = L.d[J];
-                if (kSecond) qj1[cb] = L.d[J - 1];
-            }
         }
         __builtin_amdgcn_wave_barrier(); // the loads above before the next tile's stores
     }
