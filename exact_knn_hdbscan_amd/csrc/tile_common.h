@@ -18,6 +18,8 @@
 #include <float.h>
 #include <math.h>
 
+#include <type_traits>
+
 namespace ekh {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -59,8 +61,12 @@ template <int QM> struct Tile {
 // three waves per SIMD (d <= 64), so that while one wave waits at its barrier
 // or works through its epilogue, the others keep the MFMA pipe busy.  Per-row
 // norms (and, with PAYLOAD, component labels and core distances) live in a
-// three-slot ring; tile t's are in slot (t - t_begin) mod 3.  FULL: the
-// dimension fills all QM k-steps, so the k-loop has no runtime guard.
+// second LDS pair of slots, tile t's in slot (t - t_begin) mod 2 like its
+// features: a slot is refilled only after the barrier that follows its tile's
+// epilogue.  The two slots' MFMA blocks and stores are separate code, so their
+// LDS addresses are immediate offsets rather than per-tile vector additions.
+// FULL: the dimension fills all QM k-steps, so the k-loop has no runtime
+// guard.
 //
 // The database is read from its point-major copy Bp: row j holds features
 // 0 .. dp - 1 of point j with dp = 16 * chunks (features >= d are zero), so a
@@ -79,9 +85,9 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ Bp, int dp, 
     const uint32_t t_end = __builtin_amdgcn_readfirstlane((uint32_t)t_end_);
     const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)m_);
     __shared__ __align__(16) float sm_tile[2][T::TR * T::RS];
-    __shared__ __align__(16) float sm_nrm[3][T::TR];
-    __shared__ int32_t sm_comp[3][PAYLOAD ? T::TR : 1];
-    __shared__ float sm_core[3][PAYLOAD ? T::TR : 1];
+    __shared__ __align__(16) float sm_nrm[2][T::TR];
+    __shared__ int32_t sm_comp[2][PAYLOAD ? T::TR : 1];
+    __shared__ float sm_core[2][PAYLOAD ? T::TR : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, g = lane >> 4, li = lane & 15;
@@ -124,6 +130,8 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ Bp, int dp, 
         return __builtin_amdgcn_make_buffer_rsrc((void *)(const char *)base, (short)0, (int)bytes, 0x00020000);
     };
     const uint32_t row_bytes = __builtin_amdgcn_readfirstlane((uint32_t)dp * 4u);
+    const bool short_db = m < (uint32_t)T::TR;                              // the database is shorter than a tile
+    const uint32_t last0 = __builtin_amdgcn_readfirstlane(short_db ? 0u : m - T::TR); // first row of a partial last tile
     // One load sequence for every tile, with no address arithmetic (a branch
     // around the loads would cost the wait counts that let the next tile's
     // loads overlap this tile's MFMAs).  A partial last tile is read as rows
@@ -133,11 +141,11 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ Bp, int dp, 
         const uint32_t tt = t < t_end ? t : t_end - 1;
         const uint32_t rt = tt * (uint32_t)T::TR; // the tile's first row (< 2^32: m < 2^31)
         const bool part = rt + (uint32_t)T::TR > m;
-        const uint32_t row0 = __builtin_amdgcn_readfirstlane(part && m >= (uint32_t)T::TR ? m - T::TR : rt);
+        const uint32_t row0 = part ? last0 : rt;
         P.row0 = row0;
         // rows lrow in [lo, hi) belong to this tile (scalar bounds)
-        const uint32_t lo = part && m >= (uint32_t)T::TR ? rt - row0 : 0u;
-        const uint32_t hi = part && m < (uint32_t)T::TR ? m : (uint32_t)T::TR;
+        const uint32_t lo = part && !short_db ? rt - row0 : 0u;
+        const uint32_t hi = part && short_db ? m : (uint32_t)T::TR;
         P.nv = (uint32_t)lrow >= lo && (uint32_t)lrow < hi;
         const uint32_t rows = m - row0 < (uint32_t)T::TR ? m - row0 : (uint32_t)T::TR;
         const auto r = rsrc(sbase(Bp + (uint64_t)row0 * (uint32_t)dp), rows * row_bytes);
@@ -156,19 +164,21 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ Bp, int dp, 
                 __builtin_amdgcn_raw_buffer_load_b32(rsrc(sbase(core_b + row0), 0x7fffffff), lr * 4u, 0, 0));
         }
     };
-    auto store = [&](const Pref &P, int buf, int slot) {
+    auto store = [&](const Pref &P, auto BUF) {
+        constexpr int buf = decltype(BUF)::value;
 #pragma unroll
         for (int h = 0; h < T::NL; ++h)
             if (has[h]) *reinterpret_cast<f4 *>(sm_tile[buf] + lds_off[h]) = P.v[h];
         if (tid < T::TR) {
-            sm_nrm[slot][tid] = P.nv ? P.n : INFINITY; // padding rows never qualify
+            sm_nrm[buf][tid] = P.nv ? P.n : INFINITY; // padding rows never qualify
             if (PAYLOAD) {
-                sm_comp[slot][tid] = P.nv ? P.comp : -1;
-                sm_core[slot][tid] = P.nv ? P.core : INFINITY;
+                sm_comp[buf][tid] = P.nv ? P.comp : -1;
+                sm_core[buf][tid] = P.nv ? P.core : INFINITY;
             }
         }
     };
-    auto mma = [&](int buf, f4 (&acc)[T::RB][CB]) {
+    auto mma = [&](auto BUF, f4 (&acc)[T::RB][CB]) {
+        constexpr int buf = decltype(BUF)::value;
 #pragma unroll
         for (int rb = 0; rb < T::RB; ++rb)
 #pragma unroll
@@ -218,22 +228,29 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ Bp, int dp, 
     };
 
     if (t_begin >= t_end) return;
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
     Pref P;
     load(P, t_begin);
-    store(P, 0, 0);
+    store(P, B0{});
     __syncthreads();
     f4 acc[T::RB][CB];
-    int buf = 0, sl = 0;    // tile t's LDS buffer and norm slot
-    uint32_t rcur = P.row0; // and its first row
+    uint32_t rcur = P.row0; // tile t's first row
     for (uint32_t t = t_begin; t < t_end; ++t) {
-        const int sn = sl == 2 ? 0 : sl + 1;
+        const bool odd = ((t - t_begin) & 1u) != 0u; // wave-uniform: tile t's buffer and norm slot
         if (t + 1 < t_end) load(P, t + 1);
-        mma(buf, acc);
-        finish(acc, rcur, sl);
-        if (t + 1 < t_end) store(P, buf ^ 1, sn);
+        if (odd)
+            mma(B1{}, acc);
+        else
+            mma(B0{}, acc);
+        finish(acc, rcur, odd ? 1 : 0);
+        if (t + 1 < t_end) {
+            if (odd)
+                store(P, B0{});
+            else
+                store(P, B1{});
+        }
         __syncthreads();
-        buf ^= 1;
-        sl = sn;
         rcur = P.row0;
     }
 }
