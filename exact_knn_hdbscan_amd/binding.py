@@ -143,6 +143,14 @@ def _stream(dev):
     return torch.cuda.current_stream(dev).cuda_stream
 
 
+def _out(t, shape, dtype, dev, name):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or t.device != dev:
+        raise ValueError("%s must be a contiguous %s tensor %s on %s" % (name, dtype, tuple(shape), dev))
+    return t
+
+
 def _workspace(nbytes: int, dev):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dev)
 
@@ -168,12 +176,15 @@ def mst_workspace_bytes(n: int, d: int, min_samples: int, with_neighbours: bool 
     return int(library().ekh_mst_workspace_bytes(n, d, min_samples, 1 if with_neighbours else 0))
 
 
-def knn(X: torch.Tensor, Y: torch.Tensor, k: int, max_chunk_dots: int = 0, workspace: torch.Tensor = None):
+def knn(X: torch.Tensor, Y: torch.Tensor, k: int, max_chunk_dots: int = 0, workspace: torch.Tensor = None,
+        out_idx: torch.Tensor = None, out_dist: torch.Tensor = None):
     """k nearest points of Y for every point of X.
 
     Returns ``(idx int32 [n, k], dist float32 [n, k])``; rows ascending under
     (squared distance, index).  Passing the same tensor as X and Y makes the set
-    its own database (self pairs at distance 0).
+    its own database (self pairs at distance 0).  A caller-owned ``workspace``
+    (uint8, at least knn_workspace_bytes()) and outputs may be passed in; the
+    library checks the workspace size itself.
     """
     lib = library()
     px, ldx, n, d = _points(X, "X")
@@ -182,10 +193,10 @@ def knn(X: torch.Tensor, Y: torch.Tensor, k: int, max_chunk_dots: int = 0, works
         raise ValueError("X and Y differ in dimension")
     if X.device != Y.device:
         raise ValueError("X and Y on different devices")
-    idx = torch.empty((n, k), dtype=torch.int32, device=X.device)
-    dist = torch.empty((n, k), dtype=torch.float32, device=X.device)
-    need = lib.ekh_knn_workspace_bytes(n, m, d, k, max_chunk_dots)
-    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, X.device)
+    idx = _out(out_idx, (n, k), torch.int32, X.device, "out_idx")
+    dist = _out(out_dist, (n, k), torch.float32, X.device, "out_dist")
+    ws = workspace if workspace is not None else _workspace(lib.ekh_knn_workspace_bytes(n, m, d, k, max_chunk_dots),
+                                                            X.device)
     _check(lib.ekh_knn(px, ldx, n, py, ldy, m, d, k, idx.data_ptr(), dist.data_ptr(), max_chunk_dots,
                        ws.data_ptr(), ws.numel(), _stream(X.device)))
     return idx, dist

@@ -36,6 +36,28 @@ def test_knn_odd_sizes_and_leading_dimension():
     check_knn(X, Y, 10, host(i), host(dd), rescored=True)
 
 
+def test_knn_caller_outputs_and_workspace():
+    """Outputs and workspace passed in: the same lists bit for bit; a workspace
+    below the size the library needs is refused."""
+    import torch
+    X = datagen.gaussian_mixture(3001, 61, 6, seed=21)
+    Y = datagen.gaussian_mixture(1499, 61, 6, seed=22)
+    Xg, Yg = dev(X), dev(Y)
+    say("knn with caller outputs and workspace")
+    i0, d0 = ekh.knn(Xg, Yg, 9)
+    need = ekh.knn_workspace_bytes(3001, 1499, 61, 9)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    oi = torch.full((3001, 9), -7, dtype=torch.int32, device="cuda:0")
+    od = torch.full((3001, 9), -7.0, dtype=torch.float32, device="cuda:0")
+    i1, d1 = ekh.knn(Xg, Yg, 9, workspace=ws, out_idx=oi, out_dist=od)
+    assert i1.data_ptr() == oi.data_ptr() and d1.data_ptr() == od.data_ptr()
+    assert np.array_equal(host(i0), host(i1)) and np.array_equal(host(d0).view(np.uint32), host(d1).view(np.uint32))
+    with pytest.raises(ekh.EkhError):
+        ekh.knn(Xg, Yg, 9, workspace=ws[: need - 1])
+    with pytest.raises(ValueError):
+        ekh.knn(Xg, Yg, 9, out_idx=oi[:, :8])
+
+
 def test_knn_and_core_leading_dimension_past_2_25():
     """A leading dimension of 2^25 + 17 floats (the tiles read the point-major
     copy, so no tile address depends on it): ekh_knn and ekh_core_distances."""
