@@ -161,12 +161,12 @@ constexpr int64_t kWarmupWork = 12000;    // warm-up of fresh lists, in 32-row t
 constexpr int kChunkStreams = 2;          // chunks of one kNN call in flight at once (measured: 2 best)
 
 // kNN workgroups resident per CU: one per wave per SIMD that the registers
-// allow (four-wave workgroups), fewer if the double-buffered LDS tile and the
-// three-slot norm ring do not fit that many times (the lists live in registers)
+// allow (four-wave workgroups), fewer if the double-buffered LDS tile and its
+// norms do not fit that many times (the lists live in registers)
 int64_t knn_groups_per_cu(int K, int QM) {
     const int64_t tr = tile_rows(QM), rs = 4 * QM + 4;
-    // tile double buffer, norm ring, and the slow path's dot products (column blocks x rows per lane)
-    const int64_t lds = 2 * tr * rs * 4 + 3 * tr * 4 + knn_col_blocks(K, QM) * 4 * (tr / 16) * kThreads * 4;
+    // tile double buffer, its norms, and the slow path's dot products (column blocks x rows per lane)
+    const int64_t lds = 2 * tr * rs * 4 + 2 * tr * 4 + knn_col_blocks(K, QM) * 4 * (tr / 16) * kThreads * 4;
     const int64_t by_lds = kLdsPerCu / lds;
     const int64_t want = knn_waves_per_simd(K, QM);
     return by_lds < want ? (by_lds < 1 ? 1 : by_lds) : want;
@@ -217,11 +217,11 @@ int64_t chunk_part_entries(const KnnPlan &p, int64_t rows) {
     return c.splits > 1 ? (rows - c.body_q * p.QT) * c.splits * p.K : 0;
 }
 
-// Boruvka scan workgroups resident per CU (the LDS tile, and a three-slot ring
-// of norms, component labels and core distances)
+// Boruvka scan workgroups resident per CU (the double-buffered LDS tile with
+// its rows' norms, component labels and core distances)
 int64_t scan_groups_per_cu(int QM) {
     const int64_t tr = tile_rows(QM), rs = 4 * QM + 4;
-    const int64_t lds = 2 * tr * rs * 4 + 3 * 3 * tr * 4;
+    const int64_t lds = 2 * tr * rs * 4 + 2 * 3 * tr * 4;
     const int64_t by_lds = kLdsPerCu / lds;
     const int64_t want = scan_waves_per_simd(QM);
     return by_lds < want ? (by_lds < 1 ? 1 : by_lds) : want;
