@@ -372,7 +372,6 @@ int run_knn(const KnnPlan &p, const float *X, int64_t ldx, int64_t n, const floa
         a.m = m;
         a.nrm_b = ny;
         a.d = d;
-        a.chunks = p.chunks;
         a.self = self ? 1 : 0;
         const ChunkPlan cp = plan_chunk(p, a.nq);
         a.body_q = cp.body_q;
@@ -729,7 +728,6 @@ int ekh_mst_boruvka(const float *X, int64_t ldx, int64_t n, int32_t d, const flo
     sa.compW = w.compW;
     sa.best = w.best;
     sa.d = d;
-    sa.chunks = feature_chunks(d);
 
     // One host read-back per round, after the merge: the scans size their work
     // from the device-side active counts, and the largest component of the next

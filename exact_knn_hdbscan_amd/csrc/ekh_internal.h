@@ -19,15 +19,16 @@ namespace ekh {
 constexpr int kWaves = 4;             // waves per workgroup (two workgroups per CU)
 constexpr int kThreads = kWaves * 64; // 256 threads
 
-// QM = k-steps held in registers (4 features each): d <= 4 * QM.
+// QM = k-steps of the contraction (4 features each), 4 * feature_chunks(d):
+// the tile kernels are instantiated for every 16-feature chunk count (QM = 4,
+// 8, ..., 64), so the k-loop is always fully unrolled with no runtime guard.
 // CB = 16-column query blocks per wave; TR = database rows per LDS tile.
-template <int QM> struct TileGeo;
-template <> struct TileGeo<16> { static constexpr int TR = 32; };
-template <> struct TileGeo<32> { static constexpr int TR = 32; };
-template <> struct TileGeo<56> { static constexpr int TR = 32; };
-// d > 224: 16-row tiles keep the prefetch registers and the LDS tile small
-// enough for two workgroups per CU without spills
-template <> struct TileGeo<64> { static constexpr int TR = 16; };
+constexpr int kMaxQM = 64;
+template <int QM> struct TileGeo {
+    // d > 224: 16-row tiles keep the prefetch registers and the LDS tile small
+    // enough for two workgroups per CU without spills
+    static constexpr int TR = QM > 56 ? 16 : 32;
+};
 
 // instantiated list lengths; a request for k uses the smallest K >= k
 constexpr int kNumK = 6;
@@ -37,12 +38,14 @@ inline int pick_k(int k) {
         if (k <= kKList[i]) return kKList[i];
     return -1;
 }
-// (with 32-row tiles the loader needs 4 * QM to be a multiple of 32)
-inline int pick_qm(int d) { return d <= 64 ? 16 : (d <= 128 ? 32 : (d <= 224 ? 56 : 64)); }
-inline int tile_rows(int qm) { return qm == 64 ? 16 : 32; }
+// 16-feature chunks actually run for dimension d (identical in every kernel,
+// which keeps D2 bitwise the same everywhere)
+inline int feature_chunks(int d) { return (d + 15) / 16; }
+inline int pick_qm(int d) { return 4 * feature_chunks(d); }
+inline int tile_rows(int qm) { return qm > 56 ? 16 : 32; }
 // kNN tile kernel occupancy: three waves per SIMD where the registers fit
 // without spills (d <= 64 and K <= 16; d <= 128 and K <= 11), two otherwise
-constexpr int knn_waves_per_simd(int K, int QM) { return (QM == 16 && K <= 16) || (QM == 32 && K <= 11) ? 3 : 2; }
+constexpr int knn_waves_per_simd(int K, int QM) { return (QM <= 16 && K <= 16) || (QM <= 32 && K <= 11) ? 3 : 2; }
 // Boruvka scan kernel occupancy: three waves per SIMD for d <= 128, two otherwise
 constexpr int scan_waves_per_simd(int QM) { return QM <= 32 ? 3 : 2; }
 // 16-column query blocks per wave: two when the registers allow it
@@ -50,12 +53,13 @@ constexpr int knn_col_blocks(int K, int QM) { return (K > 11 || QM > 16) ? 1 : 2
 constexpr int scan_col_blocks(int QM) { return QM > 16 ? 1 : 2; }
 inline int knn_query_tile(int K, int QM) { return kWaves * 16 * knn_col_blocks(K, QM); }
 inline int scan_query_tile(int QM) { return kWaves * 16 * scan_col_blocks(QM); }
-// 16-feature chunks actually run for dimension d (identical in every kernel,
-// which keeps D2 bitwise the same everywhere)
-inline int feature_chunks(int d) { return (d + 15) / 16; }
 // row stride (floats) of the point-major copies the tiles read: every feature a
 // tile loads, zero past d
 inline int tile_dim(int d) { return 16 * feature_chunks(d); }
+
+// X(QM) for every instantiated QM (the multiples of 4 up to kMaxQM), e.g. the
+// cases of a switch on a runtime QM.
+#define EKH_FOR_EACH_QM(X) X(4) X(8) X(12) X(16) X(20) X(24) X(28) X(32) X(36) X(40) X(44) X(48) X(52) X(56) X(60) X(64)
 
 // Correctly rounded float32 square root.  (__fsqrt_rn lowers to the native,
 // approximate instruction in this toolchain; __builtin_sqrtf gets the correctly
@@ -86,7 +90,6 @@ struct KnnArgs {
     int64_t m;        // database points
     const float *nrm_b; // |b|^2 [m]
     int d;
-    int chunks;       // feature_chunks(d)
     int self;         // Q == B: the pair (i, i) is forced to D2 = 0
     int64_t body_q;   // leading query tiles run whole (one workgroup, final lists)
     int splits;       // database splits of every later query tile
@@ -150,7 +153,6 @@ struct ScanArgs {
     const uint32_t *nact; // their number, read on the device (set by the activity pass)
     uint64_t *best;       // per-point best key (W bits << 32 | partner), atomicMin
     int d;
-    int chunks;
     int64_t tiles;        // database tiles
 };
 // Database tiles per split of the scan, at least (the split count is chosen on

@@ -1,6 +1,7 @@
-// Instantiation of the kNN tile and merge kernels for one list length K.
-// Compiled once per K with -DEKH_KNN_K=<K> (2, 4, 8, 11, 16, 32), so the
-// instantiations build in parallel.
+// Instantiation of the kNN tile and merge kernels for one list length K (the
+// tile kernel once per 16-feature chunk count).  Compiled once per K with
+// -DEKH_KNN_K=<K> (2, 4, 8, 11, 16, 32), so the instantiations build in
+// parallel.
 #include "tile_common.h"
 
 #ifndef EKH_KNN_K
@@ -10,26 +11,25 @@
 namespace ekh {
 
 namespace {
-template <int K, int QM, bool FULL> hipError_t knn_tile_launch(const KnnArgs &a, hipStream_t s) {
+template <int K, int QM> hipError_t knn_tile_launch(const KnnArgs &a, hipStream_t s) {
     constexpr int CB = knn_col_blocks(K, QM);
     constexpr int QT = kWaves * 16 * CB;
     const int64_t tail_q = (a.nq - a.body_q * QT + QT - 1) / QT;
     const int64_t groups = a.body_q + tail_q * a.splits;
-    if (a.body_q < 0 || tail_q < 0 || a.splits < 1 || groups > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((knn_tile_kernel<K, QM, FULL>), dim3((unsigned)groups), dim3(kThreads), 0, s, a);
+    if (a.body_q < 0 || tail_q < 0 || a.splits < 1 || groups > 0x7fffffff || a.dp != 4 * QM || a.d > 4 * QM ||
+        a.d <= 4 * QM - 16)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((knn_tile_kernel<K, QM>), dim3((unsigned)groups), dim3(kThreads), 0, s, a);
     return hipGetLastError();
-}
-template <int K, int QM> hipError_t knn_tile_full(const KnnArgs &a, hipStream_t s) {
-    return a.chunks == QM / 4 ? knn_tile_launch<K, QM, true>(a, s) : knn_tile_launch<K, QM, false>(a, s);
 }
 } // namespace
 
 template <> hipError_t launch_knn_tile_k<EKH_KNN_K>(int QM, const KnnArgs &a, hipStream_t s) {
     switch (QM) {
-    case 16: return knn_tile_full<EKH_KNN_K, 16>(a, s);
-    case 32: return knn_tile_full<EKH_KNN_K, 32>(a, s);
-    case 56: return knn_tile_full<EKH_KNN_K, 56>(a, s);
-    case 64: return knn_tile_full<EKH_KNN_K, 64>(a, s);
+#define EKH_KNN_TILE_CASE(q)                                                                                           \
+    case q: return knn_tile_launch<EKH_KNN_K, q>(a, s);
+        EKH_FOR_EACH_QM(EKH_KNN_TILE_CASE)
+#undef EKH_KNN_TILE_CASE
     default: return hipErrorInvalidValue;
     }
 }

@@ -38,8 +38,8 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
 }
 
 // ---------------------------------------------------------------- tile loop
-// Feature order of the contraction: with qs = 4 * ceil(d / 16) k-steps, lane
-// group g supplies feature g * qs + s at k-step s (features >= d are zero).
+// Feature order of the contraction: with QM = 4 * ceil(d / 16) k-steps, lane
+// group g supplies feature g * QM + s at k-step s (features >= d are zero).
 // Any fixed assignment of features to (s, g) gives the same dot product up to
 // rounding; using this one in every kernel keeps D2 bitwise identical (and
 // symmetric), and it lets a lane read four consecutive k-steps of its A
@@ -47,10 +47,10 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
 template <int QM> struct Tile {
     static constexpr int TR = TileGeo<QM>::TR;  // database rows per tile
     static constexpr int RB = TR / 16;          // 16-row blocks per tile
-    static constexpr int FD = QM * 4;           // features held (d <= FD)
+    static constexpr int FD = QM * 4;           // features per row (d <= FD, zero past d)
     static constexpr int RS = FD + 4;           // LDS row stride in floats: 16-byte reads of 8 rows hit distinct banks
-    static constexpr int NL = TR * QM / kThreads; // 16-byte pieces each thread loads per tile (at d = FD)
-    static_assert((TR * QM) % kThreads == 0, "tile shape");
+    static constexpr int NP = TR * QM;          // 16-byte pieces per tile
+    static constexpr int NL = (NP + kThreads - 1) / kThreads; // pieces each thread loads per tile
 };
 
 // Streams database tiles [t_begin, t_end) through a double-buffered LDS tile
@@ -65,21 +65,20 @@ template <int QM> struct Tile {
 // features: a slot is refilled only after the barrier that follows its tile's
 // epilogue.  The two slots' MFMA blocks and stores are separate code, so their
 // LDS addresses are immediate offsets rather than per-tile vector additions.
-// FULL: the dimension fills all QM k-steps, so the k-loop has no runtime
-// guard.
+// The kernels are instantiated per 16-feature chunk count, so the k-loop runs
+// all QM k-steps, fully unrolled, with the next k-steps' A operands read ahead.
 //
 // The database is read from its point-major copy Bp: row j holds features
-// 0 .. dp - 1 of point j with dp = 16 * chunks (features >= d are zero), so a
+// 0 .. dp - 1 of point j with dp = 4 * QM (features >= d are zero), so a
 // tile is one contiguous block of TR * dp floats.  Thread tid loads its 16-byte
 // pieces tid, tid + 256, ... of the block (coalesced) with buffer loads whose
 // base is the tile's first row (a scalar) and whose lane offsets never change;
 // each piece goes to LDS with one 16-byte store.  Point counts are below 2^31,
 // so tile and row counters are 32-bit scalars.
-template <int QM, int CB, bool PAYLOAD, bool FULL, class Epi>
-__device__ __forceinline__ void run_tiles(const float *__restrict__ Bp, int dp, int32_t m_,
-                                          const float *__restrict__ nrm_b, const int32_t *__restrict__ comp_b,
-                                          const float *__restrict__ core_b, int chunks, int32_t t_begin_,
-                                          int32_t t_end_, const float (&bq)[CB][QM], Epi &epi) {
+template <int QM, int CB, bool PAYLOAD, class Epi>
+__device__ __forceinline__ void run_tiles(const float *__restrict__ Bp, int32_t m_, const float *__restrict__ nrm_b,
+                                          const int32_t *__restrict__ comp_b, const float *__restrict__ core_b,
+                                          int32_t t_begin_, int32_t t_end_, const float (&bq)[CB][QM], Epi &epi) {
     using T = Tile<QM>;
     const uint32_t t_begin = __builtin_amdgcn_readfirstlane((uint32_t)t_begin_);
     const uint32_t t_end = __builtin_amdgcn_readfirstlane((uint32_t)t_end_);
@@ -91,19 +90,17 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ Bp, int dp, 
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, g = lane >> 4, li = lane & 15;
-    const int qs = FULL ? QM : 4 * chunks; // k-steps run
-    const int ppr = FULL ? QM : qs;        // 16-byte pieces per row (dp / 4)
-    const int pieces = T::TR * ppr;        // per tile
+    constexpr int qs = QM; // k-steps run
 
     // this thread's pieces: LDS position (row * RS + 4 * column) and whether
-    // the piece exists at this dimension
+    // the piece exists (a tile may have fewer pieces than 256 * NL)
     int lds_off[T::NL];
     bool has[T::NL];
 #pragma unroll
     for (int h = 0; h < T::NL; ++h) {
         const int c = tid + kThreads * h;
-        has[h] = FULL || c < pieces;
-        const int row = c / ppr, col = c - row * ppr;
+        has[h] = T::NP % kThreads == 0 || c < T::NP;
+        const int row = c / QM, col = c - row * QM;
         lds_off[h] = row * T::RS + 4 * col;
     }
     const int lrow = tid % T::TR; // the thread also loads row lrow's norm (and payload)
@@ -129,7 +126,7 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ Bp, int dp, 
     auto rsrc = [](gchar base, uint32_t bytes) {
         return __builtin_amdgcn_make_buffer_rsrc((void *)(const char *)base, (short)0, (int)bytes, 0x00020000);
     };
-    const uint32_t row_bytes = __builtin_amdgcn_readfirstlane((uint32_t)dp * 4u);
+    constexpr uint32_t row_bytes = (uint32_t)T::FD * 4u;
     const bool short_db = m < (uint32_t)T::TR;                              // the database is shorter than a tile
     const uint32_t last0 = __builtin_amdgcn_readfirstlane(short_db ? 0u : m - T::TR); // first row of a partial last tile
     // One load sequence for every tile, with no address arithmetic (a branch
@@ -148,9 +145,9 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ Bp, int dp, 
         const uint32_t hi = part && short_db ? m : (uint32_t)T::TR;
         P.nv = (uint32_t)lrow >= lo && (uint32_t)lrow < hi;
         const uint32_t rows = m - row0 < (uint32_t)T::TR ? m - row0 : (uint32_t)T::TR;
-        const auto r = rsrc(sbase(Bp + (uint64_t)row0 * (uint32_t)dp), rows * row_bytes);
-        // pieces past the tile (a dimension below FD) lie past the resource's
-        // end: they read as zeros and are not stored
+        const auto r = rsrc(sbase(Bp + (uint64_t)row0 * (uint32_t)T::FD), rows * row_bytes);
+        // pieces past the tile (more threads than pieces, or rows past m) lie
+        // past the resource's end: they read as zeros and are not stored
 #pragma unroll
         for (int h = 0; h < T::NL; ++h) {
             const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (tid + kThreads * h) * 16, 0, 0);
@@ -185,41 +182,18 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ Bp, int dp, 
             for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f4{0.f, 0.f, 0.f, 0.f};
         // this lane's feature block of each row it reads
         const float *tl = sm_tile[buf] + li * T::RS + g * qs;
-        if (FULL) {
-            constexpr int PRE = QM < 4 ? QM : 4; // k-steps whose A operands are read ahead
+        constexpr int PRE = 4; // k-steps whose A operands are read at once (one 16-byte read per row block)
 #pragma unroll
-            for (int s0 = 0; s0 < QM; s0 += PRE) {
-                f4 a4[PRE / 4][T::RB];
+        for (int s0 = 0; s0 < QM; s0 += PRE) {
+            f4 a4[T::RB];
 #pragma unroll
-                for (int c = 0; c < PRE / 4; ++c)
+            for (int rb = 0; rb < T::RB; ++rb) a4[rb] = *reinterpret_cast<const f4 *>(tl + rb * 16 * T::RS + s0);
 #pragma unroll
-                    for (int rb = 0; rb < T::RB; ++rb)
-                        a4[c][rb] = *reinterpret_cast<const f4 *>(tl + rb * 16 * T::RS + s0 + 4 * c);
+            for (int s = 0; s < PRE; ++s)
 #pragma unroll
-                for (int s = 0; s < PRE; ++s)
+                for (int rb = 0; rb < T::RB; ++rb)
 #pragma unroll
-                    for (int rb = 0; rb < T::RB; ++rb)
-#pragma unroll
-                        for (int cb = 0; cb < CB; ++cb)
-                            acc[rb][cb] = mfma16(a4[s / 4][rb][s % 4], bq[cb][s0 + s], acc[rb][cb]);
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < QM / 4; ++c) {
-                if (c < chunks) {
-                    f4 a4[T::RB];
-#pragma unroll
-                    for (int rb = 0; rb < T::RB; ++rb)
-                        a4[rb] = *reinterpret_cast<const f4 *>(tl + rb * 16 * T::RS + 4 * c);
-#pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4)
-#pragma unroll
-                        for (int rb = 0; rb < T::RB; ++rb)
-#pragma unroll
-                            for (int cb = 0; cb < CB; ++cb)
-                                acc[rb][cb] = mfma16(a4[rb][s4], bq[cb][c * 4 + s4], acc[rb][cb]);
-                }
-            }
+                    for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = mfma16(a4[rb][s], bq[cb][s0 + s], acc[rb][cb]);
         }
     };
     auto finish = [&](const f4 (&acc)[T::RB][CB], uint32_t row0, int slot) {
@@ -256,15 +230,14 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ Bp, int dp, 
 }
 
 // Loads the register-resident query operand: lane (g, i) holds feature
-// g * qs + s of its query column at k-step s (qs = 4 * chunks).
+// g * QM + s of its query column at k-step s.
 template <int QM>
 __device__ __forceinline__ void load_query(const float *__restrict__ Q, int64_t ldq, int64_t col, bool valid, int d,
-                                           int chunks, int g, float (&bq)[QM]) {
-    const int qs = 4 * chunks;
+                                           int g, float (&bq)[QM]) {
 #pragma unroll
     for (int s = 0; s < QM; ++s) {
-        const int f = g * qs + s;
-        bq[s] = (valid && s < qs && f < d) ? Q[(int64_t)f * ldq + col] : 0.f;
+        const int f = g * QM + s;
+        bq[s] = (valid && f < d) ? Q[(int64_t)f * ldq + col] : 0.f;
     }
 }
 
@@ -586,7 +559,7 @@ __device__ __forceinline__ void write_list(const KnnArgs &a, const TopK<K> &L, i
     }
 }
 
-template <int K, int QM, bool FULL>
+template <int K, int QM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(knn_waves_per_simd(K, QM), knn_waves_per_simd(K, QM))))
 void knn_tile_kernel(KnnArgs a) {
     constexpr int CB = knn_col_blocks(K, QM);
@@ -613,7 +586,7 @@ void knn_tile_kernel(KnnArgs a) {
         const int64_t ql = qbase + wave * 16 * CB + cb * 16 + li;
         qv[cb] = ql < a.nq;
         const int64_t q = a.q0 + (qv[cb] ? ql : 0);
-        load_query<QM>(a.Q, a.ldq, q, qv[cb], a.d, a.chunks, g, bq[cb]);
+        load_query<QM>(a.Q, a.ldq, q, qv[cb], a.d, g, bq[cb]);
         nq[cb] = qv[cb] ? a.nrm_q[q] : 0.f;
         qrow[cb] = (int32_t)(a.q0 + ql);
     }
@@ -630,8 +603,7 @@ void knn_tile_kernel(KnnArgs a) {
     epi.g = g;
     epi.sv = sv;
     epi.tid = tid;
-    run_tiles<QM, CB, false, FULL>(a.Bt, a.dp, (int32_t)a.m, a.nrm_b, nullptr, nullptr, a.chunks, (int32_t)tb,
-                                   (int32_t)te, bq, epi);
+    run_tiles<QM, CB, false>(a.Bt, (int32_t)a.m, a.nrm_b, nullptr, nullptr, (int32_t)tb, (int32_t)te, bq, epi);
 
     // merge the four lane groups that share each query column
 #pragma unroll

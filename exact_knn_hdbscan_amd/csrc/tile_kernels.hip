@@ -226,7 +226,7 @@ template <int CB, int RB> struct EpiScan {
     }
 };
 
-template <int QM, bool FULL>
+template <int QM>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(scan_waves_per_simd(QM), scan_waves_per_simd(QM))))
 void scan_tile_kernel(ScanArgs a) {
@@ -265,7 +265,7 @@ void scan_tile_kernel(ScanArgs a) {
             valid[cb] = c < nact;
             const int32_t p = valid[cb] ? a.act[c] : 0;
             pt[cb] = p;
-            load_query<QM>(a.X, a.ldx, p, valid[cb], a.d, a.chunks, g, bq[cb]);
+            load_query<QM>(a.X, a.ldx, p, valid[cb], a.d, g, bq[cb]);
             epi.na[cb] = a.nrm[p];
             epi.corea[cb] = a.core[p];
             epi.ca[cb] = a.comp[p];
@@ -278,8 +278,7 @@ void scan_tile_kernel(ScanArgs a) {
             epi.thr[cb] = (!valid[cb] || epi.corea[cb] > w0) ? -INFINITY : scan_threshold(w0);
         }
         const int64_t tb = a.tiles * split / sp, te = a.tiles * (split + 1) / sp;
-        run_tiles<QM, CB, true, FULL>(a.Xb, a.dp, (int32_t)a.nb, a.nrm_b, a.comp_b, a.core_b, a.chunks, (int32_t)tb,
-                                      (int32_t)te, bq, epi);
+        run_tiles<QM, CB, true>(a.Xb, (int32_t)a.nb, a.nrm_b, a.comp_b, a.core_b, (int32_t)tb, (int32_t)te, bq, epi);
 
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
@@ -296,22 +295,19 @@ void scan_tile_kernel(ScanArgs a) {
     }
 }
 
-template <int QM, bool FULL> static hipError_t scan_launch(const ScanArgs &a, int64_t grid, hipStream_t s) {
-    hipLaunchKernelGGL((scan_tile_kernel<QM, FULL>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+template <int QM> static hipError_t scan_launch(const ScanArgs &a, int64_t grid, hipStream_t s) {
+    if (a.dp != 4 * QM || a.d > 4 * QM || a.d <= 4 * QM - 16) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((scan_tile_kernel<QM>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
-}
-
-template <int QM> static hipError_t scan_full(const ScanArgs &a, int64_t grid, hipStream_t s) {
-    return a.chunks == QM / 4 ? scan_launch<QM, true>(a, grid, s) : scan_launch<QM, false>(a, grid, s);
 }
 
 hipError_t launch_scan_tile(int QM, const ScanArgs &a, int64_t grid, hipStream_t s) {
     if (grid <= 0 || grid > 0x7fffffff || a.tiles <= 0) return hipErrorInvalidValue;
     switch (QM) {
-    case 16: return scan_full<16>(a, grid, s);
-    case 32: return scan_full<32>(a, grid, s);
-    case 56: return scan_full<56>(a, grid, s);
-    case 64: return scan_full<64>(a, grid, s);
+#define EKH_SCAN_CASE(q)                                                                                               \
+    case q: return scan_launch<q>(a, grid, s);
+        EKH_FOR_EACH_QM(EKH_SCAN_CASE)
+#undef EKH_SCAN_CASE
     default: return hipErrorInvalidValue;
     }
 }
