@@ -28,15 +28,6 @@ __device__ __forceinline__ f4 mfma16(float a, float b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// A wave-uniform 64-bit value, held in scalar registers (the compiler cannot
-// always prove uniformity through 64-bit arithmetic, and would otherwise keep
-// tile counters and row bases in vector registers).
-__device__ __forceinline__ int64_t uniform64(int64_t x) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
 // ---------------------------------------------------------------- tile loop
 // Feature order of the contraction: with QM = 4 * ceil(d / 16) k-steps, lane
 // group g supplies feature g * QM + s at k-step s (features >= d are zero).
