@@ -73,13 +73,26 @@ def test_knn_and_core_leading_dimension_past_2_25():
     assert rep["max_rel_core"] <= REL_D
 
 
-@pytest.mark.parametrize("d", [1, 3, 17, 60, 64, 65, 102, 128, 129, 200, 256])
+# every tile-kernel instantiation (QM = 4 ceil(d / 16) k-steps: 4, 8, ..., 64),
+# at both ends of its range where it matters
+@pytest.mark.parametrize("d", [1, 3, 16, 17, 33, 48, 60, 64, 65, 90, 102, 112, 128, 129, 150, 170, 185, 200, 220,
+                               225, 240, 256])
 def test_knn_dimensions(d):
     X = datagen.gaussian_mixture(333, d, 5, seed=d)
     Y = datagen.gaussian_mixture(517, d, 5, seed=d + 1000)
     say("knn d=%d" % d)
     i, dd = ekh.knn(dev(X), dev(Y), 10)
     check_knn(X, Y, 10, host(i), host(dd), rescored=True)
+
+
+@pytest.mark.parametrize("k,d", [(2, 33), (4, 90), (8, 150), (16, 102), (32, 200), (32, 250)])
+def test_knn_k_values_other_widths(k, d):
+    """List lengths other than K = 11 at other tile-kernel widths."""
+    X = datagen.gaussian_mixture(900, d, 6, seed=k + d)
+    say("knn self k=%d d=%d" % (k, d))
+    Xg = dev(X)
+    i, dd = ekh.knn(Xg, Xg, k)
+    check_knn(X, X, k, host(i), host(dd), rescored=True)
 
 
 @pytest.mark.parametrize("k", [1, 2, 3, 8, 10, 11, 12, 16, 17, 32])

@@ -120,10 +120,10 @@ def test_pruning_is_exact():
     check_mst(X, 10, *ref)
 
 
-@pytest.mark.parametrize("d", [100, 129, 200, 256])
+@pytest.mark.parametrize("d", [9, 33, 90, 100, 129, 170, 200, 240, 256])
 def test_mst_dimensions(d):
-    """The scan kernel at every feature width it is built for (d <= 128: 32
-    features per k-step group; 128 < d <= 224 and d > 224: the wider forms)."""
+    """The scan kernel across its instantiations (QM = 4 ceil(d / 16) k-steps;
+    32-row tiles up to d = 224, 16-row tiles beyond)."""
     X = datagen.gaussian_mixture(1500, d, 6, seed=d)
     say("mst d=%d" % d)
     lo, hi, w, st = gpu_mst(X, 5, stats=True)
