@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 METRIC = "kNN pair-distances/s + Borůvka MST time at 500k×61; % fp32 MFMA peak"
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X published dense fp32 matrix peak
 COPY_BYTES = 1 << 30  # size of the calibration copy of --pmc-probe
+SECTION_WARM_S = 0.5  # seconds of repeated section calls before they are timed
 HBM_PEAK_GBS = 8000.0
 TAIL_MIN_CLUSTER_SIZE = 20  # the HDBSCAN page's results use min_cluster_size = 20
 
@@ -250,11 +251,11 @@ def time_clips(ekh, datagen, oracle_too, reps=5):
     return out
 
 
-def time_sections(ekh, datagen, oracle_too=False, reps=5):
+def time_sections(ekh, datagen, oracle_too=False, reps=9):
     """ekh_knn on the two section workloads (50,000 x 5,000 at d = 102, k = 10; and
     200,000 x 20,000 at d = 200, k = 10, in chunks of max_chunk_dots = 64e6): median
-    time per call with inputs resident, the tile kernel's rate per launch, the
-    rate over the whole call, and the pair rate."""
+    time per call with inputs resident, after SECTION_WARM_S of the same call, the
+    tile kernel's rate per launch, the rate over the whole call, and the pair rate."""
     import numpy as np
     import torch
 
@@ -270,6 +271,13 @@ def time_sections(ekh, datagen, oracle_too=False, reps=5):
         od = torch.empty((X.shape[1], k), dtype=torch.float32, device=X.device)
         ekh.knn(X, Y, k, max_chunk_dots=dots, workspace=ws, out_idx=oi, out_dist=od)
         torch.cuda.synchronize()
+        # steady state first: the same call repeated for SECTION_WARM_S (after
+        # idle, or after other work, the first calls of a short kernel run at
+        # lower clocks)
+        t_end = time.perf_counter() + SECTION_WARM_S
+        while time.perf_counter() < t_end:
+            ekh.knn(X, Y, k, max_chunk_dots=dots, workspace=ws, out_idx=oi, out_dist=od)
+            torch.cuda.synchronize()
         # the calls are timed with the library's kernel timer off; the tile
         # launches' own durations come from a second set of calls with it on
         ts = []

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(PKG, "libekh.so")
 # (source, object name, extra flags); the kNN kernels are instantiated once per list length
-KNN_KS = [2, 4, 8, 11, 16, 32]
+KNN_KS = [2, 4, 8, 10, 11, 16, 32]
 SOURCES = [("tile_kernels.hip", "tile_kernels", []), ("boruvka_kernels.hip", "boruvka_kernels", []),
            ("api.hip", "api", []), ("bipartite.hip", "bipartite", []),
            ("kmeanspp.hip", "kmeanspp", ["-ffp-contract=off"])] + [("knn_inst.hip", "knn_k%d" % k, ["-DEKH_KNN_K=%d" % k]) for k in KNN_KS]

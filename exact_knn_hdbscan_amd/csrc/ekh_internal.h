@@ -31,8 +31,8 @@ template <int QM> struct TileGeo {
 };
 
 // instantiated list lengths; a request for k uses the smallest K >= k
-constexpr int kNumK = 6;
-constexpr int kKList[kNumK] = {2, 4, 8, 11, 16, 32};
+constexpr int kNumK = 7;
+constexpr int kKList[kNumK] = {2, 4, 8, 10, 11, 16, 32};
 inline int pick_k(int k) {
     for (int i = 0; i < kNumK; ++i)
         if (k <= kKList[i]) return kKList[i];

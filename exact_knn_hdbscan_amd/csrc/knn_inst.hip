@@ -1,6 +1,6 @@
 // Instantiation of the kNN tile and merge kernels for one list length K (the
 // tile kernel once per 16-feature chunk count).  Compiled once per K with
-// -DEKH_KNN_K=<K> (2, 4, 8, 11, 16, 32), so the instantiations build in
+// -DEKH_KNN_K=<K> (2, 4, 8, 10, 11, 16, 32), so the instantiations build in
 // parallel.
 #include "tile_common.h"
 

@@ -645,59 +645,102 @@ template <int K> __global__ __launch_bounds__(256) void knn_merge_kernel(KnnArgs
 
 // Direct-difference D2 of the selected neighbours, for the reported kNN
 // distances and the core distances: sum_f (q_f - y_f)^2 with fmaf in feature
-// order, which carries no cancellation error.  One lane per (row, list entry),
-// kRowLanes lanes per row (a power of two >= K), so a row's K gathers run in
-// parallel: the neighbour's features come from the point-major copy Bt, four
-// per 16-byte load, and the query's from LDS, where each wave first stages its
-// rows' features (feature-major source, coalesced).  Padding features are zero
-// on both sides and add exact zeros.  The row's order is then taken across its
-// lanes by ranks (shuffles), with no sort network.
+// order, which carries no cancellation error.  One lane per (row, list entry)
+// "slot", kRowLanes lanes per row (a power of two >= K): 64 slots per wave.
+// Each lane sums its own slot in feature order, 16 features (one chunk) at a
+// time, from LDS: the wave first stages the chunk of every slot's neighbour
+// (its 64 bytes of the point-major copy Bt, read by four adjacent lanes, so a
+// load instruction touches 16 cache lines instead of 64) and of its rows'
+// query features (feature-major source), with the next two chunks' loads
+// already in flight.  Padding features are zero on both sides and add exact
+// zeros.  The row's order is then taken across its lanes by ranks (shuffles),
+// with no sort network.
 template <int K> struct DirectRows {
     static constexpr int kRowLanes = K <= 16 ? 16 : 32;
     static constexpr int kRowsPerWave = 64 / kRowLanes;
     static constexpr int kRowsPerBlock = kRowsPerWave * 4; // 256 threads
 };
-constexpr int kDirectMaxDim = 256; // EKH_MAX_DIM rounded to 4
+constexpr int kDirectMaxDim = 256; // EKH_MAX_DIM rounded to 16
+// floats per staged 16-feature row: 4 floats of padding make the 16-byte reads
+// of 8 consecutive slots fall on distinct banks
+constexpr int kSlotStride = 20;
+// per wave: 64 slot rows, then up to 4 query rows
+constexpr int kDirectWaveFloats = (64 + 4) * kSlotStride;
+constexpr int kDirectBlockFloats = 4 * kDirectWaveFloats; // LDS of a direct-difference workgroup
 
-// D2 of this lane's entry (row q, entry t) and its key; returns false for lanes
-// past the rows.  sq: LDS [kRowsPerBlock][kDirectMaxDim].
+// D2 of this lane's slot (row q, entry t) and its key; returns false for lanes
+// past the rows.  lds: kDirectBlockFloats floats.
 template <int K>
-__device__ __forceinline__ bool direct_d2(const KnnArgs &a, float *sq, int64_t &q, int &t, int32_t &jo, float &d2) {
+__device__ __forceinline__ bool direct_d2(const KnnArgs &a, float *lds, int64_t &q, int &t, int32_t &jo, float &d2) {
     using R = DirectRows<K>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rw = lane / R::kRowLanes; // row within the wave
     t = lane % R::kRowLanes;
     const int64_t qb = ((int64_t)blockIdx.x * 4 + wave) * R::kRowsPerWave; // first local row of the wave
-    float *sw = sq + wave * R::kRowsPerWave * kDirectMaxDim;
-    // stage the wave's rows' features: lane l loads row (l % rows) feature (l / rows) + step
-    for (int f = lane / R::kRowsPerWave; f < a.dp; f += 64 / R::kRowsPerWave) {
-        const int r = lane % R::kRowsPerWave;
-        const int64_t qq = qb + r;
-        sw[r * kDirectMaxDim + f] = (qq < a.nq && f < a.d) ? a.Q[(int64_t)f * a.ldq + a.q0 + qq] : 0.f;
-    }
-    __builtin_amdgcn_wave_barrier(); // the LDS stores above before the loads below (one wave)
     const int64_t ql = qb + rw;
     q = a.q0 + ql;
-    if (ql >= a.nq) return false;
-    jo = t < a.k_out ? a.out_idx[q * a.k_out + t] : 0x7fffffff;
+    const bool live = ql < a.nq;
+    jo = (live && t < a.k_out) ? a.out_idx[q * a.k_out + t] : 0x7fffffff;
     // an entry outside [0, m) cannot come from a finished search (k <= m); it is
-    // never used as an address: row 0 is read and the entry ranks last
-    const bool ok = t < a.k_out && jo >= 0 && jo < a.m;
-    const int32_t jr = ok ? jo : 0;
-    const f4 *y = reinterpret_cast<const f4 *>(a.Bt + (int64_t)jr * a.dp);
-    const f4 *x = reinterpret_cast<const f4 *>(sw + rw * kDirectMaxDim);
-    float s = 0.f;
-#pragma unroll 4
-    for (int f = 0; f < a.dp / 4; ++f) {
-        const f4 yv = y[f], xv = x[f];
+    // never used as an address: the slot stages zeros and ranks last
+    const bool ok = live && t < a.k_out && jo >= 0 && jo < a.m;
+    const int32_t jr = ok ? jo : -1;
+
+    // loader roles: piece p of this lane is quarter (lane & 3) of slot p * 16 + lane / 4;
+    // query feature (lane / rows) of the chunk for row (lane % rows)
+    const int pq = lane & 3;
+    const float *ysrc[4];
+    bool yhas[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float v = xv[e] - yv[e];
-            s = fmaf(v, v, s);
+    for (int p = 0; p < 4; ++p) {
+        const int32_t js = __shfl(jr, p * 16 + (lane >> 2));
+        yhas[p] = js >= 0;
+        ysrc[p] = a.Bt + (int64_t)(yhas[p] ? js : 0) * a.dp + 4 * pq;
+    }
+    const int xr = lane % R::kRowsPerWave, xf = lane / R::kRowsPerWave;
+    const bool xrow = qb + xr < a.nq && xf < 16;
+    const float *xsrc = a.Q + a.q0 + (xrow ? qb + xr : 0) + (int64_t)xf * a.ldq;
+    float *yw = lds + wave * kDirectWaveFloats; // [64][kSlotStride]
+    float *xw = yw + 64 * kSlotStride;          // [rows][kSlotStride]
+
+    auto load = [&](int c, f4 (&yv)[4], float &xv) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) yv[p] = yhas[p] ? *reinterpret_cast<const f4 *>(ysrc[p] + c * 16) : f4{0.f, 0.f, 0.f, 0.f};
+        xv = (xrow && c * 16 + xf < a.d) ? xsrc[(int64_t)c * 16 * a.ldq] : 0.f;
+    };
+    const int nc = a.dp / 16;
+    f4 ya[4], yb[4];
+    float xa, xb = 0.f;
+    load(0, ya, xa);
+    if (nc > 1) load(1, yb, xb);
+    const f4 *ymine = reinterpret_cast<const f4 *>(yw + lane * kSlotStride);
+    const f4 *xmine = reinterpret_cast<const f4 *>(xw + rw * kSlotStride);
+    float s = 0.f;
+    for (int c = 0; c < nc; ++c) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) *reinterpret_cast<f4 *>(yw + (p * 16 + (lane >> 2)) * kSlotStride + 4 * pq) = ya[p];
+        if (xf < 16) xw[xr * kSlotStride + xf] = xa;
+        // the stores above before this wave's reads below (LDS runs one wave's
+        // operations in order; this keeps the compiler from moving them)
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int p = 0; p < 4; ++p) ya[p] = yb[p];
+        xa = xb;
+        if (c + 2 < nc) load(c + 2, yb, xb);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const f4 yv = ymine[j], xv = xmine[j];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float v = xv[e] - yv[e];
+                s = fmaf(v, v, s);
+            }
         }
+        // this chunk's reads before the next chunk's stores
+        __builtin_amdgcn_wave_barrier();
     }
     d2 = ok ? s : INFINITY;
-    return true;
+    return live;
 }
 
 // Rank of this lane's (d2, index) among its row's lanes (lanes past k_out hold
@@ -719,12 +762,12 @@ template <int K> __device__ __forceinline__ int direct_rank(float d2, int32_t jo
 // and reported as sqrt_rn of the direct D2.  The neighbour set itself is the
 // one the GEMM-form D2 selected.
 template <int K> __global__ __launch_bounds__(256) void knn_rescore_kernel(KnnArgs a) {
-    __shared__ __align__(16) float sq[DirectRows<K>::kRowsPerBlock * kDirectMaxDim];
+    __shared__ __align__(16) float lds[kDirectBlockFloats];
     int64_t q;
     int t;
     int32_t jo = 0x7fffffff;
     float d2 = INFINITY;
-    const bool live = direct_d2<K>(a, sq, q, t, jo, d2);
+    const bool live = direct_d2<K>(a, lds, q, t, jo, d2);
     const int rank = direct_rank<K>(d2, jo, t); // every lane takes part in the shuffles
     if (!live || t >= a.k_out) return;
     // every lane has read its own entry before any lane of the row writes (the
@@ -742,12 +785,12 @@ template <int K> __global__ __launch_bounds__(256) void knn_rescore_kernel(KnnAr
 // algorithm on the device": the distance to the min_samples-th neighbour, the
 // point itself counted).
 template <int K> __global__ __launch_bounds__(256) void knn_core_kernel(KnnArgs a) {
-    __shared__ __align__(16) float sq[DirectRows<K>::kRowsPerBlock * kDirectMaxDim];
+    __shared__ __align__(16) float lds[kDirectBlockFloats];
     int64_t q;
     int t;
     int32_t jo = 0x7fffffff;
     float d2 = INFINITY;
-    const bool live = direct_d2<K>(a, sq, q, t, jo, d2);
+    const bool live = direct_d2<K>(a, lds, q, t, jo, d2);
     const int rank = direct_rank<K>(d2, jo, t);
     if (live && t < a.k_out && rank == a.min_samples - 1) a.out_core[q] = sqrt_rn(d2);
 }

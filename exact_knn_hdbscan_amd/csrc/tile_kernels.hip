@@ -116,6 +116,7 @@ hipError_t launch_knn_tile(int K, int QM, const KnnArgs &a, hipStream_t s) {
     case 2: return launch_knn_tile_k<2>(QM, a, s);
     case 4: return launch_knn_tile_k<4>(QM, a, s);
     case 8: return launch_knn_tile_k<8>(QM, a, s);
+    case 10: return launch_knn_tile_k<10>(QM, a, s);
     case 11: return launch_knn_tile_k<11>(QM, a, s);
     case 16: return launch_knn_tile_k<16>(QM, a, s);
     case 32: return launch_knn_tile_k<32>(QM, a, s);
@@ -129,6 +130,7 @@ hipError_t launch_knn_rescore(int K, const KnnArgs &a, hipStream_t s) {
     case 2: return launch_knn_rescore_k<2>(a, s);
     case 4: return launch_knn_rescore_k<4>(a, s);
     case 8: return launch_knn_rescore_k<8>(a, s);
+    case 10: return launch_knn_rescore_k<10>(a, s);
     case 11: return launch_knn_rescore_k<11>(a, s);
     case 16: return launch_knn_rescore_k<16>(a, s);
     case 32: return launch_knn_rescore_k<32>(a, s);
@@ -142,6 +144,7 @@ hipError_t launch_knn_core(int K, const KnnArgs &a, hipStream_t s) {
     case 2: return launch_knn_core_k<2>(a, s);
     case 4: return launch_knn_core_k<4>(a, s);
     case 8: return launch_knn_core_k<8>(a, s);
+    case 10: return launch_knn_core_k<10>(a, s);
     case 11: return launch_knn_core_k<11>(a, s);
     case 16: return launch_knn_core_k<16>(a, s);
     case 32: return launch_knn_core_k<32>(a, s);
@@ -155,6 +158,7 @@ hipError_t launch_knn_merge(int K, const KnnArgs &a, hipStream_t s) {
     case 2: return launch_knn_merge_k<2>(a, s);
     case 4: return launch_knn_merge_k<4>(a, s);
     case 8: return launch_knn_merge_k<8>(a, s);
+    case 10: return launch_knn_merge_k<10>(a, s);
     case 11: return launch_knn_merge_k<11>(a, s);
     case 16: return launch_knn_merge_k<16>(a, s);
     case 32: return launch_knn_merge_k<32>(a, s);

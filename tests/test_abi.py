@@ -73,7 +73,7 @@ def test_knn_plan_of_the_clip_and_section_workloads(lib):
     assert p[3] == 5 and p[6] >= p[3]
 
 
-K_LIST = (2, 4, 8, 11, 16, 32)
+K_LIST = (2, 4, 8, 10, 11, 16, 32)
 
 
 def test_knn_plan_invariants_and_workspace(lib):
