@@ -135,7 +135,7 @@ void timer_set_flop(int64_t pos, double flop) {
 
 // ---- kNN planning -----------------------------------------------------------
 struct KnnPlan {
-    int K, QM, TR, QT, chunks;
+    int K, QM, TR, QT;
     int64_t rows;   // rows per chunk
     int64_t tiles;  // database tiles
     int64_t slots;  // workgroups resident at once, per chunk in flight
@@ -164,7 +164,7 @@ constexpr int kChunkStreams = 2;          // chunks of one kNN call in flight at
 // allow (four-wave workgroups), fewer if the double-buffered LDS tile and its
 // norms do not fit that many times (the lists live in registers)
 int64_t knn_groups_per_cu(int K, int QM) {
-    const int64_t tr = tile_rows(QM), rs = 4 * QM + 4;
+    const int64_t tr = tile_rows(QM), rs = 4 * qm_pad(QM) + 4;
     // tile double buffer, its norms, and the slow path's dot products (column blocks x rows per lane)
     const int64_t lds = 2 * tr * rs * 4 + 2 * tr * 4 + knn_col_blocks(K, QM) * 4 * (tr / 16) * kThreads * 4;
     const int64_t by_lds = kLdsPerCu / lds;
@@ -220,7 +220,7 @@ int64_t chunk_part_entries(const KnnPlan &p, int64_t rows) {
 // Boruvka scan workgroups resident per CU (the double-buffered LDS tile with
 // its rows' norms, component labels and core distances)
 int64_t scan_groups_per_cu(int QM) {
-    const int64_t tr = tile_rows(QM), rs = 4 * QM + 4;
+    const int64_t tr = tile_rows(QM), rs = 4 * qm_pad(QM) + 4;
     const int64_t lds = 2 * tr * rs * 4 + 2 * 3 * tr * 4;
     const int64_t by_lds = kLdsPerCu / lds;
     const int64_t want = scan_waves_per_simd(QM);
@@ -234,7 +234,6 @@ KnnPlan plan_knn(int64_t n, int64_t m, int d, int k, int64_t max_chunk_dots, int
     p.QM = pick_qm(d);
     p.TR = tile_rows(p.QM);
     p.QT = knn_query_tile(p.K, p.QM);
-    p.chunks = feature_chunks(d);
     p.rows = n;
     if (max_chunk_dots > 0 && m > 0) {
         const int64_t r = max_chunk_dots / m / p.QT * p.QT;
@@ -247,7 +246,7 @@ KnnPlan plan_knn(int64_t n, int64_t m, int d, int k, int64_t max_chunk_dots, int
     const int64_t nchunks = (n + p.rows - 1) / p.rows;
     p.conc = (int)std::max<int64_t>(1, std::min<int64_t>(std::min(kChunkStreams, max_conc), nchunks));
     p.slots = std::max<int64_t>(1, kCUs * knn_groups_per_cu(p.K, p.QM) / p.conc);
-    p.warm = kWarmupWork * 32 / (4 * p.chunks * p.TR); // measured at 32-row tiles
+    p.warm = kWarmupWork * 32 / (qm_pad(p.QM) * p.TR); // measured at 32-row tiles
     p.part_entries = chunk_part_entries(p, p.rows);
     if (n % p.rows) p.part_entries = std::max(p.part_entries, chunk_part_entries(p, n % p.rows));
     return p;

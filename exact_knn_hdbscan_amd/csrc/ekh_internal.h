@@ -19,9 +19,13 @@ namespace ekh {
 constexpr int kWaves = 4;             // waves per workgroup (two workgroups per CU)
 constexpr int kThreads = kWaves * 64; // 256 threads
 
-// QM = k-steps of the contraction (4 features each), 4 * feature_chunks(d):
-// the tile kernels are instantiated for every 16-feature chunk count (QM = 4,
-// 8, ..., 64), so the k-loop is always fully unrolled with no runtime guard.
+// QM = k-steps of the contraction (one feature per lane group each, four per
+// k-step), 2 * ceil(d / 8): the tile kernels are instantiated for every even
+// QM (2, 4, ..., 64), so the k-loop is always fully unrolled with no runtime
+// guard.  Lane group g supplies features g * QM .. g * QM + QM - 1; in a
+// point-major row each group's features fill a segment of qm_pad(QM) (QM
+// rounded up to 4) positions, zero past QM, so a lane reads four k-steps of
+// its operand with one aligned 16-byte read.
 // CB = 16-column query blocks per wave; TR = database rows per LDS tile.
 constexpr int kMaxQM = 64;
 template <int QM> struct TileGeo {
@@ -38,10 +42,10 @@ inline int pick_k(int k) {
         if (k <= kKList[i]) return kKList[i];
     return -1;
 }
-// 16-feature chunks actually run for dimension d (identical in every kernel,
-// which keeps D2 bitwise the same everywhere)
-inline int feature_chunks(int d) { return (d + 15) / 16; }
-inline int pick_qm(int d) { return 4 * feature_chunks(d); }
+// k-steps run for dimension d (identical in every kernel, which keeps D2
+// bitwise the same everywhere), and the positions of one lane group's segment
+__host__ __device__ constexpr int pick_qm(int d) { return 2 * ((d + 7) / 8); }
+__host__ __device__ constexpr int qm_pad(int qm) { return (qm + 3) & ~3; }
 inline int tile_rows(int qm) { return qm > 56 ? 16 : 32; }
 // kNN tile kernel occupancy: three waves per SIMD where the registers fit
 // without spills (d <= 64 and K <= 16; d <= 128 and K <= 11), two otherwise
@@ -53,13 +57,22 @@ constexpr int knn_col_blocks(int K, int QM) { return (K > 11 || QM > 16) ? 1 : 2
 constexpr int scan_col_blocks(int QM) { return QM > 16 ? 1 : 2; }
 inline int knn_query_tile(int K, int QM) { return kWaves * 16 * knn_col_blocks(K, QM); }
 inline int scan_query_tile(int QM) { return kWaves * 16 * scan_col_blocks(QM); }
-// row stride (floats) of the point-major copies the tiles read: every feature a
-// tile loads, zero past d
-inline int tile_dim(int d) { return 16 * feature_chunks(d); }
+// row stride (floats) of the point-major copies the tiles read: four segments
+// of qm_pad(QM) positions (16 * ceil(d / 16) floats); position g * qm_pad(QM) + s
+// holds feature g * QM + s for s < QM and g * QM + s < d, every other position
+// zero
+__host__ __device__ constexpr int tile_dim(int d) { return 4 * qm_pad(pick_qm(d)); }
+// feature at position p of a point-major row (-1: a zero position)
+__host__ __device__ constexpr int pm_feature(int p, int qm, int d) {
+    const int qp = qm_pad(qm), s = p % qp, f = (p / qp) * qm + s;
+    return s < qm && f < d ? f : -1;
+}
 
-// X(QM) for every instantiated QM (the multiples of 4 up to kMaxQM), e.g. the
+// X(QM) for every instantiated QM (the even numbers up to kMaxQM), e.g. the
 // cases of a switch on a runtime QM.
-#define EKH_FOR_EACH_QM(X) X(4) X(8) X(12) X(16) X(20) X(24) X(28) X(32) X(36) X(40) X(44) X(48) X(52) X(56) X(60) X(64)
+#define EKH_FOR_EACH_QM(X)                                                                                             \
+    X(2) X(4) X(6) X(8) X(10) X(12) X(14) X(16) X(18) X(20) X(22) X(24) X(26) X(28) X(30) X(32) X(34) X(36) X(38)     \
+        X(40) X(42) X(44) X(46) X(48) X(50) X(52) X(54) X(56) X(58) X(60) X(62) X(64)
 
 // Correctly rounded float32 square root.  (__fsqrt_rn lowers to the native,
 // approximate instruction in this toolchain; __builtin_sqrtf gets the correctly
@@ -101,8 +114,8 @@ struct KnnArgs {
     int32_t *out_idx; // [n, k_out] absolute rows
     float *out_dist;  // [n, k_out] (kOutKnn) or d2 lists (kOutCore)
     float *out_core;  // [n]
-    const float *Bt;  // database point-major [m, dp], features >= d zero (the tiles and the direct differences read it)
-    int dp;           // row stride of Bt: tile_dim(d) = 16 * feature_chunks(d)
+    const float *Bt;  // database point-major [m, dp] (segment layout of tile_dim; the tiles and the direct differences read it)
+    int dp;           // row stride of Bt: tile_dim(d)
 };
 
 // host launchers (return hipError_t of the launch)
@@ -139,8 +152,8 @@ struct ScanArgs {
     const float *nrm;     // |x|^2 [n]
     const float *core;    // [n]
     const int32_t *comp;  // component label of every point
-    // database side, point-major rows [nb, dp] (features >= d zero): all
-    // points, or a gathered subset whose row j is point orig[j]
+    // database side, point-major rows [nb, dp] (segment layout of tile_dim):
+    // all points, or a gathered subset whose row j is point orig[j]
     const float *Xb;
     int dp;
     int64_t nb;

@@ -1,5 +1,5 @@
 // Instantiation of the kNN tile and merge kernels for one list length K (the
-// tile kernel once per 16-feature chunk count).  Compiled once per K with
+// tile kernel once per k-step count QM).  Compiled once per K with
 // -DEKH_KNN_K=<K> (2, 4, 8, 10, 11, 16, 32), so the instantiations build in
 // parallel.
 #include "tile_common.h"
@@ -16,8 +16,8 @@ template <int K, int QM> hipError_t knn_tile_launch(const KnnArgs &a, hipStream_
     constexpr int QT = kWaves * 16 * CB;
     const int64_t tail_q = (a.nq - a.body_q * QT + QT - 1) / QT;
     const int64_t groups = a.body_q + tail_q * a.splits;
-    if (a.body_q < 0 || tail_q < 0 || a.splits < 1 || groups > 0x7fffffff || a.dp != 4 * QM || a.d > 4 * QM ||
-        a.d <= 4 * QM - 16)
+    if (a.body_q < 0 || tail_q < 0 || a.splits < 1 || groups > 0x7fffffff || a.dp != tile_dim(a.d) ||
+        pick_qm(a.d) != QM)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL((knn_tile_kernel<K, QM>), dim3((unsigned)groups), dim3(kThreads), 0, s, a);
     return hipGetLastError();

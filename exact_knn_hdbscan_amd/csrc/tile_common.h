@@ -29,18 +29,20 @@ __device__ __forceinline__ f4 mfma16(float a, float b, f4 c) {
 }
 
 // ---------------------------------------------------------------- tile loop
-// Feature order of the contraction: with QM = 4 * ceil(d / 16) k-steps, lane
+// Feature order of the contraction: with QM = 2 * ceil(d / 8) k-steps, lane
 // group g supplies feature g * QM + s at k-step s (features >= d are zero).
 // Any fixed assignment of features to (s, g) gives the same dot product up to
 // rounding; using this one in every kernel keeps D2 bitwise identical (and
-// symmetric), and it lets a lane read four consecutive k-steps of its A
-// operand with one 16-byte LDS read.
+// symmetric).  In a point-major row (and an LDS tile row) group g's features
+// sit at positions g * QP + s, QP = QM rounded up to 4, so a lane reads four
+// consecutive k-steps of its A operand with one aligned 16-byte LDS read.
 template <int QM> struct Tile {
     static constexpr int TR = TileGeo<QM>::TR;  // database rows per tile
     static constexpr int RB = TR / 16;          // 16-row blocks per tile
-    static constexpr int FD = QM * 4;           // features per row (d <= FD, zero past d)
+    static constexpr int QP = qm_pad(QM);       // positions of a lane group's segment
+    static constexpr int FD = QP * 4;           // floats per row (tile_dim(d))
     static constexpr int RS = FD + 4;           // LDS row stride in floats: 16-byte reads of 8 rows hit distinct banks
-    static constexpr int NP = TR * QM;          // 16-byte pieces per tile
+    static constexpr int NP = TR * QP;          // 16-byte pieces per tile
     static constexpr int NL = (NP + kThreads - 1) / kThreads; // pieces each thread loads per tile
 };
 
@@ -56,12 +58,12 @@ template <int QM> struct Tile {
 // features: a slot is refilled only after the barrier that follows its tile's
 // epilogue.  The two slots' MFMA blocks and stores are separate code, so their
 // LDS addresses are immediate offsets rather than per-tile vector additions.
-// The kernels are instantiated per 16-feature chunk count, so the k-loop runs
-// all QM k-steps, fully unrolled, with the next k-steps' A operands read ahead.
+// The kernels are instantiated per k-step count, so the k-loop runs all QM
+// k-steps, fully unrolled, with the next k-steps' A operands read ahead.
 //
-// The database is read from its point-major copy Bp: row j holds features
-// 0 .. dp - 1 of point j with dp = 4 * QM (features >= d are zero), so a
-// tile is one contiguous block of TR * dp floats.  Thread tid loads its 16-byte
+// The database is read from its point-major copy Bp: row j holds point j in
+// the segment layout above, dp = 4 * QP floats (zero at the padding
+// positions and past d), so a tile is one contiguous block of TR * dp floats.  Thread tid loads its 16-byte
 // pieces tid, tid + 256, ... of the block (coalesced) with buffer loads whose
 // base is the tile's first row (a scalar) and whose lane offsets never change;
 // each piece goes to LDS with one 16-byte store.  Point counts are below 2^31,
@@ -81,7 +83,6 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ Bp, int32_t 
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, g = lane >> 4, li = lane & 15;
-    constexpr int qs = QM; // k-steps run
 
     // this thread's pieces: LDS position (row * RS + 4 * column) and whether
     // the piece exists (a tile may have fewer pieces than 256 * NL)
@@ -91,7 +92,7 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ Bp, int32_t 
     for (int h = 0; h < T::NL; ++h) {
         const int c = tid + kThreads * h;
         has[h] = T::NP % kThreads == 0 || c < T::NP;
-        const int row = c / QM, col = c - row * QM;
+        const int row = c / T::QP, col = c - row * T::QP;
         lds_off[h] = row * T::RS + 4 * col;
     }
     const int lrow = tid % T::TR; // the thread also loads row lrow's norm (and payload)
@@ -171,8 +172,8 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ Bp, int32_t 
         for (int rb = 0; rb < T::RB; ++rb)
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f4{0.f, 0.f, 0.f, 0.f};
-        // this lane's feature block of each row it reads
-        const float *tl = sm_tile[buf] + li * T::RS + g * qs;
+        // this lane's feature segment of each row it reads
+        const float *tl = sm_tile[buf] + li * T::RS + g * T::QP;
         constexpr int PRE = 4; // k-steps whose A operands are read at once (one 16-byte read per row block)
 #pragma unroll
         for (int s0 = 0; s0 < QM; s0 += PRE) {
@@ -180,7 +181,7 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ Bp, int32_t 
 #pragma unroll
             for (int rb = 0; rb < T::RB; ++rb) a4[rb] = *reinterpret_cast<const f4 *>(tl + rb * 16 * T::RS + s0);
 #pragma unroll
-            for (int s = 0; s < PRE; ++s)
+            for (int s = 0; s < PRE && s0 + s < QM; ++s)
 #pragma unroll
                 for (int rb = 0; rb < T::RB; ++rb)
 #pragma unroll
@@ -647,13 +648,14 @@ template <int K> __global__ __launch_bounds__(256) void knn_merge_kernel(KnnArgs
 // distances and the core distances: sum_f (q_f - y_f)^2 with fmaf in feature
 // order, which carries no cancellation error.  One lane per (row, list entry)
 // "slot", kRowLanes lanes per row (a power of two >= K): 64 slots per wave.
-// Each lane sums its own slot in feature order, 16 features (one chunk) at a
-// time, from LDS: the wave first stages the chunk of every slot's neighbour
-// (its 64 bytes of the point-major copy Bt, read by four adjacent lanes, so a
-// load instruction touches 16 cache lines instead of 64) and of its rows'
-// query features (feature-major source), with the next two chunks' loads
-// already in flight.  Padding features are zero on both sides and add exact
-// zeros.  The row's order is then taken across its lanes by ranks (shuffles),
+// Each lane sums its own slot over the positions of the point-major layout in
+// order, 16 (one chunk) at a time, from LDS: the wave first stages the chunk
+// of every slot's neighbour (its 64 bytes of the point-major copy Bt, read by
+// four adjacent lanes, so a load instruction touches 16 cache lines instead
+// of 64) and the same positions of its rows' query features (feature-major
+// source), with the next two chunks' loads already in flight.  Positions run
+// through the features in order; the padding positions are zero on both sides
+// and add exact zeros.  The row's order is then taken across its lanes by ranks (shuffles),
 // with no sort network.
 template <int K> struct DirectRows {
     static constexpr int kRowLanes = K <= 16 ? 16 : 32;
@@ -699,14 +701,17 @@ __device__ __forceinline__ bool direct_d2(const KnnArgs &a, float *lds, int64_t 
     }
     const int xr = lane % R::kRowsPerWave, xf = lane / R::kRowsPerWave;
     const bool xrow = qb + xr < a.nq && xf < 16;
-    const float *xsrc = a.Q + a.q0 + (xrow ? qb + xr : 0) + (int64_t)xf * a.ldq;
+    const float *xsrc = a.Q + a.q0 + (xrow ? qb + xr : 0);
+    const int qm = pick_qm(a.d);
     float *yw = lds + wave * kDirectWaveFloats; // [64][kSlotStride]
     float *xw = yw + 64 * kSlotStride;          // [rows][kSlotStride]
 
     auto load = [&](int c, f4 (&yv)[4], float &xv) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) yv[p] = yhas[p] ? *reinterpret_cast<const f4 *>(ysrc[p] + c * 16) : f4{0.f, 0.f, 0.f, 0.f};
-        xv = (xrow && c * 16 + xf < a.d) ? xsrc[(int64_t)c * 16 * a.ldq] : 0.f;
+        // the query feature at this position of the point-major layout (none: zero)
+        const int f = pm_feature(c * 16 + xf, qm, a.d);
+        xv = (xrow && f >= 0) ? xsrc[(int64_t)f * a.ldq] : 0.f;
     };
     const int nc = a.dp / 16;
     f4 ya[4], yb[4];

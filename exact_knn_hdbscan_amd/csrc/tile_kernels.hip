@@ -10,16 +10,13 @@ namespace ekh {
 // chain as the tile kernels (same feature order, same k-step sequence, starting
 // from 0).  So the norm of x equals, bit for bit, the dot product the tile
 // kernels compute for x against any bitwise-identical point, and identical
-// points get D2 = fma(-2, n, 2n) = 0 exactly.
-// Squared norms of 64 points per workgroup (16 per wave), as the diagonal of
-// the same MFMA chain the tile kernels run, so that a point's distance to
-// itself is exactly 0.
-__device__ __forceinline__ void norms_block(const float *__restrict__ X, int64_t ldx, int64_t n, int d, int chunks,
+// points get D2 = fma(-2, n, 2n) = 0 exactly.  64 points per workgroup (16 per
+// wave); qs = the k-step count QM of the tile kernels for this d.
+__device__ __forceinline__ void norms_block(const float *__restrict__ X, int64_t ldx, int64_t n, int d, int qs,
                                             float *__restrict__ out, int64_t block) {
     const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
     const int64_t p = (block * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 16 + li;
     const bool valid = p < n;
-    const int qs = 4 * chunks;
     f4 acc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
     for (int s = 0; s < qs; ++s) {
@@ -32,25 +29,27 @@ __device__ __forceinline__ void norms_block(const float *__restrict__ X, int64_t
     if (valid && (li >> 2) == g) out[p] = acc[li & 3];
 }
 
-// Point-major copy of a feature-major point set, for gathers of whole points:
-// Bt[j * dp + f] = B[f * ldb + j] for f < d, 0 for d <= f < dp.  One 32 x 32
-// tile per workgroup, through LDS (one padding column), coalesced on both sides.
-__device__ __forceinline__ void point_major_block(const float *__restrict__ B, int64_t ldb, int64_t m, int d, int dp,
-                                                  float *__restrict__ Bt, int64_t bx, int by) {
+// Point-major copy of a feature-major point set, for tiles and gathers of
+// whole points: Bt[j * dp + p] = B[f * ldb + j] for the feature f at position p
+// (pm_feature), 0 at the positions that hold none.  One 32-position x
+// 32-point tile per workgroup, through LDS (one padding column), coalesced on
+// both sides.
+__device__ __forceinline__ void point_major_block(const float *__restrict__ B, int64_t ldb, int64_t m, int d, int qm,
+                                                  int dp, float *__restrict__ Bt, int64_t bx, int by) {
     __shared__ float t[32][33];
     const int64_t j0 = bx * 32;
-    const int f0 = by * 32;
+    const int p0 = by * 32;
     const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
     for (int r = ty; r < 32; r += 8) {
-        const int f = f0 + r;
+        const int f = pm_feature(p0 + r, qm, d);
         const int64_t j = j0 + tx;
-        t[r][tx] = (f < d && j < m) ? B[(int64_t)f * ldb + j] : 0.f;
+        t[r][tx] = (f >= 0 && j < m) ? B[(int64_t)f * ldb + j] : 0.f;
     }
     __syncthreads();
     for (int r = ty; r < 32; r += 8) {
         const int64_t j = j0 + r;
-        const int f = f0 + tx;
-        if (j < m && f < dp) Bt[j * dp + f] = t[tx][r];
+        const int p = p0 + tx;
+        if (j < m && p < dp) Bt[j * dp + p] = t[tx][r];
     }
 }
 
@@ -65,19 +64,19 @@ struct PrepArgs {
     const float *X, *Y;
     int64_t ldx, n, ldy, m;
     float *nx, *ny, *Bt;
-    int d, dp, chunks;
+    int d, dp, qm;
     int64_t bx, by, tiles_x; // workgroups of the X norms, of the Y norms; point-major tiles per feature block
 };
 
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     const int64_t b = blockIdx.x;
     if (b < a.bx) {
-        norms_block(a.X, a.ldx, a.n, a.d, a.chunks, a.nx, b);
+        norms_block(a.X, a.ldx, a.n, a.d, a.qm, a.nx, b);
     } else if (b < a.bx + a.by) {
-        norms_block(a.Y, a.ldy, a.m, a.d, a.chunks, a.ny, b - a.bx);
+        norms_block(a.Y, a.ldy, a.m, a.d, a.qm, a.ny, b - a.bx);
     } else {
         const int64_t t = b - a.bx - a.by;
-        point_major_block(a.Y, a.ldy, a.m, a.d, a.dp, a.Bt, t % a.tiles_x, (int)(t / a.tiles_x));
+        point_major_block(a.Y, a.ldy, a.m, a.d, a.qm, a.dp, a.Bt, t % a.tiles_x, (int)(t / a.tiles_x));
     }
 }
 } // namespace
@@ -96,7 +95,8 @@ hipError_t launch_prep(const float *X, int64_t ldx, int64_t n, float *nx, const 
     a.Bt = Bt;
     a.d = d;
     a.dp = dp;
-    a.chunks = feature_chunks(d);
+    a.qm = pick_qm(d);
+    if (dp != tile_dim(d)) return hipErrorInvalidValue;
     a.bx = nx ? norm_blocks(n) : 0;
     a.by = ny ? norm_blocks(m) : 0;
     a.tiles_x = (m + 31) / 32;
@@ -300,7 +300,7 @@ void scan_tile_kernel(ScanArgs a) {
 }
 
 template <int QM> static hipError_t scan_launch(const ScanArgs &a, int64_t grid, hipStream_t s) {
-    if (a.dp != 4 * QM || a.d > 4 * QM || a.d <= 4 * QM - 16) return hipErrorInvalidValue;
+    if (a.dp != tile_dim(a.d) || pick_qm(a.d) != QM) return hipErrorInvalidValue;
     hipLaunchKernelGGL((scan_tile_kernel<QM>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
