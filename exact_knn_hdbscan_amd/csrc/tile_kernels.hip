@@ -181,10 +181,17 @@ __device__ __forceinline__ float scan_threshold(float w) {
     return t < FLT_MAX ? t : FLT_MAX;
 }
 
+// Fast test per element, as in the kNN epilogue: t = fma(-2, s, nb) against
+// thq = thr - na, widened by 2^-20 (thr + na).  Every element whose D2 =
+// fma(-2, s, na + nb) is <= thr has t <= thq (the rounding errors between D2
+// and t + na are a few units of 2^-24 (na + nb + thr), and nb <= 2 na + 2 thr
+// for such an element), so the test never skips a candidate; the exact D2
+// decides in candidate().
 template <int CB, int RB> struct EpiScan {
     uint64_t best[CB];
     uint64_t init[CB];
     float thr[CB];
+    float thq[CB];
     float na[CB];
     float corea[CB];
     int32_t ca[CB];
@@ -200,8 +207,13 @@ template <int CB, int RB> struct EpiScan {
         const uint64_t key = ((uint64_t)__float_as_uint(W) << 32) | b;
         if (key < best[cb]) {
             best[cb] = key;
-            thr[cb] = scan_threshold(W);
+            set_threshold(cb, scan_threshold(W));
         }
+    }
+    __device__ __forceinline__ void set_threshold(int cb, float t) {
+        constexpr float kWiden = 1.0f / 1048576.0f;
+        thr[cb] = t;
+        thq[cb] = fmaf(t, 1.0f + kWiden, -na[cb] * (1.0f - kWiden));
     }
     __device__ __forceinline__ void tile(const f4 (&acc)[RB][CB], const float *nrm, const int32_t *comp,
                                          const float *core, int64_t j0) {
@@ -210,11 +222,14 @@ template <int CB, int RB> struct EpiScan {
         for (int rb = 0; rb < RB; ++rb) nb4[rb] = *reinterpret_cast<const f4 *>(nrm + rb * 16 + 4 * g);
         bool hit = false;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+        for (int cb = 0; cb < CB; ++cb) {
+            float mn = INFINITY;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+            for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb) hit |= fmaf(-2.f, acc[rb][cb][r], na[cb] + nb4[rb][r]) <= thr[cb];
+                for (int r = 0; r < 4; ++r) mn = fminf(mn, fmaf(-2.f, acc[rb][cb][r], nb4[rb][r]));
+            hit |= mn <= thq[cb];
+        }
         if (!hit) return;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -279,7 +294,7 @@ void scan_tile_kernel(ScanArgs a) {
             if (own != kNoEdge) w0 = fminf(w0, __uint_as_float((uint32_t)(own >> 32)));
             epi.init[cb] = ((uint64_t)__float_as_uint(w0) << 32) | 0xffffffffull;
             epi.best[cb] = epi.init[cb];
-            epi.thr[cb] = (!valid[cb] || epi.corea[cb] > w0) ? -INFINITY : scan_threshold(w0);
+            epi.set_threshold(cb, (!valid[cb] || epi.corea[cb] > w0) ? -INFINITY : scan_threshold(w0));
         }
         const int64_t tb = a.tiles * split / sp, te = a.tiles * (split + 1) / sp;
         run_tiles<QM, CB, true>(a.Xb, (int32_t)a.nb, a.nrm_b, a.comp_b, a.core_b, (int32_t)tb, (int32_t)te, bq, epi);
