@@ -166,7 +166,8 @@ constexpr int kChunkStreams = 2;          // chunks of one kNN call in flight at
 int64_t knn_groups_per_cu(int K, int QM) {
     const int64_t tr = tile_rows(QM), rs = 4 * qm_pad(QM) + 4;
     // tile double buffer, its norms, and the slow path's dot products (column blocks x rows per lane)
-    const int64_t lds = 2 * tr * rs * 4 + 2 * tr * 4 + knn_col_blocks(K, QM) * 4 * (tr / 16) * kThreads * 4;
+    const int64_t nbuf = 2 * knn_tiles_per_barrier(QM);
+    const int64_t lds = nbuf * tr * rs * 4 + nbuf * tr * 4 + knn_col_blocks(K, QM) * 4 * (tr / 16) * kThreads * 4;
     const int64_t by_lds = kLdsPerCu / lds;
     const int64_t want = knn_waves_per_simd(K, QM);
     return by_lds < want ? (by_lds < 1 ? 1 : by_lds) : want;

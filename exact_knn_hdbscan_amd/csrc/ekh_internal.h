@@ -52,6 +52,9 @@ inline int tile_rows(int qm) { return qm > 56 ? 16 : 32; }
 constexpr int knn_waves_per_simd(int K, int QM) { return (QM <= 16 && K <= 16) || (QM <= 32 && K <= 11) ? 3 : 2; }
 // Boruvka scan kernel occupancy: three waves per SIMD for d <= 128, two otherwise
 constexpr int scan_waves_per_simd(int QM) { return QM <= 32 ? 3 : 2; }
+// kNN tiles per barrier of the tile loop: two (four LDS tile buffers) where
+// they fit three workgroups per CU, d <= 64
+constexpr int knn_tiles_per_barrier(int QM) { return QM <= 16 ? 2 : 1; }
 // 16-column query blocks per wave: two when the registers allow it
 constexpr int knn_col_blocks(int K, int QM) { return (K > 11 || QM > 16) ? 1 : 2; }
 constexpr int scan_col_blocks(int QM) { return QM > 16 ? 1 : 2; }

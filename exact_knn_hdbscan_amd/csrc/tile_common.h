@@ -46,18 +46,20 @@ template <int QM> struct Tile {
     static constexpr int NL = (NP + kThreads - 1) / kThreads; // pieces each thread loads per tile
 };
 
-// Streams database tiles [t_begin, t_end) through a double-buffered LDS tile
+// Streams database tiles [t_begin, t_end) through LDS tile buffers
 // (row-major: [row][feature]) and hands each tile's accumulator blocks to
-// epi.tile().  One trip and one barrier per tile: the global loads of tile
-// t + 1 are in flight while the MFMAs and the epilogue of tile t run.  One
+// epi.tile().  With TPB = 1, two buffers and one barrier per tile: the global
+// loads of tile t + 1 are in flight while the MFMAs and the epilogue of tile t
+// run.  With TPB = 2, four buffers and one barrier per two tiles (see the
+// loop).  One
 // accumulator set and one prefetch set keep the registers low enough for
 // three waves per SIMD (d <= 64), so that while one wave waits at its barrier
 // or works through its epilogue, the others keep the MFMA pipe busy.  Per-row
 // norms (and, with PAYLOAD, component labels and core distances) live in a
-// second LDS pair of slots, tile t's in slot (t - t_begin) mod 2 like its
-// features: a slot is refilled only after the barrier that follows its tile's
-// epilogue.  The two slots' MFMA blocks and stores are separate code, so their
-// LDS addresses are immediate offsets rather than per-tile vector additions.
+// second set of LDS slots, tile t's in the slot of its features' buffer: a
+// slot is refilled only after a barrier that follows its tile's epilogue.
+// Each buffer's MFMA block and stores are separate code, so their LDS
+// addresses are immediate offsets rather than per-tile vector additions.
 // The kernels are instantiated per k-step count, so the k-loop runs all QM
 // k-steps, fully unrolled, with the next k-steps' A operands read ahead.
 //
@@ -68,7 +70,7 @@ template <int QM> struct Tile {
 // base is the tile's first row (a scalar) and whose lane offsets never change;
 // each piece goes to LDS with one 16-byte store.  Point counts are below 2^31,
 // so tile and row counters are 32-bit scalars.
-template <int QM, int CB, bool PAYLOAD, class Epi>
+template <int QM, int CB, bool PAYLOAD, int TPB, class Epi>
 __device__ __forceinline__ void run_tiles(const float *__restrict__ Bp, int32_t m_, const float *__restrict__ nrm_b,
                                           const int32_t *__restrict__ comp_b, const float *__restrict__ core_b,
                                           int32_t t_begin_, int32_t t_end_, const float (&bq)[CB][QM], Epi &epi) {
@@ -76,10 +78,11 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ Bp, int32_t 
     const uint32_t t_begin = __builtin_amdgcn_readfirstlane((uint32_t)t_begin_);
     const uint32_t t_end = __builtin_amdgcn_readfirstlane((uint32_t)t_end_);
     const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)m_);
-    __shared__ __align__(16) float sm_tile[2][T::TR * T::RS];
-    __shared__ __align__(16) float sm_nrm[2][T::TR];
-    __shared__ int32_t sm_comp[2][PAYLOAD ? T::TR : 1];
-    __shared__ float sm_core[2][PAYLOAD ? T::TR : 1];
+    constexpr int NBUF = 2 * TPB;
+    __shared__ __align__(16) float sm_tile[NBUF][T::TR * T::RS];
+    __shared__ __align__(16) float sm_nrm[NBUF][T::TR];
+    __shared__ int32_t sm_comp[NBUF][PAYLOAD ? T::TR : 1];
+    __shared__ float sm_core[NBUF][PAYLOAD ? T::TR : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, g = lane >> 4, li = lane & 15;
@@ -197,27 +200,70 @@ __device__ __forceinline__ void run_tiles(const float *__restrict__ Bp, int32_t 
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
     Pref P;
-    load(P, t_begin);
-    store(P, B0{});
-    __syncthreads();
     f4 acc[T::RB][CB];
-    uint32_t rcur = P.row0; // tile t's first row
-    for (uint32_t t = t_begin; t < t_end; ++t) {
-        const bool odd = ((t - t_begin) & 1u) != 0u; // wave-uniform: tile t's buffer and norm slot
-        if (t + 1 < t_end) load(P, t + 1);
-        if (odd)
-            mma(B1{}, acc);
-        else
-            mma(B0{}, acc);
-        finish(acc, rcur, odd ? 1 : 0);
-        if (t + 1 < t_end) {
+    if constexpr (TPB == 1) {
+        load(P, t_begin);
+        store(P, B0{});
+        __syncthreads();
+        uint32_t rcur = P.row0; // tile t's first row
+        for (uint32_t t = t_begin; t < t_end; ++t) {
+            const bool odd = ((t - t_begin) & 1u) != 0u; // wave-uniform: tile t's buffer and norm slot
+            if (t + 1 < t_end) load(P, t + 1);
             if (odd)
-                store(P, B0{});
+                mma(B1{}, acc);
             else
-                store(P, B1{});
+                mma(B0{}, acc);
+            finish(acc, rcur, odd ? 1 : 0);
+            if (t + 1 < t_end) {
+                if (odd)
+                    store(P, B0{});
+                else
+                    store(P, B1{});
+            }
+            __syncthreads();
+            rcur = P.row0;
+        }
+    } else {
+        // Four buffers, tile t in buffer (t - t_begin) mod 4, and a barrier after
+        // every second tile: tile t + 2 is loaded while tile t's MFMAs and
+        // epilogue run and stored into the buffer that tile t - 2 used (read
+        // before the barrier that followed tile t - 1 or t - 2), and a barrier
+        // separates that store from tile t + 2's reads.
+        static_assert(TPB == 2, "one or two tiles per barrier");
+        using B2 = std::integral_constant<int, 2>;
+        using B3 = std::integral_constant<int, 3>;
+        load(P, t_begin);
+        store(P, B0{});
+        uint32_t r0 = P.row0, r1 = P.row0; // first rows of tiles t and t + 1
+        if (t_begin + 1 < t_end) {
+            load(P, t_begin + 1);
+            store(P, B1{});
+            r1 = P.row0;
         }
         __syncthreads();
-        rcur = P.row0;
+        for (uint32_t t = t_begin; t < t_end; ++t) {
+            const uint32_t b = (t - t_begin) & 3u; // wave-uniform: tile t's buffer and norm slot
+            const bool next = t + 2 < t_end;
+            if (next) load(P, t + 2);
+            switch (b) {
+            case 0: mma(B0{}, acc); break;
+            case 1: mma(B1{}, acc); break;
+            case 2: mma(B2{}, acc); break;
+            default: mma(B3{}, acc); break;
+            }
+            finish(acc, r0, (int)b);
+            if (next) {
+                switch (b) {
+                case 0: store(P, B2{}); break;
+                case 1: store(P, B3{}); break;
+                case 2: store(P, B0{}); break;
+                default: store(P, B1{}); break;
+                }
+            }
+            if (b & 1u) __syncthreads();
+            r0 = r1;
+            r1 = P.row0;
+        }
     }
 }
 
@@ -595,7 +641,7 @@ void knn_tile_kernel(KnnArgs a) {
     epi.g = g;
     epi.sv = sv;
     epi.tid = tid;
-    run_tiles<QM, CB, false>(a.Bt, (int32_t)a.m, a.nrm_b, nullptr, nullptr, (int32_t)tb, (int32_t)te, bq, epi);
+    run_tiles<QM, CB, false, knn_tiles_per_barrier(QM)>(a.Bt, (int32_t)a.m, a.nrm_b, nullptr, nullptr, (int32_t)tb, (int32_t)te, bq, epi);
 
     // merge the four lane groups that share each query column
 #pragma unroll

@@ -297,7 +297,7 @@ void scan_tile_kernel(ScanArgs a) {
             epi.set_threshold(cb, (!valid[cb] || epi.corea[cb] > w0) ? -INFINITY : scan_threshold(w0));
         }
         const int64_t tb = a.tiles * split / sp, te = a.tiles * (split + 1) / sp;
-        run_tiles<QM, CB, true>(a.Xb, (int32_t)a.nb, a.nrm_b, a.comp_b, a.core_b, (int32_t)tb, (int32_t)te, bq, epi);
+        run_tiles<QM, CB, true, 1>(a.Xb, (int32_t)a.nb, a.nrm_b, a.comp_b, a.core_b, (int32_t)tb, (int32_t)te, bq, epi);
 
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
