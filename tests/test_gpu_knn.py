@@ -124,6 +124,21 @@ def test_knn_integer_grid_exact(d):
         assert np.any(od2[:, 1:] == od2[:, :-1])
 
 
+@pytest.mark.parametrize("d", [7, 61])
+def test_knn_short_databases_every_tile_count(d):
+    """Databases of 1 to 5 tiles of 32 rows (full and partial last tiles): at
+    d <= 64 the tile loop takes a barrier after every second tile with four
+    buffers, so odd and even tile counts and a lone partial tile take
+    different paths through it."""
+    X = datagen.gaussian_mixture(700, d, 5, seed=d)
+    for m in (1, 2, 31, 32, 33, 63, 64, 65, 95, 96, 97, 128, 129, 160):
+        Y = datagen.gaussian_mixture(m, d, 3, seed=m)
+        k = min(10, m)
+        say("knn n=700 m=%d d=%d k=%d" % (m, d, k))
+        i, dd = ekh.knn(dev(X), dev(Y), k)
+        check_knn(X, Y, k, host(i), host(dd), rescored=True)
+
+
 def test_knn_k_equals_m_and_n():
     X = datagen.random_uniform(31, 9, seed=3)
     Y = datagen.random_uniform(20, 9, seed=4)
