@@ -161,11 +161,12 @@ constexpr int64_t kWarmupWork = 12000;    // warm-up of fresh lists, in 32-row t
 constexpr int kChunkStreams = 2;          // chunks of one kNN call in flight at once (measured: 2 best)
 
 // kNN workgroups resident per CU: one per wave per SIMD that the registers
-// allow (four-wave workgroups), fewer if the double-buffered LDS tile and its
-// norms do not fit that many times (the lists live in registers)
+// allow (four-wave workgroups), fewer if the LDS tile buffers (two, or four
+// where the tile loop takes a barrier per two tiles) and their norms do not fit
+// that many times (the lists live in registers)
 int64_t knn_groups_per_cu(int K, int QM) {
     const int64_t tr = tile_rows(QM), rs = 4 * qm_pad(QM) + 4;
-    // tile double buffer, its norms, and the slow path's dot products (column blocks x rows per lane)
+    // tile buffers, their norms, and the slow path's dot products (column blocks x rows per lane)
     const int64_t nbuf = 2 * knn_tiles_per_barrier(QM);
     const int64_t lds = nbuf * tr * rs * 4 + nbuf * tr * 4 + knn_col_blocks(K, QM) * 4 * (tr / 16) * kThreads * 4;
     const int64_t by_lds = kLdsPerCu / lds;
