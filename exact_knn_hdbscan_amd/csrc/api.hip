@@ -219,8 +219,9 @@ int64_t chunk_part_entries(const KnnPlan &p, int64_t rows) {
     return c.splits > 1 ? (rows - c.body_q * p.QT) * c.splits * p.K : 0;
 }
 
-// Boruvka scan workgroups resident per CU (the double-buffered LDS tile with
-// its rows' norms, component labels and core distances)
+// Boruvka scan workgroups resident per CU (the two LDS tile buffers with their
+// rows' norms, component labels and core distances; the scan keeps one barrier
+// per tile: four buffers spill its registers at d <= 64)
 int64_t scan_groups_per_cu(int QM) {
     const int64_t tr = tile_rows(QM), rs = 4 * qm_pad(QM) + 4;
     const int64_t lds = 2 * tr * rs * 4 + 2 * 3 * tr * 4;
