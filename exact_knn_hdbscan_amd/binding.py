@@ -408,10 +408,12 @@ def merge_tree(counts, gamma: float = 1.0):
 
 class kernel_timer:
     """Context manager around ekh_timer_enable / ekh_timer_read: HIP events on
-    the launch stream around every launch of the two dense kernels."""
+    the launch stream around every launch of the dense kernels (the kNN tile
+    kernel, the Boruvka scan, the symmetric self-kNN kernel)."""
 
     KNN_TILE = 0
     SCAN_TILE = 1
+    KNN_SYM = 2
 
     def __enter__(self):
         _check(library().ekh_timer_enable(1))

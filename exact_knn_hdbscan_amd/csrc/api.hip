@@ -14,6 +14,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -435,6 +436,181 @@ int run_knn(const KnnPlan &p, const float *X, int64_t ldx, int64_t n, const floa
     return EKH_OK;
 }
 
+// ---- symmetric self-kNN (ekh_core_distances) --------------------------------
+// Plan of the symmetric self-kNN: a bound pass of all points against every
+// kSymSubset-th point, the symmetric pass over the upper block triangle in
+// `splits` pieces per query tile, the merge, and the recomputation of the
+// query tiles whose column buffers overflowed.  Taken from kSymMinPoints
+// points on at d <= 64 (the kernels' instantiations), unless EKH_CORE_DENSE is
+// set in the environment (then every pair is computed from both sides, as in
+// ekh_knn).  The workspace query and the call must see the same setting.
+struct SymPlan {
+    bool on = false;
+    int K = 0, QM = 0, TR = 0, QT = 0;
+    int64_t ns = 0, qtiles = 0, tiles = 0;
+    int splits = 1;
+    double pairs = 0; // pairs the symmetric pass computes
+    KnnPlan pa{}, pf{};
+};
+
+SymPlan plan_sym(int64_t n, int d, int k) {
+    SymPlan p;
+    p.K = pick_k(k);
+    p.QM = pick_qm(d);
+    const char *env = getenv("EKH_CORE_DENSE");
+    p.on = n >= kSymMinPoints && p.QM <= 16 && p.K > 0 && !(env && env[0] && env[0] != '0');
+    if (!p.on) return p;
+    p.TR = tile_rows(p.QM);
+    p.QT = knn_query_tile(p.K, p.QM);
+    p.ns = (n + kSymSubset - 1) / kSymSubset;
+    p.qtiles = (n + p.QT - 1) / p.QT;
+    p.tiles = (n + p.TR - 1) / p.TR;
+    // tiles of the triangle; pieces per query tile so that none is longer than
+    // half of a resident workgroup's share (the longest run first)
+    const int64_t per = p.QT / p.TR;
+    int64_t work = 0;
+    for (int64_t t = 0; t < p.qtiles; ++t) {
+        work += p.tiles - t * per;
+        const int64_t q = std::min<int64_t>(p.QT, n - t * p.QT);
+        p.pairs += (double)q * (double)(n - t * p.QT);
+    }
+    const int64_t slots = kCUs * knn_groups_per_cu(p.K, p.QM);
+    while (p.splits < kSymMaxSplits && (p.tiles + p.splits - 1) / p.splits * 2 * slots > work) ++p.splits;
+    p.pa = plan_knn(n, p.ns, d, k, 0, 1);
+    p.pf = plan_knn(n, n, d, k, 0, 1);
+    return p;
+}
+
+struct SymWs {
+    float *nx, *bt, *bs, *nrm_s, *tau, *theta;
+    int32_t *idx;
+    Entry *part_a, *part_b, *part_f, *colbuf;
+    uint32_t *colcnt, *gate;
+};
+
+size_t sym_ws(const SymPlan &p, int64_t n, int d, int k, Carver &c, SymWs &w) {
+    const int dp = tile_dim(d);
+    w.nx = c.take<float>(n);
+    w.bt = c.take<float>((size_t)n * dp);
+    w.idx = c.take<int32_t>((size_t)n * k);
+    w.bs = c.take<float>((size_t)p.ns * dp);
+    w.nrm_s = c.take<float>(p.ns);
+    w.part_a = p.pa.part_entries ? c.take<Entry>((size_t)p.pa.part_entries) : nullptr;
+    w.tau = c.take<float>(n);
+    w.theta = c.take<float>(n);
+    w.part_b = c.take<Entry>((size_t)p.splits * n * p.K);
+    w.colbuf = c.take<Entry>((size_t)n * kSymColCap);
+    w.colcnt = c.take<uint32_t>(n);
+    w.gate = c.take<uint32_t>(p.qtiles);
+    w.part_f = p.pf.part_entries ? c.take<Entry>((size_t)p.pf.part_entries) : nullptr;
+    return c.used;
+}
+
+// One pass of a kNN plan with a single chunk (no row chunking), on stream s:
+// the tile launch and, for split tiles, their merge.  flop: the launch's
+// algorithmic flop for the timer (0 where the device decides the work: the
+// launch's time then counts with no flop).
+int run_single_chunk(const KnnPlan &p, KnnArgs a, double flop, hipStream_t s) {
+    const ChunkPlan cp = plan_chunk(p, a.nq);
+    a.body_q = cp.body_q;
+    a.splits = cp.splits;
+    a.tiles = p.tiles;
+    TimedLaunch tl(0, flop, s);
+    EKH_HIP(launch_knn_tile(p.K, p.QM, a, s));
+    tl.done();
+    if (cp.splits > 1) {
+        a.q0 += cp.body_q * p.QT;
+        a.nq -= cp.body_q * p.QT;
+        EKH_HIP(launch_knn_merge(p.K, a, s));
+    }
+    return EKH_OK;
+}
+
+int run_core_sym(const SymPlan &p, const float *X, int64_t ldx, int64_t n, int d, int ms, int32_t *out_idx,
+                 float *out_d2, float *out_core, const SymWs &w, hipStream_t s) {
+    const int k = ms + 1, dp = tile_dim(d);
+    int rc;
+    // norms and the point-major copy, then the subset's rows
+    EKH_HIP(launch_prep(X, ldx, n, w.nx, X, ldx, n, nullptr, w.bt, d, dp, s));
+    EKH_HIP(launch_subset_gather(w.bt, w.nx, n, dp, kSymSubset, w.bs, w.nrm_s, s));
+    KnnArgs a{};
+    a.Q = X;
+    a.ldq = ldx;
+    a.q0 = 0;
+    a.nq = n;
+    a.nrm_q = w.nx;
+    a.d = d;
+    a.dp = dp;
+    a.k_out = k;
+    a.min_samples = ms;
+    // bound pass: tau = D2 of each point's k-th neighbour among the subset
+    {
+        KnnArgs b = a;
+        b.Bt = w.bs;
+        b.m = p.ns;
+        b.nrm_b = w.nrm_s;
+        b.part = w.part_a;
+        b.out_mode = kOutBound;
+        b.out_core = w.tau;
+        if ((rc = run_single_chunk(p.pa, b, 2.0 * d * (double)n * (double)p.ns, s)) != EKH_OK) return rc;
+    }
+    EKH_HIP(launch_sym_setup(w.tau, w.nx, n, w.theta, w.colcnt, w.gate, p.qtiles, s));
+    // symmetric pass over the upper block triangle
+    a.Bt = w.bt;
+    a.m = n;
+    a.nrm_b = w.nx;
+    a.self = 1;
+    a.tiles = p.tiles;
+    a.splits = p.splits;
+    a.part = w.part_b;
+    a.tau = w.tau;
+    a.theta = w.theta;
+    a.colbuf = w.colbuf;
+    a.colcnt = w.colcnt;
+    a.colcap = kSymColCap;
+    {
+        TimedLaunch tl(2, 2.0 * d * p.pairs, s);
+        EKH_HIP(launch_knn_sym(p.K, p.QM, a, s));
+        tl.done();
+    }
+    // final lists: the row side's pieces with the column side's candidates
+    a.out_mode = kOutCore;
+    a.out_idx = out_idx;
+    a.out_dist = out_d2;
+    a.out_core = out_core;
+    a.gate_w = w.gate;
+    a.gate_rows = p.QT;
+    EKH_HIP(launch_sym_merge(p.K, a, s));
+    // the query tiles with an overflowed buffer, recomputed from both sides
+    {
+        KnnArgs f = a;
+        f.tau = nullptr;
+        f.theta = nullptr;
+        f.colbuf = nullptr;
+        f.colcnt = nullptr;
+        f.gate_w = nullptr;
+        f.gate = w.gate;
+        f.part = w.part_f;
+        if ((rc = run_single_chunk(p.pf, f, 0.0, s)) != EKH_OK) return rc;
+    }
+    // core distances by direct differences from the final lists
+    KnnArgs c{};
+    c.Q = X;
+    c.ldq = ldx;
+    c.q0 = 0;
+    c.nq = n;
+    c.m = n;
+    c.d = d;
+    c.k_out = k;
+    c.min_samples = ms;
+    c.out_idx = out_idx;
+    c.out_core = out_core;
+    c.Bt = w.bt;
+    c.dp = dp;
+    EKH_HIP(launch_knn_core(p.K, c, s));
+    return EKH_OK;
+}
+
 // ---- MST workspace ----------------------------------------------------------
 struct MstWs {
     float *nrm;
@@ -609,6 +785,12 @@ int ekh_knn(const float *X, int64_t ldx, int64_t n, const float *Y, int64_t ldy,
 
 size_t ekh_core_workspace_bytes(int64_t n, int32_t d, int32_t min_samples) {
     if (n < 1 || d < 1 || d > EKH_MAX_DIM || min_samples < 1 || min_samples + 1 > EKH_MAX_K) return 0;
+    const SymPlan sp = plan_sym(n, d, min_samples + 1);
+    if (sp.on) {
+        Carver c(nullptr);
+        SymWs w;
+        return sym_ws(sp, n, d, min_samples + 1, c, w);
+    }
     const KnnPlan p = plan_knn(n, n, d, min_samples + 1, 0);
     Carver c(nullptr);
     float *nx, *ny, *bt;
@@ -630,6 +812,14 @@ int ekh_core_distances(const float *X, int64_t ldx, int64_t n, int32_t d, int32_
     const size_t need = ekh_core_workspace_bytes(n, d, min_samples);
     if (ws_bytes < need) return fail(EKH_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
     const int K = min_samples + 1;
+    const SymPlan sp = plan_sym(n, d, K);
+    if (sp.on) {
+        Carver c(ws);
+        SymWs w;
+        sym_ws(sp, n, d, K, c, w);
+        return run_core_sym(sp, X, ldx, n, d, min_samples, out_nbr_idx ? out_nbr_idx : w.idx, out_nbr_d2, out_core, w,
+                            (hipStream_t)stream);
+    }
     const KnnPlan p = plan_knn(n, n, d, K, 0);
     Carver c(ws);
     float *nx, *ny, *bt;
@@ -879,7 +1069,7 @@ int ekh_timer_enable(int on) {
 }
 
 int ekh_timer_read(int kernel_id, int64_t *launches, double *total_ms, double *algo_flop) {
-    if (kernel_id < 0 || kernel_id > 1) return fail(EKH_EINVAL, "unknown kernel id %d", kernel_id);
+    if (kernel_id < 0 || kernel_id > 2) return fail(EKH_EINVAL, "unknown kernel id %d", kernel_id);
     std::lock_guard<std::mutex> lk(g_tmu);
     int64_t cnt = 0;
     double ms = 0.0, fl = 0.0;

@@ -95,6 +95,7 @@ enum KnnOut : int {
     kOutKnn = 1,     // final: out_idx / out_dist, first k entries
     kOutCore = 2,    // final: nbr lists (K = ms + 1) and core = sqrt(d2[ms-1]) (GEMM form; replaced by the
                      // direct-difference value of knn_core_kernel where the caller asks for core distances)
+    kOutBound = 4,   // final: out_core[q] = D2 of entry k_out - 1 (the bound pass of the symmetric self-kNN)
 };
 
 struct KnnArgs {
@@ -119,7 +120,27 @@ struct KnnArgs {
     float *out_core;  // [n]
     const float *Bt;  // database point-major [m, dp] (segment layout of tile_dim; the tiles and the direct differences read it)
     int dp;           // row stride of Bt: tile_dim(d)
+    // query tiles to run (NULL: all): tile t = rows [t * gate_rows, (t + 1) * gate_rows) of the whole query set
+    // runs when gate[t] != 0 (the merge kernel likewise skips the rows of the other tiles)
+    const uint32_t *gate;
+    int gate_rows;
+    // symmetric self-kNN (knn_sym_kernel, sym_merge_kernel); Q and the database are the same n points
+    const float *tau;     // per point: D2 of its k_out-th neighbour among a subset, a bound on the final one
+    const float *theta;   // per point: tau widened for the column side's fast test
+    Entry *colbuf;        // per point: colcap column-side candidates (D2, query index)
+    uint32_t *colcnt;     // per point: candidates offered (may exceed colcap: then the list is recomputed)
+    int colcap;
+    uint32_t *gate_w;     // per query tile (gate_rows rows): set by sym_merge_kernel when a row's buffer overflowed
 };
+
+// Symmetric self-kNN (ekh_core_distances from kSymMinPoints points on): the
+// bound pass runs the kNN against every kSymSubset-th point; the column
+// buffers hold kSymColCap candidates per point.
+constexpr int64_t kSymMinPoints = 16384;
+constexpr int kSymSubset = 16;
+constexpr int kSymColCap = 512;
+// most database splits per query tile in the symmetric pass
+constexpr int kSymMaxSplits = 16;
 
 // host launchers (return hipError_t of the launch)
 // Norms of X (into nx), of Y when ny is set, and Y's point-major copy when Bt is
@@ -130,6 +151,16 @@ hipError_t launch_knn_tile(int K, int QM, const KnnArgs &a, hipStream_t s);
 hipError_t launch_knn_merge(int K, const KnnArgs &a, hipStream_t s);
 hipError_t launch_knn_rescore(int K, const KnnArgs &a, hipStream_t s);
 hipError_t launch_knn_core(int K, const KnnArgs &a, hipStream_t s);
+// symmetric pass: grid = query tiles x a.splits, query tile t over database
+// tiles [t * QT / TR, a.tiles) in a.splits pieces
+hipError_t launch_knn_sym(int K, int QM, const KnnArgs &a, hipStream_t s);
+hipError_t launch_sym_merge(int K, const KnnArgs &a, hipStream_t s);
+// rows 0, step, 2 step, ... of the point-major copy bt [n, dp] and their norms into bs, ns
+hipError_t launch_subset_gather(const float *bt, const float *nx, int64_t n, int dp, int step, float *bs, float *ns,
+                                hipStream_t s);
+// theta = tau widened for the column side's fast test (from tau and the norms); zeroes colcnt [n] and gate [ntiles]
+hipError_t launch_sym_setup(const float *tau, const float *nx, int64_t n, float *theta, uint32_t *colcnt,
+                            uint32_t *gate, int64_t ntiles, hipStream_t s);
 
 // ---- Boruvka ---------------------------------------------------------------
 constexpr uint64_t kNoEdge = ~0ull;

@@ -34,6 +34,33 @@ template <> hipError_t launch_knn_tile_k<EKH_KNN_K>(int QM, const KnnArgs &a, hi
     }
 }
 
+template <> hipError_t launch_knn_sym_k<EKH_KNN_K>(int QM, const KnnArgs &a, hipStream_t s) {
+    // the symmetric pass runs at d <= 64 only (the planner's choice); one
+    // instantiation per list length
+    const int64_t QT = knn_query_tile(EKH_KNN_K, QM);
+    const int64_t groups = (a.nq + QT - 1) / QT * a.splits;
+    if (a.splits < 1 || groups > 0x7fffffff || a.dp != tile_dim(a.d) || pick_qm(a.d) != QM || a.m != a.nq ||
+        a.colcap < 1 || !a.tau || !a.theta || !a.colbuf || !a.colcnt || !a.part)
+        return hipErrorInvalidValue;
+    switch (QM) {
+#define EKH_KNN_SYM_CASE(q)                                                                                            \
+    case q: hipLaunchKernelGGL((knn_sym_kernel<EKH_KNN_K, q>), dim3((unsigned)groups), dim3(kThreads), 0, s, a); break;
+        EKH_KNN_SYM_CASE(2) EKH_KNN_SYM_CASE(4) EKH_KNN_SYM_CASE(6) EKH_KNN_SYM_CASE(8) EKH_KNN_SYM_CASE(10)
+        EKH_KNN_SYM_CASE(12) EKH_KNN_SYM_CASE(14) EKH_KNN_SYM_CASE(16)
+#undef EKH_KNN_SYM_CASE
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <> hipError_t launch_sym_merge_k<EKH_KNN_K>(const KnnArgs &a, hipStream_t s) {
+    if (a.nq <= 0 || !a.gate_w || a.gate_rows < 1) return hipErrorInvalidValue;
+    const int bs = 256;
+    const int64_t threads = a.nq * kMergeLanes;
+    hipLaunchKernelGGL(sym_merge_kernel<EKH_KNN_K>, dim3((unsigned)((threads + bs - 1) / bs)), dim3(bs), 0, s, a);
+    return hipGetLastError();
+}
+
 template <> hipError_t launch_knn_rescore_k<EKH_KNN_K>(const KnnArgs &a, hipStream_t s) {
     constexpr int rows = DirectRows<EKH_KNN_K>::kRowsPerBlock;
     if (a.dp > kDirectMaxDim || a.k_out > EKH_KNN_K) return hipErrorInvalidValue;

@@ -522,6 +522,12 @@ template <int K, int CB, int RB> struct EpiKnn {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) any = any || hit[cb];
         if (!__builtin_amdgcn_ballot_w64(any)) return;
+        stash(acc);
+        insert(nb4, hit, acc, nrm, j0);
+        __builtin_amdgcn_wave_barrier(); // the loads above before the next tile's stores
+    }
+    // the wave's dot products to LDS ([value][thread])
+    __device__ __forceinline__ void stash(const f4 (&acc)[RB][CB]) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -529,6 +535,10 @@ template <int K, int CB, int RB> struct EpiKnn {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sv[((cb * RB + rb) * 4 + r) * kThreads + tid] = acc[rb][cb][r];
         __builtin_amdgcn_wave_barrier(); // the LDS stores above before the loads below
+    }
+    // the insertions, after stash()
+    __device__ __forceinline__ void insert(const f4 (&nb4)[RB], const bool (&hit)[CB], const f4 (&acc)[RB][CB],
+                                           const float *nrm, int64_t j0) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             if (!__builtin_amdgcn_ballot_w64(hit[cb])) continue;
@@ -554,7 +564,6 @@ template <int K, int CB, int RB> struct EpiKnn {
             }
             store(cb, L);
         }
-        __builtin_amdgcn_wave_barrier(); // the loads above before the next tile's stores
     }
     __device__ __forceinline__ void tile(const f4 (&acc)[RB][CB], const float *nrm, const int32_t *, const float *,
                                          int64_t j0) {
@@ -575,6 +584,12 @@ __device__ __forceinline__ void write_list(const KnnArgs &a, const TopK<K> &L, i
     if (dst) {
 #pragma unroll
         for (int t = 0; t < K; ++t) dst[t] = Entry{L.d[t], L.i[t]};
+    } else if (a.out_mode == kOutBound) {
+        float c = 0.f;
+#pragma unroll
+        for (int t = 0; t < K; ++t)
+            if (t == a.k_out - 1) c = L.d[t]; // a select per entry (no dynamic register index)
+        a.out_core[q] = c;
     } else if (a.out_mode == kOutKnn) {
 #pragma unroll
         for (int t = 0; t < K; ++t) {
@@ -614,6 +629,7 @@ void knn_tile_kernel(KnnArgs a) {
     const int split = body ? 0 : (int)(h / tail_q);
     const int nsplit = body ? 1 : a.splits;
     const int64_t qbase = body ? (int64_t)blockIdx.x * QT : tail0 + (h % tail_q) * QT; // local row of the first query
+    if (a.gate && a.gate[(a.q0 + qbase) / a.gate_rows] == 0u) return; // a tile that need not run
 
     float bq[CB][QM];
     bool qv[CB];
@@ -668,13 +684,15 @@ template <int K> __global__ __launch_bounds__(256) void knn_merge_kernel(KnnArgs
     const int r = (int)(gid % kMergeLanes);
     TopK<K> L;
     L.clear();
+    // rows of query tiles that did not run (a.gate) are skipped like rows past the end
+    const bool row = ql < a.nq && (!a.gate || a.gate[(a.q0 + ql) / a.gate_rows] != 0u);
     // the lanes of a wave run the same number of trips (a.splits is uniform and
     // r < kMergeLanes): lanes past their last split push empty lists
     for (int s0 = 0; s0 < a.splits; s0 += kMergeLanes) {
         const int s = s0 + r;
         float od[K];
         int32_t oi[K];
-        const bool have = ql < a.nq && s < a.splits;
+        const bool have = row && s < a.splits;
         const Entry *src = a.part + ((int64_t)(have ? s : 0) * a.nq + (have ? ql : 0)) * K;
 #pragma unroll
         for (int t = 0; t < K; ++t) {
@@ -687,7 +705,290 @@ template <int K> __global__ __launch_bounds__(256) void knn_merge_kernel(KnnArgs
     // every lane of the wave takes part in the shuffles (rows past the end hold empty lists)
 #pragma unroll
     for (int mask = 1; mask < kMergeLanes; mask <<= 1) L.merge_xor(mask);
-    if (ql < a.nq && r == 0) write_list<K>(a, L, a.q0 + ql, 0);
+    if (row && r == 0) write_list<K>(a, L, a.q0 + ql, 0);
+}
+
+// ---------------------------------------------------------------- symmetric self-kNN
+// D2 is bitwise symmetric (the same chain of products in the same k-order for
+// (i, j) and (j, i)), so the self-kNN computes every pair once: query tile t
+// (QT points, rows [t QT, (t + 1) QT)) runs over the database rows from its own
+// first row on, the upper block triangle.  A pair (i, j) it computes feeds
+// i's list (the row side, as in knn_tile_kernel) and, when j lies past the
+// query tile's own block, j's list through a candidate buffer (the column
+// side).  Every pair of points is then seen by both of its lists: within a
+// block by the row side, across blocks by the row side of the earlier block
+// and the column side of the later one.
+//
+// Both sides admit a candidate only within a bound on its point's final
+// k-th D2: tau, the k-th D2 among a subset of the points (a bound, since those
+// are real candidates).  The row side starts with tau instead of an empty
+// list's infinite bound (no warm-up); the column side appends (D2, i) to j's
+// buffer when D2 <= tau_j, so no candidate of the final list is missed.
+// sym_merge_kernel merges the row side's lists with the buffer; a buffer
+// that overflowed marks its query tile, whose lists the ordinary kernel then
+// recomputes (a.gate).
+//
+// Column side's fast test per element, with t = fma(-2, s, n_j) from the row
+// side: u = t - theta_j against -n_i, theta_j = tau_j + 2^-19 (n_j + tau_j).
+// For D2 = fma(-2, s, n_i + n_j) <= tau_j the point i lies within sqrt(tau_j)
+// of j, so n_i <= 2 n_j + 2 tau_j, and D2 and t + n_i differ by at most a few
+// units of 2^-24 (n_i + n_j + tau_j) < 2^-21 (n_j + tau_j); theta_j's widening
+// covers that and theta_j's own rounding, and the rounding of t - theta_j
+// keeps the order.  The exact D2 decides (the same value the row side uses).
+template <int K, int CB, int RB> struct EpiSym : EpiKnn<K, CB, RB> {
+    using Base = EpiKnn<K, CB, RB>;
+    float cap[CB];      // the query's bound tau (-inf for a column past the points)
+    bool qv[CB];        // the query column holds a point
+    int64_t col_from;   // database rows >= col_from take the column side (past the query tile's block)
+    Entry *colbuf;
+    uint32_t *colcnt;
+    int colcap;
+    // column candidates wait in a per-wave LDS queue (kSymQueue entries: row, D2,
+    // query) and go to the buffers 64 at a time, the returning atomics of a
+    // flush in flight together instead of one round trip per candidate on the
+    // way to the tile's barrier
+    static constexpr int kSymQueue = 128;
+    int32_t *qj;
+    float *qd;
+    int32_t *qq;
+    uint32_t qn; // entries queued (wave-uniform)
+    __device__ __forceinline__ void flush() {
+        const int lane = this->tid & 63;
+        __builtin_amdgcn_wave_barrier(); // the queue's writes (by any lane) before the reads below
+        for (uint32_t b = 0; b < qn; b += 64) {
+            const uint32_t e = b + (uint32_t)lane;
+            if (e < qn) {
+                const int32_t j = qj[e];
+                const uint32_t pos = atomicAdd(&colcnt[j], 1u);
+                if (pos < (uint32_t)colcap) colbuf[(int64_t)j * colcap + pos] = Entry{qd[e], qq[e]};
+            }
+        }
+        qn = 0;
+        __builtin_amdgcn_wave_barrier(); // the reads above before the queue's next writes
+    }
+
+    // Base::prepare with the bound capped by tau
+    __device__ __forceinline__ void prepare() {
+        constexpr float kWiden = 1.0f / 1048576.0f;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            if (this->dirty[cb]) {
+                const TopK<K> &L = this->lst[cb];
+                const float gq = Base::kSecond ? __uint_as_float(group_second_u32(
+                                                     __float_as_uint(L.d[Base::J]), __float_as_uint(L.d[Base::J - 1])))
+                                               : group_max_nonneg(L.d[Base::J]);
+                const float adm = fminf(fminf(group_min_nonneg(L.d[K - 1]), gq), cap[cb]);
+                this->admq[cb] = fmaf(adm, 1.0f + kWiden, -this->nq[cb] * (1.0f - kWiden));
+                this->dirty[cb] = false;
+            }
+        }
+    }
+    // comp: the rows' tau (bits), core: their theta (tile payload)
+    __device__ __forceinline__ void tile(const f4 (&acc)[RB][CB], const float *nrm, const int32_t *tau_bits,
+                                         const float *theta, int64_t j0) {
+        const int g = this->g;
+        f4 nb4[RB], th4[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            nb4[rb] = *reinterpret_cast<const f4 *>(nrm + rb * 16 + 4 * g);
+            th4[rb] = *reinterpret_cast<const f4 *>(theta + rb * 16 + 4 * g);
+        }
+        prepare();
+        // wave-uniform: a row of this tile lies past the query tile's block
+        const bool colside = j0 + RB * 16 > col_from;
+        bool hit[CB], hitc[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            float mn = INFINITY, mc = INFINITY;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float t = fmaf(-2.f, acc[rb][cb][r], nb4[rb][r]);
+                    mn = fminf(mn, t);
+                    mc = fminf(mc, t - th4[rb][r]);
+                }
+            hit[cb] = mn <= this->admq[cb];
+            hitc[cb] = colside && mc <= -this->nq[cb];
+        }
+        bool anyr = false, anyc = false;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            anyr = anyr || hit[cb];
+            anyc = anyc || hitc[cb];
+        }
+        const bool wr = __builtin_amdgcn_ballot_w64(anyr) != 0, wc = __builtin_amdgcn_ballot_w64(anyc) != 0;
+        if (!wr && !wc) return;
+        this->stash(acc);
+        if (wc) column(acc, nb4, th4, hitc, tau_bits, nrm, j0);
+        if (wr) this->insert(nb4, hit, acc, nrm, j0);
+        __builtin_amdgcn_wave_barrier(); // the loads above before the next tile's stores
+    }
+    // Column side's candidates, after stash(): a loop over the set bits of a
+    // per-lane mask as in the row side, each appending the exact D2 to the
+    // database row's buffer when it is within the row's tau.
+    __device__ __forceinline__ void column(const f4 (&acc)[RB][CB], const f4 (&nb4)[RB], const f4 (&th4)[RB],
+                                           const bool (&hitc)[CB], const int32_t *tau_bits, const float *nrm,
+                                           int64_t j0) {
+        const int g = this->g, tid = this->tid;
+        // buffer accesses from the tile's first row (a scalar base, j0 < 2^31): the
+        // lane offsets stay 32-bit (row < 64, pos < colcap)
+        const int lane = tid & 63;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            if (!__builtin_amdgcn_ballot_w64(hitc[cb])) continue;
+            uint32_t mk = 0u;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    mk |= fmaf(-2.f, acc[rb][cb][r], nb4[rb][r]) - th4[rb][r] <= -this->nq[cb] ? (1u << (4 * rb + r))
+                                                                                                 : 0u;
+            if (!qv[cb]) mk = 0u;
+            for (int trip = 0; trip < RB * 4; ++trip) {
+                if (!__builtin_amdgcn_ballot_w64(mk != 0u)) break;
+                bool take = false;
+                float d2 = 0.f;
+                int32_t j = 0;
+                if (mk != 0u) {
+                    const int e = __builtin_ctz(mk);
+                    mk &= mk - 1u;
+                    const int row = (e >> 2) * 16 + 4 * g + (e & 3);
+                    j = (int32_t)(j0 + row);
+                    d2 = fmaf(-2.f, this->sv[((cb * RB + (e >> 2)) * 4 + (e & 3)) * kThreads + tid],
+                              this->nq[cb] + nrm[row]);
+                    d2 = d2 > 0.f ? d2 : 0.f;
+                    // rows outside the tile carry NaN bits here, which no D2 satisfies
+                    take = j0 + row >= col_from && d2 <= __int_as_float(tau_bits[row]);
+                }
+                const uint64_t m = __builtin_amdgcn_ballot_w64(take);
+                if (m) {
+                    if (qn + 64 > (uint32_t)kSymQueue) flush();
+                    if (take) {
+                        const uint32_t at = qn + (uint32_t)__builtin_popcountll(m & ((1ull << lane) - 1ull));
+                        qj[at] = j;
+                        qd[at] = d2;
+                        qq[at] = this->qrow[cb];
+                    }
+                    qn += (uint32_t)__builtin_popcountll(m);
+                }
+            }
+        }
+    }
+};
+
+template <int K, int QM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(knn_waves_per_simd(K, QM), knn_waves_per_simd(K, QM))))
+void knn_sym_kernel(KnnArgs a) {
+    constexpr int CB = knn_col_blocks(K, QM);
+    using T = Tile<QM>;
+    constexpr int QT = kWaves * 16 * CB;
+    static_assert(QT % T::TR == 0, "a query tile covers whole database tiles");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, li = lane & 15;
+    // item = query tile x split (query tiles in order, the longest ranges first)
+    const int64_t qt = (int64_t)blockIdx.x / a.splits;
+    const int split = (int)((int64_t)blockIdx.x % a.splits);
+    const int64_t qbase = qt * QT;
+
+    float bq[CB][QM];
+    EpiSym<K, CB, T::RB> epi;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const int64_t q = qbase + wave * 16 * CB + cb * 16 + li;
+        epi.qv[cb] = q < a.nq;
+        const int64_t qs = epi.qv[cb] ? q : 0;
+        load_query<QM>(a.Q, a.ldq, qs, epi.qv[cb], a.d, g, bq[cb]);
+        epi.nq[cb] = epi.qv[cb] ? a.nrm_q[qs] : 0.f;
+        epi.qrow[cb] = (int32_t)q;
+        epi.cap[cb] = epi.qv[cb] ? a.tau[qs] : -INFINITY;
+    }
+    // the first database tile of the query tile's own block, and this split's share of the rest
+    const int64_t f = qt * (QT / T::TR);
+    const int64_t len = a.tiles - f;
+    const int64_t tb = f + len * split / a.splits, te = f + len * (split + 1) / a.splits;
+
+    __shared__ float sv[EpiSym<K, CB, T::RB>::NV * kThreads];
+    constexpr int QL = EpiSym<K, CB, T::RB>::kSymQueue;
+    __shared__ int32_t sq_j[kWaves * QL], sq_q[kWaves * QL];
+    __shared__ float sq_d[kWaves * QL];
+    epi.init();
+    epi.qj = sq_j + wave * QL;
+    epi.qd = sq_d + wave * QL;
+    epi.qq = sq_q + wave * QL;
+    epi.qn = 0;
+    epi.g = g;
+    epi.sv = sv;
+    epi.tid = tid;
+    epi.col_from = qbase + QT;
+    epi.colbuf = a.colbuf;
+    epi.colcnt = a.colcnt;
+    epi.colcap = a.colcap;
+    // the row side's bound starts at tau (prepare() re-forms it once a list changes)
+    constexpr float kWiden = 1.0f / 1048576.0f;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) epi.admq[cb] = fmaf(epi.cap[cb], 1.0f + kWiden, -epi.nq[cb] * (1.0f - kWiden));
+    run_tiles<QM, CB, true, 1>(a.Bt, (int32_t)a.m, a.nrm_b, reinterpret_cast<const int32_t *>(a.tau), a.theta,
+                               (int32_t)tb, (int32_t)te, bq, epi);
+    if (epi.qn) epi.flush();
+
+    // the row side's list of each query: this split's partial list
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        TopK<K> L;
+        epi.load(cb, L);
+        L.merge_xor(16);
+        L.merge_xor(32);
+        if (g == 0 && epi.qv[cb]) {
+            Entry *dst = a.part + ((int64_t)split * a.nq + epi.qrow[cb]) * K;
+#pragma unroll
+            for (int t = 0; t < K; ++t) dst[t] = Entry{L.d[t], L.i[t]};
+        }
+    }
+}
+
+// Final lists of the symmetric pass: per row the a.splits partial lists of
+// the row side and the column side's candidates (in any order, so each goes
+// through the full (D2, index) comparison), kMergeLanes lanes per row as in
+// knn_merge_kernel.  A row whose buffer overflowed marks its query tile in
+// a.gate_w; its list is then recomputed.
+template <int K> __global__ __launch_bounds__(256) void sym_merge_kernel(KnnArgs a) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t ql = gid / kMergeLanes;
+    const int r = (int)(gid % kMergeLanes);
+    const bool row = ql < a.nq;
+    TopK<K> L;
+    L.clear();
+    for (int s0 = 0; s0 < a.splits; s0 += kMergeLanes) {
+        const int s = s0 + r;
+        float od[K];
+        int32_t oi[K];
+        const bool have = row && s < a.splits;
+        const Entry *src = a.part + ((int64_t)(have ? s : 0) * a.nq + (have ? ql : 0)) * K;
+#pragma unroll
+        for (int t = 0; t < K; ++t) {
+            const Entry e = have ? src[t] : Entry{INFINITY, 0x7fffffff};
+            od[t] = e.d2;
+            oi[t] = e.idx;
+        }
+        L.push_sorted(od, oi);
+    }
+    const uint32_t cnt = row ? a.colcnt[ql] : 0u;
+    const uint32_t use = cnt < (uint32_t)a.colcap ? cnt : (uint32_t)a.colcap;
+    const Entry *cand = a.colbuf + (row ? ql : 0) * a.colcap;
+    for (uint32_t e0 = 0; e0 < (uint32_t)a.colcap; e0 += kMergeLanes) {
+        const bool h = e0 + (uint32_t)r < use;
+        if (!__builtin_amdgcn_ballot_w64(h)) break;
+        if (h) {
+            const Entry e = cand[e0 + r];
+            L.push_any(e.d2, e.idx);
+        }
+    }
+#pragma unroll
+    for (int mask = 1; mask < kMergeLanes; mask <<= 1) L.merge_xor(mask);
+    if (row && r == 0) {
+        write_list<K>(a, L, ql, 0);
+        if (cnt > (uint32_t)a.colcap) atomicOr(&a.gate_w[ql / a.gate_rows], 1u);
+    }
 }
 
 // Direct-difference D2 of the selected neighbours, for the reported kNN
@@ -850,5 +1151,7 @@ template <int K> hipError_t launch_knn_tile_k(int QM, const KnnArgs &a, hipStrea
 template <int K> hipError_t launch_knn_rescore_k(const KnnArgs &a, hipStream_t s);
 template <int K> hipError_t launch_knn_core_k(const KnnArgs &a, hipStream_t s);
 template <int K> hipError_t launch_knn_merge_k(const KnnArgs &a, hipStream_t s);
+template <int K> hipError_t launch_knn_sym_k(int QM, const KnnArgs &a, hipStream_t s);
+template <int K> hipError_t launch_sym_merge_k(const KnnArgs &a, hipStream_t s);
 
 } // namespace ekh

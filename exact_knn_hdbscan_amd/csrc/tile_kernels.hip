@@ -124,6 +124,80 @@ hipError_t launch_knn_tile(int K, int QM, const KnnArgs &a, hipStream_t s) {
     }
 }
 
+hipError_t launch_knn_sym(int K, int QM, const KnnArgs &a, hipStream_t s) {
+    switch (K) {
+    case 2: return launch_knn_sym_k<2>(QM, a, s);
+    case 4: return launch_knn_sym_k<4>(QM, a, s);
+    case 8: return launch_knn_sym_k<8>(QM, a, s);
+    case 10: return launch_knn_sym_k<10>(QM, a, s);
+    case 11: return launch_knn_sym_k<11>(QM, a, s);
+    case 16: return launch_knn_sym_k<16>(QM, a, s);
+    case 32: return launch_knn_sym_k<32>(QM, a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_sym_merge(int K, const KnnArgs &a, hipStream_t s) {
+    switch (K) {
+    case 2: return launch_sym_merge_k<2>(a, s);
+    case 4: return launch_sym_merge_k<4>(a, s);
+    case 8: return launch_sym_merge_k<8>(a, s);
+    case 10: return launch_sym_merge_k<10>(a, s);
+    case 11: return launch_sym_merge_k<11>(a, s);
+    case 16: return launch_sym_merge_k<16>(a, s);
+    case 32: return launch_sym_merge_k<32>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// One thread per 16-byte piece of a gathered row.
+__global__ __launch_bounds__(256) void subset_gather_kernel(const float *__restrict__ bt, const float *__restrict__ nx,
+                                                            int64_t ns, int dp, int step, float *__restrict__ bs,
+                                                            float *__restrict__ nrm_s) {
+    const int pieces = dp / 4;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= ns * pieces) return;
+    const int64_t r = gid / pieces;
+    const int c = (int)(gid % pieces);
+    const int64_t src = r * step;
+    reinterpret_cast<f4 *>(bs + r * dp)[c] = reinterpret_cast<const f4 *>(bt + src * dp)[c];
+    if (c == 0) nrm_s[r] = nx[src];
+}
+
+hipError_t launch_subset_gather(const float *bt, const float *nx, int64_t n, int dp, int step, float *bs, float *ns,
+                                hipStream_t s) {
+    if (step < 1 || dp % 4) return hipErrorInvalidValue;
+    const int64_t rows = (n + step - 1) / step;
+    const int64_t threads = rows * (dp / 4);
+    if ((threads + 255) / 256 > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(subset_gather_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, bt, nx, rows,
+                       dp, step, bs, ns);
+    return hipGetLastError();
+}
+
+// theta = tau + 2^-19 (n + tau) (see the symmetric pass's column side), and
+// the zeroed counters of one call
+__global__ __launch_bounds__(256) void sym_setup_kernel(const float *__restrict__ tau, const float *__restrict__ nx,
+                                                        int64_t n, float *__restrict__ theta,
+                                                        uint32_t *__restrict__ colcnt, uint32_t *__restrict__ gate,
+                                                        int64_t ntiles) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        const float t = tau[i];
+        theta[i] = fmaf(nx[i] + t, 1.0f / 524288.0f, t);
+        colcnt[i] = 0u;
+    }
+    if (i < ntiles) gate[i] = 0u;
+}
+
+hipError_t launch_sym_setup(const float *tau, const float *nx, int64_t n, float *theta, uint32_t *colcnt,
+                            uint32_t *gate, int64_t ntiles, hipStream_t s) {
+    const int64_t m = n > ntiles ? n : ntiles;
+    hipLaunchKernelGGL(sym_setup_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, tau, nx, n, theta, colcnt,
+                       gate, ntiles);
+    return hipGetLastError();
+}
+
 hipError_t launch_knn_rescore(int K, const KnnArgs &a, hipStream_t s) {
     if (a.nq <= 0) return hipSuccess;
     switch (K) {

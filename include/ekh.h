@@ -175,6 +175,19 @@ size_t ekh_core_workspace_bytes(int64_t n, int32_t d, int32_t min_samples);
  *  ws: at least ekh_core_workspace_bytes() (norms, split lists, a point-major
  *      copy of X [n, 16 ceil(d / 16)] that the tiles stream and the direct
  *      differences gather from, and the list indices).
+ *
+ * From 16,384 points on at d <= 64 the self-kNN computes every pair once
+ * (D2 is bitwise symmetric): a bound pass finds each point's (min_samples + 1)-th
+ * nearest among every 16th point, a bound on its final one; the symmetric
+ * pass runs each query block over its own and the later blocks' points, a
+ * pair feeding the query's list and, within the later point's bound, that
+ * point's candidate buffer (512 entries per point in the workspace, 4 KB);
+ * the lists are then merged, and a query block with an overflowed buffer is
+ * recomputed from both sides.  The lists are the same bit for bit as with
+ * every pair computed from both sides, which the environment variable
+ * EKH_CORE_DENSE (set and not "0") selects instead; the workspace query and
+ * the call must see the same setting.  (A reading: the pages compute every
+ * pair of the core-distance kernel; symmetry changes no result.)
  */
 int ekh_core_distances(const float *X, int64_t ldx, int64_t n, int32_t d, int32_t min_samples, float *out_core,
                        int32_t *out_nbr_idx, float *out_nbr_d2, void *ws, size_t ws_bytes, void *stream);
@@ -416,7 +429,9 @@ int ekh_hdbscan_tail(const int32_t *lo, const int32_t *hi, const float *w, int64
 /*
  * Optional per-kernel timing with HIP events recorded on the launch stream
  * around every launch of the two dense kernels, for roofline figures.
- * kernel id: 0 = the kNN tile kernel, 1 = the Boruvka scan tile kernel.
+ * kernel id: 0 = the kNN tile kernel (with the bound pass of ekh_core_distances'
+ * symmetric self-kNN), 1 = the Boruvka scan tile kernel, 2 = the symmetric
+ * self-kNN kernel (its flop: 2 d per pair it computes, each once).
  * ekh_timer_enable(1) clears and starts recording; ekh_timer_read() waits for
  * the recorded events and returns the launch count, summed milliseconds and
  * summed algorithmic flop (2 d per distance pair actually evaluated, padding
