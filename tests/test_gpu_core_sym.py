@@ -15,8 +15,8 @@ from gpu_util import dev, host, say
 pytestmark = pytest.mark.gpu
 
 
-def run_both(X, ms):
-    Xg = dev(X)
+def run_both(X, ms, ld=None):
+    Xg = dev(X, ld=ld)
     os.environ["EKH_CORE_DENSE"] = "1"
     try:
         c0, i0, d0 = ekh.core_distances(Xg, ms, return_neighbours=True)
@@ -47,6 +47,17 @@ def test_core_symmetric_equals_dense(n, d, ms, seed):
     X = datagen.gaussian_mixture(n, d, 30, seed=seed)
     say("core symmetric vs dense n=%d d=%d ms=%d" % (n, d, ms))
     assert_same(*run_both(X, ms))
+
+
+@pytest.mark.parametrize("n,d,ms,ld", [
+    (16385, 1, 10, None),      # d = 1; the last query tile holds one point, the last database tile one row
+    (18000, 61, 10, 18013),    # leading dimension past n
+    (16512, 64, 16, None),     # exactly 129 query tiles, list length 32 (k = 17)
+])
+def test_core_symmetric_edge_shapes(n, d, ms, ld):
+    X = datagen.gaussian_mixture(n, d, 25, seed=n % 31)
+    say("core symmetric vs dense n=%d d=%d ms=%d ld=%s" % (n, d, ms, ld))
+    assert_same(*run_both(X, ms, ld))
 
 
 def test_core_symmetric_clips_100000():
