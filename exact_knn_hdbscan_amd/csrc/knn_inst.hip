@@ -19,6 +19,12 @@ template <int K, int QM> hipError_t knn_tile_launch(const KnnArgs &a, hipStream_
     if (a.body_q < 0 || tail_q < 0 || a.splits < 1 || groups > 0x7fffffff || a.dp != tile_dim(a.d) ||
         pick_qm(a.d) != QM)
         return hipErrorInvalidValue;
+    // the bound pass (d <= 64) keeps values only
+    if constexpr (QM <= 16)
+        if (a.out_mode == kOutBound) {
+            hipLaunchKernelGGL((knn_tile_kernel<K, QM, true>), dim3((unsigned)groups), dim3(kThreads), 0, s, a);
+            return hipGetLastError();
+        }
     hipLaunchKernelGGL((knn_tile_kernel<K, QM>), dim3((unsigned)groups), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }

@@ -377,6 +377,42 @@ template <int K> struct TopK {
     }
 };
 
+// The K smallest values only (no indices): the bound pass of the symmetric
+// self-kNN needs the K-th smallest D2 of each row, a value, which any choice
+// among equal values leaves the same.  Insertion: slot t takes med3(old t - 1,
+// v, old t), slot 0 min(v, old 0); no comparison, no index to carry.
+template <int K> struct TopV {
+    float d[K];
+
+    __device__ __forceinline__ void clear() {
+#pragma unroll
+        for (int t = 0; t < K; ++t) d[t] = INFINITY;
+    }
+    __device__ __forceinline__ void push(float v) {
+        float nd[K];
+        nd[0] = fminf(v, d[0]);
+#pragma unroll
+        for (int t = 1; t < K; ++t) nd[t] = __builtin_amdgcn_fmed3f(d[t - 1], v, d[t]);
+#pragma unroll
+        for (int t = 0; t < K; ++t) d[t] = nd[t];
+    }
+    __device__ __forceinline__ void push_ascending(float v, int32_t) { push(v); }
+    // pushes an ascending list; stops once no lane of the wave has a value below its last
+    __device__ __forceinline__ void push_sorted(const float (&od)[K]) {
+#pragma unroll
+        for (int t = 0; t < K; ++t) {
+            if (!__builtin_amdgcn_ballot_w64(od[t] < d[K - 1])) break;
+            push(od[t]);
+        }
+    }
+    __device__ __forceinline__ void merge_xor(int mask) {
+        float od[K];
+#pragma unroll
+        for (int t = 0; t < K; ++t) od[t] = __shfl_xor(d[t], mask);
+        push_sorted(od);
+    }
+};
+
 // ---------------------------------------------------------------- lane groups
 // Min / max over the four lanes (lane ^ 16, lane ^ 32) that share a query
 // column, with the gfx950 lane-swap instructions: permlane16_swap(v, v) yields
@@ -433,10 +469,10 @@ __device__ __forceinline__ float group_max_nonneg(float v) { return __uint_as_fl
 // reach the final list and is not admitted (on equality it is, since a lower
 // index can still win the tie).  Without this, each lane would keep filling its
 // own list with candidates that the final merge drops.
-template <int K, int CB, int RB> struct EpiKnn {
+template <int K, int CB, int RB, class List = TopK<K>> struct EpiKnn {
     static constexpr int J = (K + 3) / 4 - 1;
     static constexpr bool kSecond = 4 * (J + 1) == K + 1 && J >= 1;
-    TopK<K> lst[CB]; // this lane's lists, in registers
+    List lst[CB]; // this lane's lists, in registers
     float nq[CB];
     float admq[CB]; // admission bound on D2 shared by the column's four lanes, moved to nb - 2 s and widened
                     // by the rounding margin
@@ -452,8 +488,8 @@ template <int K, int CB, int RB> struct EpiKnn {
             dirty[cb] = false;
         }
     }
-    __device__ __forceinline__ void load(int cb, TopK<K> &L) { L = lst[cb]; }
-    __device__ __forceinline__ void store(int cb, const TopK<K> &L) { lst[cb] = L; }
+    __device__ __forceinline__ void load(int cb, List &L) { L = lst[cb]; }
+    __device__ __forceinline__ void store(int cb, const List &L) { lst[cb] = L; }
 
     // D2 = fma(-2, s, nq + nb).  The pair (i, i) needs no special case: the
     // norms come from the same MFMA chain as the dot products, so it is
@@ -477,7 +513,7 @@ template <int K, int CB, int RB> struct EpiKnn {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             if (dirty[cb]) {
-                const TopK<K> &L = lst[cb];
+                const List &L = lst[cb];
                 const float gq = kSecond ? __uint_as_float(group_second_u32(__float_as_uint(L.d[J]),
                                                                              __float_as_uint(L.d[J - 1])))
                                          : group_max_nonneg(L.d[J]);
@@ -549,7 +585,7 @@ template <int K, int CB, int RB> struct EpiKnn {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     mk |= fmaf(-2.f, acc[rb][cb][r], nb4[rb][r]) <= admq[cb] ? (1u << (4 * rb + r)) : 0u;
-            TopK<K> L;
+            List L;
             load(cb, L);
             for (int trip = 0; trip < RB * 4; ++trip) {
                 if (!__builtin_amdgcn_ballot_w64(mk != 0u)) break;
@@ -576,6 +612,22 @@ template <int K, int CB, int RB> struct EpiKnn {
         slow(acc, nb4, hit, nrm, j0);
     }
 };
+
+// A finished value list (the bound pass): its k_out-th value to out_core, or
+// to the split scratch (index 0 for every entry: the merge keeps the values).
+template <int K>
+__device__ __forceinline__ void write_list(const KnnArgs &a, const TopV<K> &L, int64_t q, Entry *dst) {
+    if (dst) {
+#pragma unroll
+        for (int t = 0; t < K; ++t) dst[t] = Entry{L.d[t], 0};
+    } else {
+        float c = 0.f;
+#pragma unroll
+        for (int t = 0; t < K; ++t)
+            if (t == a.k_out - 1) c = L.d[t]; // a select per entry (no dynamic register index)
+        a.out_core[q] = c;
+    }
+}
 
 // Writes a finished list for absolute row q: to the split scratch at dst when
 // it is one split's partial list, else in the final form a.out_mode names.
@@ -612,9 +664,11 @@ __device__ __forceinline__ void write_list(const KnnArgs &a, const TopK<K> &L, i
     }
 }
 
-template <int K, int QM>
+// VAL: value lists (the bound pass of the symmetric self-kNN, a.out_mode == kOutBound)
+template <int K, int QM, bool VAL = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(knn_waves_per_simd(K, QM), knn_waves_per_simd(K, QM))))
 void knn_tile_kernel(KnnArgs a) {
+    using List = typename std::conditional<VAL, TopV<K>, TopK<K>>::type;
     constexpr int CB = knn_col_blocks(K, QM);
     using T = Tile<QM>;
     constexpr int QT = kWaves * 16 * CB;
@@ -646,8 +700,8 @@ void knn_tile_kernel(KnnArgs a) {
     }
     const int64_t tb = a.tiles * split / nsplit, te = a.tiles * (split + 1) / nsplit;
 
-    __shared__ float sv[EpiKnn<K, CB, T::RB>::NV * kThreads];
-    EpiKnn<K, CB, T::RB> epi;
+    __shared__ float sv[EpiKnn<K, CB, T::RB, List>::NV * kThreads];
+    EpiKnn<K, CB, T::RB, List> epi;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         epi.nq[cb] = nq[cb];
@@ -662,7 +716,7 @@ void knn_tile_kernel(KnnArgs a) {
     // merge the four lane groups that share each query column
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-        TopK<K> L;
+        List L;
         epi.load(cb, L);
         L.merge_xor(16);
         L.merge_xor(32);
