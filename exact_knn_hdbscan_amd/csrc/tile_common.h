@@ -664,9 +664,12 @@ __device__ __forceinline__ void write_list(const KnnArgs &a, const TopK<K> &L, i
     }
 }
 
-// VAL: value lists (the bound pass of the symmetric self-kNN, a.out_mode == kOutBound)
+// VAL: value lists (the bound pass of the symmetric self-kNN, a.out_mode == kOutBound).  Without the
+// indices the kernel fits 128 VGPRs, so it runs four waves per SIMD with one barrier per tile (two LDS
+// tile buffers: four workgroups per CU)
 template <int K, int QM, bool VAL = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(knn_waves_per_simd(K, QM), knn_waves_per_simd(K, QM))))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(VAL ? 4 : knn_waves_per_simd(K, QM),
+                                                                           VAL ? 4 : knn_waves_per_simd(K, QM))))
 void knn_tile_kernel(KnnArgs a) {
     using List = typename std::conditional<VAL, TopV<K>, TopK<K>>::type;
     constexpr int CB = knn_col_blocks(K, QM);
@@ -711,7 +714,7 @@ void knn_tile_kernel(KnnArgs a) {
     epi.g = g;
     epi.sv = sv;
     epi.tid = tid;
-    run_tiles<QM, CB, false, knn_tiles_per_barrier(QM)>(a.Bt, (int32_t)a.m, a.nrm_b, nullptr, nullptr, (int32_t)tb, (int32_t)te, bq, epi);
+    run_tiles<QM, CB, false, VAL ? 1 : knn_tiles_per_barrier(QM)>(a.Bt, (int32_t)a.m, a.nrm_b, nullptr, nullptr, (int32_t)tb, (int32_t)te, bq, epi);
 
     // merge the four lane groups that share each query column
 #pragma unroll
