@@ -446,8 +446,9 @@ int run_knn(const KnnPlan &p, const float *X, int64_t ldx, int64_t n, const floa
 // ekh_knn).  The workspace query and the call must see the same setting.
 struct SymPlan {
     bool on = false;
-    int K = 0, QM = 0, TR = 0, QT = 0;
-    int64_t ns = 0, qtiles = 0, tiles = 0;
+    int K = 0, QM = 0, TR = 0;
+    int QT = 0, GT = 0; // query tile of the symmetric pass; of the dense kernel (the overflow gates' unit)
+    int64_t ns = 0, qtiles = 0, gtiles = 0, tiles = 0;
     int splits = 1;
     double pairs = 0; // pairs the symmetric pass computes
     KnnPlan pa{}, pf{};
@@ -461,9 +462,11 @@ SymPlan plan_sym(int64_t n, int d, int k) {
     p.on = n >= kSymMinPoints && p.QM <= 16 && p.K > 0 && !(env && env[0] && env[0] != '0');
     if (!p.on) return p;
     p.TR = tile_rows(p.QM);
-    p.QT = knn_query_tile(p.K, p.QM);
+    p.QT = sym_query_tile(p.K, p.QM);
+    p.GT = knn_query_tile(p.K, p.QM);
     p.ns = (n + kSymSubset - 1) / kSymSubset;
     p.qtiles = (n + p.QT - 1) / p.QT;
+    p.gtiles = (n + p.GT - 1) / p.GT;
     p.tiles = (n + p.TR - 1) / p.TR;
     // tiles of the triangle; pieces per query tile so that none is longer than
     // half of a resident workgroup's share (the longest run first)
@@ -474,7 +477,9 @@ SymPlan plan_sym(int64_t n, int d, int k) {
         const int64_t q = std::min<int64_t>(p.QT, n - t * p.QT);
         p.pairs += (double)q * (double)(n - t * p.QT);
     }
-    const int64_t slots = kCUs * knn_groups_per_cu(p.K, p.QM);
+    // workgroups resident per CU: one per wave per SIMD (the LDS, two tile
+    // buffers with the slow path's dot products and the column queue, fits four)
+    const int64_t slots = kCUs * sym_waves_per_simd(p.K, p.QM);
     while (p.splits < kSymMaxSplits && (p.tiles + p.splits - 1) / p.splits * 2 * slots > work) ++p.splits;
     p.pa = plan_knn(n, p.ns, d, k, 0, 1);
     p.pf = plan_knn(n, n, d, k, 0, 1);
@@ -501,7 +506,7 @@ size_t sym_ws(const SymPlan &p, int64_t n, int d, int k, Carver &c, SymWs &w) {
     w.part_b = c.take<Entry>((size_t)p.splits * n * p.K);
     w.colbuf = c.take<Entry>((size_t)n * kSymColCap);
     w.colcnt = c.take<uint32_t>(n);
-    w.gate = c.take<uint32_t>(p.qtiles);
+    w.gate = c.take<uint32_t>(p.gtiles);
     w.part_f = p.pf.part_entries ? c.take<Entry>((size_t)p.pf.part_entries) : nullptr;
     return c.used;
 }
@@ -554,7 +559,7 @@ int run_core_sym(const SymPlan &p, const float *X, int64_t ldx, int64_t n, int d
         b.out_core = w.tau;
         if ((rc = run_single_chunk(p.pa, b, 2.0 * d * (double)n * (double)p.ns, s)) != EKH_OK) return rc;
     }
-    EKH_HIP(launch_sym_setup(w.tau, w.nx, n, w.theta, w.colcnt, w.gate, p.qtiles, s));
+    EKH_HIP(launch_sym_setup(w.tau, w.nx, n, w.theta, w.colcnt, w.gate, p.gtiles, s));
     // symmetric pass over the upper block triangle
     a.Bt = w.bt;
     a.m = n;
@@ -579,7 +584,7 @@ int run_core_sym(const SymPlan &p, const float *X, int64_t ldx, int64_t n, int d
     a.out_dist = out_d2;
     a.out_core = out_core;
     a.gate_w = w.gate;
-    a.gate_rows = p.QT;
+    a.gate_rows = p.GT;
     EKH_HIP(launch_sym_merge(p.K, a, s));
     // the query tiles with an overflowed buffer, recomputed from both sides
     {

@@ -43,7 +43,7 @@ template <> hipError_t launch_knn_tile_k<EKH_KNN_K>(int QM, const KnnArgs &a, hi
 template <> hipError_t launch_knn_sym_k<EKH_KNN_K>(int QM, const KnnArgs &a, hipStream_t s) {
     // the symmetric pass runs at d <= 64 only (the planner's choice); one
     // instantiation per list length
-    const int64_t QT = knn_query_tile(EKH_KNN_K, QM);
+    const int64_t QT = sym_query_tile(EKH_KNN_K, QM);
     const int64_t groups = (a.nq + QT - 1) / QT * a.splits;
     if (a.splits < 1 || groups > 0x7fffffff || a.dp != tile_dim(a.d) || pick_qm(a.d) != QM || a.m != a.nq ||
         a.colcap < 1 || !a.tau || !a.theta || !a.colbuf || !a.colcnt || !a.part)

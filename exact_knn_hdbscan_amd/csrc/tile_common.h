@@ -935,9 +935,9 @@ template <int K, int CB, int RB> struct EpiSym : EpiKnn<K, CB, RB> {
 };
 
 template <int K, int QM>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(knn_waves_per_simd(K, QM), knn_waves_per_simd(K, QM))))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sym_waves_per_simd(K, QM), sym_waves_per_simd(K, QM))))
 void knn_sym_kernel(KnnArgs a) {
-    constexpr int CB = knn_col_blocks(K, QM);
+    constexpr int CB = sym_col_blocks(K, QM);
     using T = Tile<QM>;
     constexpr int QT = kWaves * 16 * CB;
     static_assert(QT % T::TR == 0, "a query tile covers whole database tiles");
