@@ -50,14 +50,15 @@ inline int tile_rows(int qm) { return qm > 56 ? 16 : 32; }
 // kNN tile kernel occupancy: three waves per SIMD where the registers fit
 // without spills (d <= 64 and K <= 16; d <= 128 and K <= 11), two otherwise
 constexpr int knn_waves_per_simd(int K, int QM) { return (QM <= 16 && K <= 16) || (QM <= 32 && K <= 11) ? 3 : 2; }
-// Boruvka scan kernel occupancy: three waves per SIMD for d <= 128, two otherwise
-constexpr int scan_waves_per_simd(int QM) { return QM <= 32 ? 3 : 2; }
+// Boruvka scan kernel occupancy: four waves per SIMD for d <= 64 (one column
+// block per wave: 125 VGPRs), three for d <= 128, two otherwise
+constexpr int scan_waves_per_simd(int QM) { return QM <= 16 ? 4 : QM <= 32 ? 3 : 2; }
 // kNN tiles per barrier of the tile loop: two (four LDS tile buffers) where
 // they fit three workgroups per CU, d <= 64
 constexpr int knn_tiles_per_barrier(int QM) { return QM <= 16 ? 2 : 1; }
 // 16-column query blocks per wave: two when the registers allow it
 constexpr int knn_col_blocks(int K, int QM) { return (K > 11 || QM > 16) ? 1 : 2; }
-constexpr int scan_col_blocks(int QM) { return QM > 16 ? 1 : 2; }
+constexpr int scan_col_blocks(int) { return 1; }
 inline int knn_query_tile(int K, int QM) { return kWaves * 16 * knn_col_blocks(K, QM); }
 // symmetric pass: one 16-column query block per wave, so that (up to K = 16) the
 // kernel fits 128 VGPRs and runs four waves per SIMD
