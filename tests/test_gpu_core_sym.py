@@ -49,6 +49,21 @@ def test_core_symmetric_equals_dense(n, d, ms, seed):
     assert_same(*run_both(X, ms))
 
 
+def _random_shapes(count, seed):
+    # seeded draws over the symmetric path's range: n from its threshold to 60,000 (whole and partial
+    # tiles), every d up to 64 (odd feature counts, partial k-steps), min_samples 1 to 31 (every list length)
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(16384, 60001)), int(rng.integers(1, 65)), int(rng.integers(1, 32)), int(rng.integers(0, 1 << 20)))
+            for _ in range(count)]
+
+
+@pytest.mark.parametrize("n,d,ms,seed", _random_shapes(8, 2026))
+def test_core_symmetric_equals_dense_random_shapes(n, d, ms, seed):
+    X = datagen.gaussian_mixture(n, d, 40, seed=seed)
+    say("core symmetric vs dense (random shape) n=%d d=%d ms=%d seed=%d" % (n, d, ms, seed))
+    assert_same(*run_both(X, ms))
+
+
 @pytest.mark.parametrize("n,d,ms,ld", [
     (16385, 1, 10, None),      # d = 1; the last query tile holds one point, the last database tile one row
     (18000, 61, 10, 18013),    # leading dimension past n
