@@ -60,10 +60,11 @@ constexpr int knn_tiles_per_barrier(int QM) { return QM <= 16 ? 2 : 1; }
 constexpr int knn_col_blocks(int K, int QM) { return (K > 11 || QM > 16) ? 1 : 2; }
 constexpr int scan_col_blocks(int) { return 1; }
 inline int knn_query_tile(int K, int QM) { return kWaves * 16 * knn_col_blocks(K, QM); }
-// symmetric pass: one 16-column query block per wave, so that (up to K = 16) the
-// kernel fits 128 VGPRs and runs four waves per SIMD
+// symmetric pass: one 16-column query block per wave and no LDS beyond the tile
+// loop's, so that the kernel runs five waves per SIMD up to K = 11 (96 VGPRs),
+// four at K = 16 (128)
 constexpr int sym_col_blocks(int, int) { return 1; }
-constexpr int sym_waves_per_simd(int K, int QM) { return K <= 16 ? 4 : knn_waves_per_simd(K, QM); }
+constexpr int sym_waves_per_simd(int K, int QM) { return K <= 11 ? 5 : K <= 16 ? 4 : knn_waves_per_simd(K, QM); }
 inline int sym_query_tile(int K, int QM) { return kWaves * 16 * sym_col_blocks(K, QM); }
 inline int scan_query_tile(int QM) { return kWaves * 16 * scan_col_blocks(QM); }
 // row stride (floats) of the point-major copies the tiles read: four segments

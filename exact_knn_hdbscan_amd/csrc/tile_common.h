@@ -559,7 +559,9 @@ template <int K, int CB, int RB, class List = TopK<K>> struct EpiKnn {
         for (int cb = 0; cb < CB; ++cb) any = any || hit[cb];
         if (!__builtin_amdgcn_ballot_w64(any)) return;
         stash(acc);
-        insert(nb4, hit, acc, nrm, j0);
+        insert(nb4, hit, acc, nrm, j0, [&](int cb, int e) {
+            return sv[((cb * RB + (e >> 2)) * 4 + (e & 3)) * kThreads + tid];
+        });
         __builtin_amdgcn_wave_barrier(); // the loads above before the next tile's stores
     }
     // the wave's dot products to LDS ([value][thread])
@@ -572,9 +574,10 @@ template <int K, int CB, int RB, class List = TopK<K>> struct EpiKnn {
                 for (int r = 0; r < 4; ++r) sv[((cb * RB + rb) * 4 + r) * kThreads + tid] = acc[rb][cb][r];
         __builtin_amdgcn_wave_barrier(); // the LDS stores above before the loads below
     }
-    // the insertions, after stash()
+    // the insertions; dot(cb, e) gives the dot product of element e (= 4 rb + r) of block cb
+    template <class Dot>
     __device__ __forceinline__ void insert(const f4 (&nb4)[RB], const bool (&hit)[CB], const f4 (&acc)[RB][CB],
-                                           const float *nrm, int64_t j0) {
+                                           const float *nrm, int64_t j0, Dot dot) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             if (!__builtin_amdgcn_ballot_w64(hit[cb])) continue;
@@ -593,8 +596,7 @@ template <int K, int CB, int RB, class List = TopK<K>> struct EpiKnn {
                     const int e = __builtin_ctz(mk);
                     mk &= mk - 1u;
                     const int row = (e >> 2) * 16 + 4 * g + (e & 3);
-                    const float d2 = fmaf(-2.f, sv[((cb * RB + (e >> 2)) * 4 + (e & 3)) * kThreads + tid],
-                                          nq[cb] + nrm[row]);
+                    const float d2 = fmaf(-2.f, dot(cb, e), nq[cb] + nrm[row]);
                     L.push_ascending(d2 > 0.f ? d2 : 0.f, (int32_t)(j0 + row));
                 }
             }
@@ -800,28 +802,19 @@ template <int K, int CB, int RB> struct EpiSym : EpiKnn<K, CB, RB> {
     Entry *colbuf;
     uint32_t *colcnt;
     int colcap;
-    // column candidates wait in a per-wave LDS queue (kSymQueue entries: row, D2,
-    // query) and go to the buffers 64 at a time, the returning atomics of a
-    // flush in flight together instead of one round trip per candidate on the
-    // way to the tile's barrier
-    static constexpr int kSymQueue = 128;
-    int32_t *qj;
-    float *qd;
-    int32_t *qq;
-    uint32_t qn; // entries queued (wave-uniform)
-    __device__ __forceinline__ void flush() {
-        const int lane = this->tid & 63;
-        __builtin_amdgcn_wave_barrier(); // the queue's writes (by any lane) before the reads below
-        for (uint32_t b = 0; b < qn; b += 64) {
-            const uint32_t e = b + (uint32_t)lane;
-            if (e < qn) {
-                const int32_t j = qj[e];
-                const uint32_t pos = atomicAdd(&colcnt[j], 1u);
-                if (pos < (uint32_t)colcap) colbuf[(int64_t)j * colcap + pos] = Entry{qd[e], qq[e]};
-            }
-        }
-        qn = 0;
-        __builtin_amdgcn_wave_barrier(); // the reads above before the queue's next writes
+    // The slow paths take each passing element's dot product from registers (a
+    // select over the lane's RB * 4 values) and append column candidates to the
+    // buffers directly (a returning atomicAdd on the row's count, then a store):
+    // no LDS stash and no LDS queue, so a workgroup needs only the tile loop's
+    // LDS and fits five per CU.
+    __device__ __forceinline__ static float dot_of(const f4 (&acc)[RB][CB], int cb, int e) {
+        float v = acc[0][cb][0];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (rb * 4 + r > 0) v = e == rb * 4 + r ? acc[rb][cb][r] : v;
+        return v;
     }
 
     // Base::prepare with the bound capped by tau
@@ -876,21 +869,16 @@ template <int K, int CB, int RB> struct EpiSym : EpiKnn<K, CB, RB> {
         }
         const bool wr = __builtin_amdgcn_ballot_w64(anyr) != 0, wc = __builtin_amdgcn_ballot_w64(anyc) != 0;
         if (!wr && !wc) return;
-        this->stash(acc);
         if (wc) column(acc, nb4, th4, hitc, tau_bits, nrm, j0);
-        if (wr) this->insert(nb4, hit, acc, nrm, j0);
-        __builtin_amdgcn_wave_barrier(); // the loads above before the next tile's stores
+        if (wr) this->insert(nb4, hit, acc, nrm, j0, [&](int cb, int e) { return dot_of(acc, cb, e); });
     }
-    // Column side's candidates, after stash(): a loop over the set bits of a
-    // per-lane mask as in the row side, each appending the exact D2 to the
-    // database row's buffer when it is within the row's tau.
+    // Column side's candidates: a loop over the set bits of a per-lane mask as
+    // in the row side, each appending the exact D2 to the database row's buffer
+    // when it is within the row's tau.
     __device__ __forceinline__ void column(const f4 (&acc)[RB][CB], const f4 (&nb4)[RB], const f4 (&th4)[RB],
                                            const bool (&hitc)[CB], const int32_t *tau_bits, const float *nrm,
                                            int64_t j0) {
-        const int g = this->g, tid = this->tid;
-        // buffer accesses from the tile's first row (a scalar base, j0 < 2^31): the
-        // lane offsets stay 32-bit (row < 64, pos < colcap)
-        const int lane = tid & 63;
+        const int g = this->g;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             if (!__builtin_amdgcn_ballot_w64(hitc[cb])) continue;
@@ -912,22 +900,14 @@ template <int K, int CB, int RB> struct EpiSym : EpiKnn<K, CB, RB> {
                     mk &= mk - 1u;
                     const int row = (e >> 2) * 16 + 4 * g + (e & 3);
                     j = (int32_t)(j0 + row);
-                    d2 = fmaf(-2.f, this->sv[((cb * RB + (e >> 2)) * 4 + (e & 3)) * kThreads + tid],
-                              this->nq[cb] + nrm[row]);
+                    d2 = fmaf(-2.f, dot_of(acc, cb, e), this->nq[cb] + nrm[row]);
                     d2 = d2 > 0.f ? d2 : 0.f;
                     // rows outside the tile carry NaN bits here, which no D2 satisfies
                     take = j0 + row >= col_from && d2 <= __int_as_float(tau_bits[row]);
                 }
-                const uint64_t m = __builtin_amdgcn_ballot_w64(take);
-                if (m) {
-                    if (qn + 64 > (uint32_t)kSymQueue) flush();
-                    if (take) {
-                        const uint32_t at = qn + (uint32_t)__builtin_popcountll(m & ((1ull << lane) - 1ull));
-                        qj[at] = j;
-                        qd[at] = d2;
-                        qq[at] = this->qrow[cb];
-                    }
-                    qn += (uint32_t)__builtin_popcountll(m);
+                if (take) {
+                    const uint32_t pos = atomicAdd(&colcnt[j], 1u);
+                    if (pos < (uint32_t)colcap) colbuf[(int64_t)j * colcap + pos] = Entry{d2, this->qrow[cb]};
                 }
             }
         }
@@ -964,17 +944,9 @@ void knn_sym_kernel(KnnArgs a) {
     const int64_t len = a.tiles - f;
     const int64_t tb = f + len * split / a.splits, te = f + len * (split + 1) / a.splits;
 
-    __shared__ float sv[EpiSym<K, CB, T::RB>::NV * kThreads];
-    constexpr int QL = EpiSym<K, CB, T::RB>::kSymQueue;
-    __shared__ int32_t sq_j[kWaves * QL], sq_q[kWaves * QL];
-    __shared__ float sq_d[kWaves * QL];
     epi.init();
-    epi.qj = sq_j + wave * QL;
-    epi.qd = sq_d + wave * QL;
-    epi.qq = sq_q + wave * QL;
-    epi.qn = 0;
     epi.g = g;
-    epi.sv = sv;
+    epi.sv = nullptr; // no stash: the slow paths select the dot products from registers
     epi.tid = tid;
     epi.col_from = qbase + QT;
     epi.colbuf = a.colbuf;
@@ -986,7 +958,6 @@ void knn_sym_kernel(KnnArgs a) {
     for (int cb = 0; cb < CB; ++cb) epi.admq[cb] = fmaf(epi.cap[cb], 1.0f + kWiden, -epi.nq[cb] * (1.0f - kWiden));
     run_tiles<QM, CB, true, 1>(a.Bt, (int32_t)a.m, a.nrm_b, reinterpret_cast<const int32_t *>(a.tau), a.theta,
                                (int32_t)tb, (int32_t)te, bq, epi);
-    if (epi.qn) epi.flush();
 
     // the row side's list of each query: this split's partial list
 #pragma unroll
